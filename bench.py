@@ -1,0 +1,262 @@
+"""Benchmark: SeedLM fused decode-GEMV on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 4] [--batch 1]
+
+One step = one batch-1 pass of the fused decode-GEMV over every weight matrix
+of one synthetic Llama-3-70B decoder layer (q, k, v, o 8192x8192 / 1024x8192,
+gate, up 28672x8192, down 8192x28672), 4-bit SeedLM (C=8, P=3, K=16), fp16 x
+and y, inputs resident in HBM.  Records are drawn by workloads.gen_records
+(seeds uniform in [1, 65535], coefficients uniform in [-8, 7], exponents uniform
+in [-12, -6]); x is N(0,1) fp16.  Two copies of the layer's packed buffers are
+rotated so that consecutive steps do not find their weights in the 256 MB MALL.
+
+Prints one JSON line: effective weights/s (value), compressed HBM GB/s and its
+fraction of 8 TB/s, the roofline of the fused kernel (HIP events on the launch
+stream), the same-chip fp16 GEMV baseline and its speed-up, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "effective weights/s + compressed HBM GB/s (% peak), 4-bit decode-GEMV bs=1"
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=4)
+    p.add_argument("--batch", type=int, default=1)
+    p.add_argument("--variant", type=int, default=0)
+    p.add_argument("--copies", type=int, default=2)
+    p.add_argument("--no-fp16", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def cpu_baseline(cfg, budget_s):
+    """Time the oracle (decode + float64 matvec) on sampled rows of each matrix."""
+    from oracle import seedlm_oracle as O
+    from workloads import gen_records, gen_x
+
+    rows_per = 8
+    weights = 0
+    t_dec = t_mv = 0.0
+    rounds = 0
+    recs = []
+    for mid, mat in enumerate(cfg.matrices):
+        s, c, e = gen_records(cfg.config_id, mid, mat.rows, mat.cols, cfg.C, cfg.P)
+        x = gen_x(cfg.config_id, mid, 1, mat.cols, cfg.x_dtype)
+        recs.append((mat, s, c, e, x))
+    rng = np.random.default_rng(12345)
+    while t_dec + t_mv < budget_s:
+        for mat, s, c, e, x in recs:
+            pick = rng.choice(mat.rows, size=rows_per, replace=False)
+            t0 = time.perf_counter()
+            W = O.decode_rows(s[pick], c[pick], e[pick], mat.cols, cfg.C, cfg.P)
+            t1 = time.perf_counter()
+            O.gemv(W, x)
+            t2 = time.perf_counter()
+            t_dec += t1 - t0
+            t_mv += t2 - t1
+            weights += rows_per * mat.cols
+        rounds += 1
+        rows_per = min(rows_per * 2, 256)
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {
+        "value": weights / (t_dec + t_mv),
+        "unit": "weights/s",
+        "cores": int(max(1, blas)),
+        "kind": "oracle",
+        "sample": (f"{weights} weights from sampled rows of the 7 layer matrices "
+                   f"({rounds} rounds); decode {t_dec:.2f} s (NumPy, 1 thread), "
+                   f"float64 matvec {t_mv:.2f} s; host cores available "
+                   f"{len(os.sched_getaffinity(0))}"),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import prng_seeded_decode_amd as S
+    from workloads import CONFIGS, gen_records, gen_x
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    ydt = torch.float16 if cfg.x_dtype == "f16" else torch.float32
+    xdt = ydt
+    batch = args.batch
+
+    # ---- pack the layer (copies for rotation) ----
+    mats = []  # per matrix: dict
+    for mid, mat in enumerate(cfg.matrices):
+        s, c, e = gen_records(cfg.config_id, mid, mat.rows, mat.cols, cfg.C, cfg.P)
+        copies = [S.seedlm_pack(s, c, e, mat.rows, mat.cols, cfg.C, cfg.P, cfg.K)
+                  for _ in range(args.copies)]
+        del s, c, e
+        x = torch.from_numpy(gen_x(cfg.config_id, mid, batch, mat.cols, cfg.x_dtype)).to(dev)
+        y = torch.empty((batch, mat.rows), dtype=ydt, device=dev)
+        mats.append({"mat": mat, "copies": copies, "x": x, "y": y,
+                     "bytes": copies[0].compressed_bytes})
+    torch.cuda.synchronize()
+
+    def run_step(k):
+        for d in mats:
+            S.seedlm_gemv(d["copies"][k % args.copies], d["x"], d["y"], batch=batch,
+                          stream=stream, variant=args.variant)
+
+    # ---- whole-step timing ----
+    for k in range(args.warmup):
+        run_step(k)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for k in range(args.steps):
+        run_step(k)
+    ev1.record(stream)
+    ev1.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-launch timing (events bracket every launch on the launch stream) ----
+    per = {d["mat"].name: [] for d in mats}
+    evs = []
+    for k in range(args.steps):
+        for d in mats:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            S.seedlm_gemv(d["copies"][k % args.copies], d["x"], d["y"], batch=batch,
+                          stream=stream, variant=args.variant)
+            b.record(stream)
+            evs.append((d["mat"].name, a, b))
+    torch.cuda.synchronize()
+    for name, a, b in evs:
+        per[name].append(a.elapsed_time(b))
+
+    layer_weights = sum(d["mat"].rows * d["mat"].cols for d in mats)
+    layer_bytes = sum(d["bytes"] for d in mats)
+    act_bytes = sum(batch * (d["mat"].cols + d["mat"].rows) * (2 if ydt == torch.float16 else 4)
+                    for d in mats)
+    per_matrix = {}
+    for d in mats:
+        n = d["mat"].name
+        t = float(np.median(per[n])) * 1e-3
+        per_matrix[n] = {
+            "shape": [d["mat"].rows, d["mat"].cols],
+            "us": round(t * 1e6, 2),
+            "compressed_GBps": round(d["bytes"] / t / 1e9, 1),
+            "weights_per_s": d["mat"].rows * d["mat"].cols / t,
+        }
+    # Dominant kernel: the fused decode-GEMV; its launches over one step.
+    launch_s = [np.mean(per[d["mat"].name]) * 1e-3 for d in mats]
+    alg_bytes = [d["bytes"] + batch * (d["mat"].cols + d["mat"].rows) * 2 for d in mats]
+    achieved = (np.mean(alg_bytes) / np.mean(launch_s)) / 1e9
+    t_step = ms_per_step * 1e-3
+
+    # ---- fp16 baselines on the same shapes ----
+    fp16 = None
+    if not args.no_fp16:
+        Ws = []
+        for d in mats:
+            r, ccol = d["mat"].rows, d["mat"].cols
+            Ws.append([torch.randn(r, ccol, device=dev, dtype=torch.float16) for _ in range(2)])
+        xs = [d["x"].half() for d in mats]
+        ys = [torch.empty((batch, d["mat"].rows), dtype=torch.float16, device=dev) for d in mats]
+
+        def fp16_step(k, own):
+            for i in range(len(mats)):
+                W = Ws[i][k % 2]
+                if own:
+                    S.seedlm_fp16_gemv(W, xs[i], ys[i], batch=batch, stream=stream)
+                else:
+                    torch.nn.functional.linear(xs[i], W, out=ys[i])
+
+        res = {}
+        for own, name in ((True, "own_fp16_gemv"), (False, "torch_linear_fp16")):
+            for k in range(args.warmup):
+                fp16_step(k, own)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for k in range(args.steps):
+                fp16_step(k, own)
+            ev1.record(stream)
+            ev1.synchronize()
+            res[name] = ev0.elapsed_time(ev1) / args.steps
+        best = min(res.values())
+        fp16 = {"ms_per_step": {k: round(v, 4) for k, v in res.items()},
+                "fp16_GBps": round(sum(2 * r * c for r, c in ((d["mat"].rows, d["mat"].cols) for d in mats))
+                                   / (best * 1e-3) / 1e9, 1),
+                "speedup_vs_best_fp16": round(best / ms_per_step, 3)}
+        del Ws
+
+    out = {
+        "metric": METRIC,
+        "value": layer_weights / t_step,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: q,k,v,o,gate,up,down fused decode-GEMV, "
+                         f"SeedLM C={cfg.C} P={cfg.P} K={cfg.K}, batch {batch}, "
+                         f"x/y {cfg.x_dtype}"),
+            "batch": batch,
+            "compressed_bytes_per_step": layer_bytes,
+            "weights_per_step": layer_weights,
+            "rotated_copies": args.copies,
+            "variant": args.variant,
+        },
+        "compressed_GBps": round(layer_bytes / t_step / 1e9, 1),
+        "pct_hbm_peak": round(100 * layer_bytes / t_step / 1e9 / HBM_PEAK_GBPS, 2),
+        "activation_bytes_per_step": act_bytes,
+        "per_matrix": per_matrix,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(float(achieved), 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(float(achieved) / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "fp16_baseline": fp16,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

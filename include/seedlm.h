@@ -1,0 +1,186 @@
+/*
+ * seedlm.h -- C ABI of the SeedLM decompress-and-multiply library for MI355X (gfx950).
+ *
+ * The method (SeedLM, "Compressing LLM Weights into Seeds of Pseudo-Random
+ * Generators"): each block of C weights is stored as a K-bit seed s, P 4-bit
+ * coefficients t and a shared exponent e.  At inference the seed drives a
+ * Linear Feedback Shift Register that emits the C x P matrix U(s), and the
+ * block is rebuilt as w = 2^e * U(s) * t
+ *   - paperdance.org/p/2410.10714, English abstract (seed fed to an LFSR that
+ *     generates a random matrix, linearly combined with compressed coefficients);
+ *   - atlas.scime.ai summary, "Approach" (blocks of C weights, P columns,
+ *     K-bit seed, 4-bit quantized coefficients);
+ *   - paperhub.cn OpenReview discussion, rebuttal text for the paragraph before
+ *     Eq. (1) (s and t are fetched from memory, weights are rebuilt on the fly
+ *     and used to compute activations; no full-precision weights are kept) and
+ *     the rebuttal on shared exponents.
+ *
+ * Format fixed by this library (the pages leave these open):
+ *   LFSR      16-bit Fibonacci, right shift: z' = (z >> 1) | (f << 15) with
+ *             f = bit0 ^ bit2 ^ bit3 ^ bit5 of z (x^16 + x^5 + x^3 + x^2 + 1,
+ *             period 65535).  The seed is the first state, z_0 = s, s != 0.
+ *   values    v_n = (z_n - 2^15) / 2^15.
+ *   U(s)      column-major: U[i][j] = v_{j*C + i}, i < C, j < P.
+ *   block     w_i = 2^e * sum_j U[i][j] * t_j, t_j in [-8, 7], e in [-15, 0].
+ *   blocks    lie along a row: block b of row r holds columns b*C .. b*C+C-1;
+ *             nb = ceil(cols / C); the last block keeps its first
+ *             cols - (nb-1)*C weights.
+ *   word      uint32 per block: bits 0..15 seed, 16..19 t0, 20..23 t1,
+ *             24..27 t2 (two's-complement nibbles);
+ *             (C,P)=(8,3):  bits 28..31 g = e + 15;
+ *             (C,P)=(12,4): bits 28..31 t3, and g sits in a nibble array.
+ *   panels    rows padded to Mp = 4*ceil(rows/4) (padding words = 0x00000001),
+ *             blocks grouped in panels of 32; word (r, b) with p = b/32,
+ *             q = b%32, Qp = width of panel p, quad = r/4, r4 = r%4 is at
+ *             index p*Mp*32 + (quad*Qp + q)*4 + r4.  For (12,4) the exponent
+ *             nibble of (r, b) is nibble r4 of uint16 number
+ *             p*(Mp/4)*32 + quad*Qp + q of an array starting at byte
+ *             align256(4*Mp*nb) of the same buffer.
+ *   Supported (C, P, K): (8, 3, 16) -- 4 bits per weight; (12, 4, 16) -- 3 bits
+ *   per weight (36 bits per 12-weight block).
+ *
+ * Conventions: every call returns a status (0 = SEEDLM_OK, negative = error);
+ * no C++ exception crosses this boundary.  "device" pointers are HIP device
+ * memory of the current device; "host" pointers are ordinary host memory.
+ * Streams are hipStream_t passed as void* (NULL = the null stream).  Kernel
+ * launches are asynchronous: a fault inside a kernel is reported by the
+ * caller's next synchronisation, not by these calls.
+ */
+#ifndef SEEDLM_H
+#define SEEDLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SEEDLM_API __attribute__((visibility("default")))
+
+/* Status codes. */
+#define SEEDLM_OK 0
+#define SEEDLM_E_INVALID (-1)     /* bad argument: null pointer, range, shape      */
+#define SEEDLM_E_UNSUPPORTED (-2) /* (C, P, K) or dtype combination not supported  */
+#define SEEDLM_E_NOMEM (-3)       /* host or device allocation failed              */
+#define SEEDLM_E_DEVICE (-4)      /* a HIP runtime call failed                     */
+
+/* Element types for activations and outputs. */
+#define SEEDLM_F32 0
+#define SEEDLM_F16 1
+
+/* Largest batch accepted by seedlm_gemv. */
+#define SEEDLM_MAX_BATCH 16
+
+typedef struct seedlm_matrix* seedlm_handle;
+
+typedef struct seedlm_info_t {
+  int64_t rows;             /* M */
+  int64_t cols;             /* N */
+  int32_t C, P, K;
+  int64_t blocks_per_row;   /* nb = ceil(N / C) */
+  int64_t padded_rows;      /* Mp = 4 * ceil(M / 4) */
+  int64_t compressed_bytes; /* size of the packed buffer, padding included */
+} seedlm_info_t;
+
+/*
+ * seedlm_pack_host -- write the packed layout into host memory (no GPU use).
+ *   seeds  host uint16 [rows][nb], each in [1, 65535]
+ *   coeffs host int8   [rows][nb][P], each in [-8, 7]
+ *   exps   host int8   [rows][nb], each in [-15, 0]
+ *   dst    host buffer of *bytes bytes, or NULL to query the size.
+ * On entry *bytes is the capacity of dst; on return it is the layout size.
+ * Errors: SEEDLM_E_INVALID (null pointers, rows/cols <= 0, out-of-range
+ * record, dst too small), SEEDLM_E_UNSUPPORTED ((C,P,K) not supported).
+ * Source: the per-block record {seed, coefficients, shared exponent} of the
+ * pages (atlas.scime.ai "Approach"; paperhub.cn rebuttal on shared exponents).
+ */
+SEEDLM_API int seedlm_pack_host(const uint16_t* seeds, const int8_t* coeffs,
+                                const int8_t* exps, int64_t rows, int64_t cols,
+                                int C, int P, int K, void* dst, size_t* bytes);
+
+/*
+ * seedlm_pack -- validate and pack records, upload them to the current device
+ * and return a handle that owns the device copy (plus a small workspace for
+ * split-reduction partials).  Synchronous.  The caller keeps ownership of the
+ * host arrays (layouts as for seedlm_pack_host).
+ * Errors: as seedlm_pack_host, plus SEEDLM_E_NOMEM and SEEDLM_E_DEVICE.
+ * Source: as seedlm_pack_host.
+ */
+SEEDLM_API int seedlm_pack(const uint16_t* seeds, const int8_t* coeffs,
+                           const int8_t* exps, int64_t rows, int64_t cols,
+                           int C, int P, int K, seedlm_handle* out);
+
+/*
+ * seedlm_gemv -- y = W x for a batch of activation vectors, with W rebuilt from
+ * the handle's seeds and coefficients inside the kernel and never stored
+ * (paperhub.cn rebuttal text before Eq. (1): weights are reconstructed on the
+ * fly from s and t and used to compute the activations).
+ *   x  device [batch][cols], x_dtype SEEDLM_F32 or SEEDLM_F16 (row-major)
+ *   y  device [batch][rows], y_dtype SEEDLM_F32 or SEEDLM_F16 (fp16: round to
+ *      nearest even); both caller-owned.
+ *   batch in [1, SEEDLM_MAX_BATCH].  batch 1 runs the fused decode-GEMV;
+ *   batch > 1 decodes each weight tile once and contracts it on the matrix
+ *   cores in fp16 with fp32 accumulation.
+ * Asynchronous on `stream`.  Calls that share a handle use the handle's
+ * workspace and must not overlap in time (serialise them on one stream).
+ * Inputs must be finite.
+ * Errors: SEEDLM_E_INVALID (null, batch out of range),
+ * SEEDLM_E_UNSUPPORTED (dtype), SEEDLM_E_DEVICE (launch failure).
+ */
+SEEDLM_API int seedlm_gemv(seedlm_handle h, const void* x, void* y, int batch,
+                           int x_dtype, int y_dtype, void* stream);
+
+/*
+ * seedlm_decode -- write the dense weights W[rows][cols] as fp32 (row-major,
+ * caller-owned device memory).  Bit-exact: the block's integer sum times a
+ * power of two is exact in fp32.  Asynchronous on `stream`.
+ * Source: the block reconstruction of the abstract (paperdance.org) and the
+ * "Approach" section (atlas.scime.ai).
+ * Errors: SEEDLM_E_INVALID, SEEDLM_E_DEVICE.
+ */
+SEEDLM_API int seedlm_decode(seedlm_handle h, float* W_out, void* stream);
+
+/* seedlm_destroy -- free the handle's device memory; NULL is a no-op. */
+SEEDLM_API int seedlm_destroy(seedlm_handle h);
+
+/* seedlm_info -- shape, format and compressed size of a packed matrix. */
+SEEDLM_API int seedlm_info(seedlm_handle h, seedlm_info_t* info);
+
+/* seedlm_export -- copy the packed buffer back to host memory (synchronous).
+ * On entry *bytes is the capacity of host (host may be NULL to query). */
+SEEDLM_API int seedlm_export(seedlm_handle h, void* host, size_t* bytes);
+
+/* seedlm_status_string -- a static message for a status code. */
+SEEDLM_API const char* seedlm_status_string(int status);
+
+/*
+ * Kernel variants of the batch-1 path, for A/B measurement only.  The default
+ * (SEEDLM_VARIANT_AUTO) is what seedlm_gemv runs.
+ *   SEEDLM_VARIANT_LUT     basis bits from GF(2) byte tables in LDS, dot with x
+ *                          through per-panel activation byte tables in LDS
+ *   SEEDLM_VARIANT_TABLE   basis bits from a 2^16-entry table resident in L2
+ *   SEEDLM_VARIANT_SIMPLE  one wave per row, per-lane LFSR stepping
+ */
+#define SEEDLM_VARIANT_AUTO 0
+#define SEEDLM_VARIANT_LUT 1
+#define SEEDLM_VARIANT_TABLE 2
+#define SEEDLM_VARIANT_SIMPLE 3
+SEEDLM_API int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch,
+                                   int x_dtype, int y_dtype, int variant, void* stream);
+
+/*
+ * seedlm_fp16_gemv -- measurement baseline, not part of the method: a plain
+ * fp16 GEMV y[batch][rows] = W[rows][cols] x[batch][cols] with fp16 W, x, y
+ * and fp32 accumulation, used as the speed-up denominator (the pages compare
+ * against an FP16 design: atlas.scime.ai "Key results").
+ * All pointers are device memory; cols must be a multiple of 8.
+ */
+SEEDLM_API int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t rows,
+                                int64_t cols, int batch, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEEDLM_H */

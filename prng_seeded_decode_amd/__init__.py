@@ -1,0 +1,32 @@
+"""SeedLM decompress-and-multiply on MI355X (gfx950).
+
+A small C-ABI library (libseedlm.so: hand-written HIP kernels) plus this
+ctypes binding.  Weights are stored per block as a 16-bit LFSR seed, 4-bit
+coefficients and a shared exponent, and rebuilt inside the kernels while
+multiplying (SeedLM: paperdance.org abstract; atlas.scime.ai "Approach").
+"""
+from ._binding import (  # noqa: F401
+    E_DEVICE,
+    E_INVALID,
+    E_NOMEM,
+    E_UNSUPPORTED,
+    F16,
+    F32,
+    MAX_BATCH,
+    OK,
+    VARIANT_AUTO,
+    VARIANT_LUT,
+    VARIANT_SIMPLE,
+    VARIANT_TABLE,
+    SeedLMError,
+    SeedLMMatrix,
+    lib,
+    pack_host_status,
+    seedlm_decode,
+    seedlm_export,
+    seedlm_fp16_gemv,
+    seedlm_gemv,
+    seedlm_pack,
+    seedlm_pack_host,
+    status_string,
+)

@@ -1,0 +1,246 @@
+"""ctypes binding of libseedlm.so: argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; PyTorch is used only
+for device memory (tensors) and streams.  Loading fails loudly when the built
+library is missing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libseedlm.so")
+
+OK = 0
+E_INVALID = -1
+E_UNSUPPORTED = -2
+E_NOMEM = -3
+E_DEVICE = -4
+F32 = 0
+F16 = 1
+MAX_BATCH = 16
+VARIANT_AUTO = 0
+VARIANT_LUT = 1
+VARIANT_TABLE = 2
+VARIANT_SIMPLE = 3
+
+EXPORTED = (
+    "seedlm_pack_host",
+    "seedlm_pack",
+    "seedlm_gemv",
+    "seedlm_gemv_variant",
+    "seedlm_decode",
+    "seedlm_destroy",
+    "seedlm_info",
+    "seedlm_export",
+    "seedlm_status_string",
+    "seedlm_fp16_gemv",
+)
+
+
+class SeedLMError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_string(status)} ({status})")
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("C", ctypes.c_int32),
+        ("P", ctypes.c_int32),
+        ("K", ctypes.c_int32),
+        ("blocks_per_row", ctypes.c_int64),
+        ("padded_rows", ctypes.c_int64),
+        ("compressed_bytes", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libseedlm.so (once).  Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m prng_seeded_decode_amd.build`"
+        )
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.seedlm_pack_host.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, vp, ctypes.POINTER(sz)]
+    L.seedlm_pack.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, ctypes.POINTER(vp)]
+    L.seedlm_gemv.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    L.seedlm_gemv_variant.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    L.seedlm_decode.argtypes = [vp, vp, vp]
+    L.seedlm_destroy.argtypes = [vp]
+    L.seedlm_info.argtypes = [vp, ctypes.POINTER(_Info)]
+    L.seedlm_export.argtypes = [vp, vp, ctypes.POINTER(sz)]
+    L.seedlm_status_string.argtypes = [i32]
+    L.seedlm_status_string.restype = ctypes.c_char_p
+    L.seedlm_fp16_gemv.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    for name in EXPORTED:
+        if name != "seedlm_status_string":
+            getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().seedlm_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise SeedLMError(status, what)
+
+
+def _records(seeds, coeffs, exps, rows, cols, C, P):
+    nb = -(-cols // C)
+    seeds = np.ascontiguousarray(seeds, dtype=np.uint16)
+    coeffs = np.ascontiguousarray(coeffs, dtype=np.int8)
+    exps = np.ascontiguousarray(exps, dtype=np.int8)
+    if seeds.shape != (rows, nb) or coeffs.shape != (rows, nb, P) or exps.shape != (rows, nb):
+        raise ValueError("record arrays must be seeds[rows][nb], coeffs[rows][nb][P], exps[rows][nb]")
+    return seeds, coeffs, exps
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def seedlm_pack_host(seeds, coeffs, exps, rows, cols, C, P, K=16) -> bytes:
+    """Packed layout written on the host (no GPU involved)."""
+    seeds, coeffs, exps = _records(seeds, coeffs, exps, rows, cols, C, P)
+    n = ctypes.c_size_t(0)
+    _check(lib().seedlm_pack_host(_ptr(seeds), _ptr(coeffs), _ptr(exps), rows, cols, C, P, K,
+                                  None, ctypes.byref(n)), "seedlm_pack_host")
+    buf = ctypes.create_string_buffer(n.value)
+    _check(lib().seedlm_pack_host(_ptr(seeds), _ptr(coeffs), _ptr(exps), rows, cols, C, P, K,
+                                  ctypes.cast(buf, ctypes.c_void_p), ctypes.byref(n)),
+           "seedlm_pack_host")
+    return buf.raw[: n.value]
+
+
+def pack_host_status(seeds, coeffs, exps, rows, cols, C, P, K=16) -> int:
+    """Raw status of seedlm_pack_host on arbitrary arrays (for error-path tests)."""
+    seeds = np.ascontiguousarray(seeds, dtype=np.uint16)
+    coeffs = np.ascontiguousarray(coeffs, dtype=np.int8)
+    exps = np.ascontiguousarray(exps, dtype=np.int8)
+    n = ctypes.c_size_t(0)
+    return lib().seedlm_pack_host(_ptr(seeds), _ptr(coeffs), _ptr(exps), rows, cols, C, P, K,
+                                  None, ctypes.byref(n))
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+class SeedLMMatrix:
+    """A packed matrix on the GPU (owns a libseedlm handle)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+        info = _Info()
+        _check(lib().seedlm_info(self._h, ctypes.byref(info)), "seedlm_info")
+        self.rows = info.rows
+        self.cols = info.cols
+        self.C, self.P, self.K = info.C, info.P, info.K
+        self.blocks_per_row = info.blocks_per_row
+        self.padded_rows = info.padded_rows
+        self.compressed_bytes = info.compressed_bytes
+
+    @property
+    def handle(self):
+        if self._h is None or not self._h.value:
+            raise ValueError("matrix has been destroyed")
+        return self._h
+
+    def destroy(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(lib().seedlm_destroy(self._h), "seedlm_destroy")
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def seedlm_pack(seeds, coeffs, exps, rows, cols, C, P, K=16) -> SeedLMMatrix:
+    """Validate, pack and upload records; returns a SeedLMMatrix."""
+    seeds, coeffs, exps = _records(seeds, coeffs, exps, rows, cols, C, P)
+    h = ctypes.c_void_p()
+    _check(lib().seedlm_pack(_ptr(seeds), _ptr(coeffs), _ptr(exps), rows, cols, C, P, K,
+                             ctypes.byref(h)), "seedlm_pack")
+    return SeedLMMatrix(h.value)
+
+
+def seedlm_gemv(m: SeedLMMatrix, x, y, batch=None, stream=None, variant=VARIANT_AUTO):
+    """y[batch][rows] = W x[batch][cols] on the GPU (torch CUDA tensors)."""
+    if batch is None:
+        batch = 1 if x.dim() == 1 else x.shape[0]
+    if x.numel() != batch * m.cols or y.numel() != batch * m.rows:
+        raise ValueError("x must hold batch*cols and y batch*rows elements")
+    if not (x.is_cuda and y.is_cuda and x.is_contiguous() and y.is_contiguous()):
+        raise ValueError("x and y must be contiguous device tensors")
+    _check(lib().seedlm_gemv_variant(m.handle, ctypes.c_void_p(x.data_ptr()),
+                                     ctypes.c_void_p(y.data_ptr()), batch, _dtype_code(x),
+                                     _dtype_code(y), variant, _stream_ptr(stream)),
+           "seedlm_gemv")
+    return y
+
+
+def seedlm_decode(m: SeedLMMatrix, W_out, stream=None):
+    """W_out[rows][cols] (fp32 device tensor) = the dense decoded weights."""
+    import torch
+
+    if W_out.dtype != torch.float32 or W_out.numel() != m.rows * m.cols:
+        raise ValueError("W_out must be a float32 tensor with rows*cols elements")
+    if not (W_out.is_cuda and W_out.is_contiguous()):
+        raise ValueError("W_out must be a contiguous device tensor")
+    _check(lib().seedlm_decode(m.handle, ctypes.c_void_p(W_out.data_ptr()), _stream_ptr(stream)),
+           "seedlm_decode")
+    return W_out
+
+
+def seedlm_export(m: SeedLMMatrix) -> bytes:
+    n = ctypes.c_size_t(0)
+    _check(lib().seedlm_export(m.handle, None, ctypes.byref(n)), "seedlm_export")
+    buf = ctypes.create_string_buffer(n.value)
+    _check(lib().seedlm_export(m.handle, ctypes.cast(buf, ctypes.c_void_p), ctypes.byref(n)),
+           "seedlm_export")
+    return buf.raw[: n.value]
+
+
+def seedlm_fp16_gemv(W, x, y, batch=None, stream=None):
+    """Baseline: y = W x with fp16 W[rows][cols], x[batch][cols], y[batch][rows]."""
+    rows, cols = W.shape
+    if batch is None:
+        batch = 1 if x.dim() == 1 else x.shape[0]
+    _check(lib().seedlm_fp16_gemv(ctypes.c_void_p(W.data_ptr()), ctypes.c_void_p(x.data_ptr()),
+                                  ctypes.c_void_p(y.data_ptr()), rows, cols, batch,
+                                  _stream_ptr(stream)), "seedlm_fp16_gemv")
+    return y

@@ -1,0 +1,91 @@
+// C-ABI entry points that launch kernels: argument checks and kernel choice.
+#include <mutex>
+
+#include "lfsr_device.h"
+#include "seedlm_internal.h"
+
+namespace seedlm {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+namespace {
+
+__global__ void ext_table_kernel(uint32_t* __restrict__ table) {
+  const uint32_t s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s < 65536u) table[s] = ext_bits<uint32_t>(s);
+}
+
+bool dtype_ok(int d) { return d == SEEDLM_F32 || d == SEEDLM_F16; }
+
+int check_common(seedlm_handle h, const void* x, void* y, int batch, int xdt, int ydt) {
+  if (!h || !x || !y) return SEEDLM_E_INVALID;
+  if (batch < 1 || batch > SEEDLM_MAX_BATCH) return SEEDLM_E_INVALID;
+  if (!dtype_ok(xdt) || !dtype_ok(ydt)) return SEEDLM_E_UNSUPPORTED;
+  return SEEDLM_OK;
+}
+
+}  // namespace
+
+// The 2^16-entry table of extension bits b[16..47] (the TABLE variant keeps it
+// resident in L2 / the MALL instead of rebuilding the bits per block).
+int build_ext_table(seedlm_matrix* h) {
+  if (h->d_ext_table) return SEEDLM_OK;
+  SEEDLM_HIP_CHECK(hipMalloc((void**)&h->d_ext_table, 65536 * sizeof(uint32_t)));
+  hipLaunchKernelGGL(ext_table_kernel, dim3(256), dim3(256), 0, 0, h->d_ext_table);
+  SEEDLM_HIP_CHECK(hipGetLastError());
+  SEEDLM_HIP_CHECK(hipDeviceSynchronize());
+  return SEEDLM_OK;
+}
+
+}  // namespace seedlm
+
+using namespace seedlm;
+
+extern "C" {
+
+int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch, int x_dtype,
+                        int y_dtype, int variant, void* stream) {
+  int st = check_common(h, x, y, batch, x_dtype, y_dtype);
+  if (st != SEEDLM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (variant) {
+    case SEEDLM_VARIANT_AUTO:
+      return launch_gemv_simple(h, x, y, batch, x_dtype, y_dtype, s);
+    case SEEDLM_VARIANT_SIMPLE:
+      return launch_gemv_simple(h, x, y, batch, x_dtype, y_dtype, s);
+    default:
+      return SEEDLM_E_UNSUPPORTED;
+  }
+}
+
+int seedlm_gemv(seedlm_handle h, const void* x, void* y, int batch, int x_dtype, int y_dtype,
+                void* stream) {
+  return seedlm_gemv_variant(h, x, y, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, stream);
+}
+
+int seedlm_decode(seedlm_handle h, float* W_out, void* stream) {
+  if (!h || !W_out) return SEEDLM_E_INVALID;
+  return launch_decode(h, W_out, static_cast<hipStream_t>(stream));
+}
+
+int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,
+                     int batch, void* stream) {
+  if (!W || !x || !y || rows <= 0 || cols <= 0 || cols % 8 != 0) return SEEDLM_E_INVALID;
+  if (batch < 1 || batch > SEEDLM_MAX_BATCH) return SEEDLM_E_INVALID;
+  return launch_fp16_gemv(W, x, y, rows, cols, batch, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+// Host packer and handle management of libseedlm.
+//
+// The packed buffer holds one 32-bit word per block {seed, coefficients,
+// biased shared exponent} (4-bit format) or {seed, coefficients} plus a nibble
+// array of exponents (3-bit format), grouped into 32-block panels and 4-row
+// quads.  The record itself is the pages' {seed s, coefficients t, shared
+// exponent} (atlas.scime.ai "Approach"; paperhub.cn rebuttal on shared
+// exponents); the bit positions and the panel order are this library's.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "seedlm_internal.h"
+
+using namespace seedlm;
+
+namespace {
+
+bool supported(int C, int P, int K) {
+  return K == 16 && ((C == 8 && P == 3) || (C == 12 && P == 4));
+}
+
+struct Layout {
+  int64_t nb, Mp, np, nwords;
+  size_t exp_off, bytes;
+};
+
+Layout make_layout(int64_t rows, int64_t cols, int C, int P) {
+  Layout L;
+  L.nb = (cols + C - 1) / C;
+  L.Mp = (rows + kQuadRows - 1) / kQuadRows * kQuadRows;
+  L.np = (L.nb + kPanelBlocks - 1) / kPanelBlocks;
+  L.nwords = L.Mp * L.nb;
+  if (P == 3) {
+    L.exp_off = 0;
+    L.bytes = (size_t)L.nwords * 4;
+  } else {
+    L.exp_off = ((size_t)L.nwords * 4 + 255) / 256 * 256;
+    L.bytes = L.exp_off + (size_t)(L.Mp / kQuadRows) * L.nb * 2;
+  }
+  return L;
+}
+
+int validate(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps, int64_t rows,
+             int64_t cols, int C, int P, int K) {
+  if (!seeds || !coeffs || !exps) return SEEDLM_E_INVALID;
+  if (rows <= 0 || cols <= 0) return SEEDLM_E_INVALID;
+  if (!supported(C, P, K)) return SEEDLM_E_UNSUPPORTED;
+  // Keep every index of the layout (and of the kernels' 32-bit row math) in range.
+  if (rows > (1LL << 30) || cols > (1LL << 30)) return SEEDLM_E_INVALID;
+  const int64_t nb = (cols + C - 1) / C;
+  const int64_t n = rows * nb;
+  for (int64_t k = 0; k < n; ++k) {
+    if (seeds[k] == 0) return SEEDLM_E_INVALID;
+    if (exps[k] < -15 || exps[k] > 0) return SEEDLM_E_INVALID;
+  }
+  for (int64_t k = 0; k < n * P; ++k)
+    if (coeffs[k] < -8 || coeffs[k] > 7) return SEEDLM_E_INVALID;
+  return SEEDLM_OK;
+}
+
+void write_layout(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps, int64_t rows,
+                  int C, int P, const Layout& L, uint8_t* dst) {
+  (void)C;
+  uint32_t* words = reinterpret_cast<uint32_t*>(dst);
+  for (int64_t k = 0; k < L.nwords; ++k) words[k] = kPadWord;
+  uint16_t* ex = nullptr;
+  if (P == 4) {
+    memset(dst + (size_t)L.nwords * 4, 0, L.exp_off - (size_t)L.nwords * 4);
+    ex = reinterpret_cast<uint16_t*>(dst + L.exp_off);
+    memset(ex, 0, L.bytes - L.exp_off);
+  }
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < L.nb; ++b) {
+      const int64_t k = r * L.nb + b;
+      uint32_t w = seeds[k];
+      for (int j = 0; j < P; ++j) w |= (uint32_t)(coeffs[k * P + j] & 0xF) << (16 + 4 * j);
+      const uint32_t g = (uint32_t)(exps[k] + 15);
+      if (P == 3) {
+        w |= g << 28;
+      } else {
+        ex[exp_index(r, b, L.Mp, L.nb)] |= (uint16_t)(g << (4 * (r % kQuadRows)));
+      }
+      words[word_index(r, b, L.Mp, L.nb)] = w;
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* seedlm_status_string(int status) {
+  switch (status) {
+    case SEEDLM_OK: return "ok";
+    case SEEDLM_E_INVALID: return "invalid argument";
+    case SEEDLM_E_UNSUPPORTED: return "unsupported format or dtype";
+    case SEEDLM_E_NOMEM: return "out of memory";
+    case SEEDLM_E_DEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int seedlm_pack_host(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps,
+                     int64_t rows, int64_t cols, int C, int P, int K, void* dst,
+                     size_t* bytes) {
+  if (!bytes) return SEEDLM_E_INVALID;
+  int st = validate(seeds, coeffs, exps, rows, cols, C, P, K);
+  if (st != SEEDLM_OK) return st;
+  const Layout L = make_layout(rows, cols, C, P);
+  if (!dst) {
+    *bytes = L.bytes;
+    return SEEDLM_OK;
+  }
+  if (*bytes < L.bytes) {
+    *bytes = L.bytes;
+    return SEEDLM_E_INVALID;
+  }
+  write_layout(seeds, coeffs, exps, rows, C, P, L, static_cast<uint8_t*>(dst));
+  *bytes = L.bytes;
+  return SEEDLM_OK;
+}
+
+int seedlm_pack(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps, int64_t rows,
+                int64_t cols, int C, int P, int K, seedlm_handle* out) {
+  if (!out) return SEEDLM_E_INVALID;
+  *out = nullptr;
+  int st = validate(seeds, coeffs, exps, rows, cols, C, P, K);
+  if (st != SEEDLM_OK) return st;
+  const Layout L = make_layout(rows, cols, C, P);
+
+  uint8_t* host = nullptr;
+  if (hipHostMalloc((void**)&host, L.bytes, hipHostMallocDefault) != hipSuccess)
+    return SEEDLM_E_NOMEM;
+  write_layout(seeds, coeffs, exps, rows, C, P, L, host);
+
+  seedlm_matrix* h = new (std::nothrow) seedlm_matrix();
+  if (!h) {
+    hipHostFree(host);
+    return SEEDLM_E_NOMEM;
+  }
+  h->rows = rows;
+  h->cols = cols;
+  h->C = C;
+  h->P = P;
+  h->K = K;
+  h->nb = L.nb;
+  h->Mp = L.Mp;
+  h->np = L.np;
+  h->bytes = L.bytes;
+  h->exp_off = L.exp_off;
+  // Partials of the split reduction: one float per (batch column, panel, row).
+  h->work_bytes = (size_t)SEEDLM_MAX_BATCH * L.np * L.Mp * sizeof(float);
+
+  int rc = SEEDLM_OK;
+  if (hipGetDevice(&h->device) != hipSuccess) rc = SEEDLM_E_DEVICE;
+  if (rc == SEEDLM_OK && hipMalloc(&h->d_buf, L.bytes) != hipSuccess) rc = SEEDLM_E_NOMEM;
+  if (rc == SEEDLM_OK && hipMalloc((void**)&h->d_work, h->work_bytes) != hipSuccess)
+    rc = SEEDLM_E_NOMEM;
+  if (rc == SEEDLM_OK && hipMemcpy(h->d_buf, host, L.bytes, hipMemcpyHostToDevice) != hipSuccess)
+    rc = SEEDLM_E_DEVICE;
+  hipHostFree(host);
+  if (rc != SEEDLM_OK) {
+    seedlm_destroy(h);
+    return rc;
+  }
+  *out = h;
+  return SEEDLM_OK;
+}
+
+int seedlm_destroy(seedlm_handle h) {
+  if (!h) return SEEDLM_OK;
+  int rc = SEEDLM_OK;
+  if (h->d_buf && hipFree(h->d_buf) != hipSuccess) rc = SEEDLM_E_DEVICE;
+  if (h->d_work && hipFree(h->d_work) != hipSuccess) rc = SEEDLM_E_DEVICE;
+  if (h->d_ext_table && hipFree(h->d_ext_table) != hipSuccess) rc = SEEDLM_E_DEVICE;
+  delete h;
+  return rc;
+}
+
+int seedlm_info(seedlm_handle h, seedlm_info_t* info) {
+  if (!h || !info) return SEEDLM_E_INVALID;
+  info->rows = h->rows;
+  info->cols = h->cols;
+  info->C = h->C;
+  info->P = h->P;
+  info->K = h->K;
+  info->blocks_per_row = h->nb;
+  info->padded_rows = h->Mp;
+  info->compressed_bytes = (int64_t)h->bytes;
+  return SEEDLM_OK;
+}
+
+int seedlm_export(seedlm_handle h, void* host, size_t* bytes) {
+  if (!h || !bytes) return SEEDLM_E_INVALID;
+  if (!host) {
+    *bytes = h->bytes;
+    return SEEDLM_OK;
+  }
+  if (*bytes < h->bytes) {
+    *bytes = h->bytes;
+    return SEEDLM_E_INVALID;
+  }
+  SEEDLM_HIP_CHECK(hipMemcpy(host, h->d_buf, h->bytes, hipMemcpyDeviceToHost));
+  *bytes = h->bytes;
+  return SEEDLM_OK;
+}
+
+}  // extern "C"

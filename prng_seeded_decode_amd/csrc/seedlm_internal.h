@@ -1,0 +1,81 @@
+// Internal declarations shared by the host packer, the launch wrappers and the
+// HIP kernels of libseedlm.  Not part of the public ABI (see include/seedlm.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/seedlm.h"
+
+namespace seedlm {
+
+// Packed layout constants (documented in include/seedlm.h).
+constexpr int kPanelBlocks = 32;  // blocks per panel
+constexpr int kQuadRows = 4;      // rows per quad
+constexpr int kStateBits = 16;    // K
+constexpr uint32_t kHalf = 1u << (kStateBits - 1);
+constexpr uint32_t kPadWord = 0x00000001u;  // seed 1, t = 0, g = 0
+
+}  // namespace seedlm
+
+// The handle.  Immutable after seedlm_pack except for the workspace contents.
+struct seedlm_matrix {
+  int64_t rows = 0, cols = 0;
+  int C = 0, P = 0, K = 0;
+  int64_t nb = 0;       // blocks per row
+  int64_t Mp = 0;       // rows padded to a multiple of 4
+  int64_t np = 0;       // panels per row: ceil(nb / 32)
+  size_t bytes = 0;     // packed buffer size
+  size_t exp_off = 0;   // byte offset of the exponent nibble array (P == 4)
+  int device = 0;
+  void* d_buf = nullptr;      // packed buffer (device)
+  float* d_work = nullptr;    // split-reduction partials (device)
+  size_t work_bytes = 0;
+  uint32_t* d_ext_table = nullptr;  // 2^16-entry extension table (variant TABLE)
+};
+
+namespace seedlm {
+
+// Layout helpers (host and device).
+__host__ __device__ inline int64_t panel_width(int64_t p, int64_t nb) {
+  int64_t w = nb - (int64_t)kPanelBlocks * p;
+  return w < kPanelBlocks ? w : kPanelBlocks;
+}
+
+__host__ __device__ inline int64_t word_index(int64_t r, int64_t b, int64_t Mp, int64_t nb) {
+  int64_t p = b / kPanelBlocks, q = b % kPanelBlocks;
+  int64_t Qp = panel_width(p, nb);
+  int64_t quad = r / kQuadRows, r4 = r % kQuadRows;
+  return p * Mp * kPanelBlocks + (quad * Qp + q) * kQuadRows + r4;
+}
+
+__host__ __device__ inline int64_t exp_index(int64_t r, int64_t b, int64_t Mp, int64_t nb) {
+  int64_t p = b / kPanelBlocks, q = b % kPanelBlocks;
+  int64_t Qp = panel_width(p, nb);
+  int64_t quad = r / kQuadRows;
+  return p * (Mp / kQuadRows) * kPanelBlocks + quad * Qp + q;
+}
+
+// Launch wrappers implemented in the .hip files.  All return a status code.
+int launch_decode(const seedlm_matrix* h, float* W, hipStream_t s);
+int launch_gemv_simple(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt,
+                       int ydt, hipStream_t s);
+int launch_gemv_lut(const seedlm_matrix* h, const void* x, void* y, int xdt, int ydt,
+                    bool global_table, hipStream_t s);
+int launch_gemm_skinny(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt,
+                       int ydt, hipStream_t s);
+int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,
+                     int batch, hipStream_t s);
+int build_ext_table(seedlm_matrix* h);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace seedlm
+
+#define SEEDLM_HIP_CHECK(expr)                 \
+  do {                                         \
+    hipError_t _e = (expr);                    \
+    if (_e != hipSuccess) return SEEDLM_E_DEVICE; \
+  } while (0)

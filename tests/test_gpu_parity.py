@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (written here, applied below):
+  * seedlm_decode: bit-exact fp32 (the integer block sum times a power of two
+    is exact in fp32).
+  * seedlm_gemv, normwise error max|y - y_ref| / max|y_ref| against the
+    float64 oracle: <= 1e-5 for fp32 output, <= 2e-3 for fp16 output.
+Small cases run the oracle on every output; the full configuration shapes are
+checked on sampled rows, which the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import seedlm_oracle as O
+from workloads import CONFIGS, gen_records, gen_x
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3}
+
+
+def _S():
+    import prng_seeded_decode_amd as S
+
+    return S
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _pack(seeds, coeffs, exps, rows, cols, C, P):
+    return _S().seedlm_pack(seeds, coeffs, exps, rows, cols, C, P, 16)
+
+
+def _decode_gpu(m, rows, cols):
+    W = torch.empty((rows, cols), dtype=torch.float32, device=_dev())
+    _S().seedlm_decode(m, W)
+    torch.cuda.synchronize()
+    return W
+
+
+def _gemv_gpu(m, x_np, ydt, variant=0):
+    dev = _dev()
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(dev)
+    y = torch.empty((x.shape[0], m.rows), dtype=torch.float16 if ydt == "f16" else torch.float32,
+                    device=dev)
+    _S().seedlm_gemv(m, x, y, batch=x.shape[0], variant=variant)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def _random_records(rng, rows, cols, C, P, erange=(-15, 0)):
+    nb = math.ceil(cols / C)
+    s = rng.integers(1, 65536, (rows, nb)).astype(np.uint16)
+    c = rng.integers(-8, 8, (rows, nb, P)).astype(np.int8)
+    e = rng.integers(erange[0], erange[1] + 1, (rows, nb)).astype(np.int8)
+    return s, c, e
+
+
+SMALL = [
+    # (C, P, rows, cols, batch, xdt, ydt)
+    (8, 3, 512, 512, 1, "f32", "f32"),
+    (8, 3, 37, 8 * 45 + 5, 1, "f16", "f16"),
+    (8, 3, 300, 8 * 70, 1, "f16", "f32"),
+    (8, 3, 64, 1000, 1, "f32", "f16"),
+    (12, 4, 30, 12 * 70 + 7, 1, "f16", "f16"),
+    (12, 4, 129, 4096, 1, "f16", "f32"),
+    (8, 3, 40, 520, 4, "f16", "f16"),
+    (8, 3, 33, 8 * 33, 8, "f16", "f16"),
+    (12, 4, 70, 12 * 40 + 4, 16, "f16", "f16"),
+    (12, 4, 20, 300, 3, "f32", "f32"),
+    (8, 3, 1, 1, 1, "f32", "f32"),
+    (12, 4, 1, 5, 2, "f16", "f16"),
+]
+
+
+@pytest.mark.parametrize("C,P,rows,cols,batch,xdt,ydt", SMALL,
+                         ids=[f"C{c[0]}_{c[2]}x{c[3]}_b{c[4]}_{c[5]}{c[6]}" for c in SMALL])
+def test_small_full_parity(C, P, rows, cols, batch, xdt, ydt):
+    rng = np.random.default_rng(rows * 7919 + cols * 31 + batch)
+    s, c, e = _random_records(rng, rows, cols, C, P)
+    m = _pack(s, c, e, rows, cols, C, P)
+    W_ref = O.decode_rows(s, c, e, cols, C, P)
+    _say(f"decode C={C} {rows}x{cols}")
+    W = _decode_gpu(m, rows, cols).cpu().numpy()
+    assert np.array_equal(W, W_ref.astype(np.float32)), "decode must be bit-exact"
+    x = rng.standard_normal((batch, cols)).astype(np.float16 if xdt == "f16" else np.float32)
+    y_ref = O.gemv(W_ref, x)
+    _say(f"gemv C={C} {rows}x{cols} batch={batch} {xdt}->{ydt}")
+    y = _gemv_gpu(m, x, ydt)
+    assert O.normwise_error(y, y_ref) <= TOL[ydt]
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3], ids=["auto", "lut", "table", "simple"])
+@pytest.mark.parametrize("C,P,rows,cols", [(8, 3, 203, 8 * 97 + 3), (12, 4, 96, 12 * 77 + 8)])
+def test_variants_agree_with_oracle(variant, C, P, rows, cols):
+    S = _S()
+    rng = np.random.default_rng(variant + 100 * rows)
+    s, c, e = _random_records(rng, rows, cols, C, P)
+    m = _pack(s, c, e, rows, cols, C, P)
+    W_ref = O.decode_rows(s, c, e, cols, C, P)
+    for xdt, ydt in (("f16", "f16"), ("f32", "f32"), ("f16", "f32")):
+        x = rng.standard_normal((1, cols)).astype(np.float16 if xdt == "f16" else np.float32)
+        _say(f"variant {variant} C={C} {rows}x{cols} {xdt}->{ydt}")
+        try:
+            y = _gemv_gpu(m, x, ydt, variant=variant)
+        except S.SeedLMError as err:
+            if err.status == S.E_UNSUPPORTED:
+                pytest.skip(f"variant {variant} not available for C={C}")
+            raise
+        assert O.normwise_error(y, O.gemv(W_ref, x)) <= TOL[ydt]
+
+
+def test_edge_records_extremes():
+    # All coefficients at the ends of the 4-bit range, exponents at both ends,
+    # seeds 1 and 65535, zero activations, and a single-column matrix.
+    rows, cols, C, P = 16, 8 * 40, 8, 3
+    nb = cols // C
+    s = np.where(np.arange(rows * nb).reshape(rows, nb) % 2 == 0, 1, 65535).astype(np.uint16)
+    c = np.full((rows, nb, P), -8, np.int8)
+    c[::2] = 7
+    e = np.zeros((rows, nb), np.int8)
+    e[:, ::3] = -15
+    m = _pack(s, c, e, rows, cols, C, P)
+    W_ref = O.decode_rows(s, c, e, cols, C, P)
+    W = _decode_gpu(m, rows, cols).cpu().numpy()
+    assert np.array_equal(W, W_ref.astype(np.float32))
+    x0 = np.zeros((1, cols), np.float32)
+    assert np.all(_gemv_gpu(m, x0, "f32") == 0)
+    x = np.random.default_rng(1).standard_normal((1, cols)).astype(np.float32)
+    assert O.normwise_error(_gemv_gpu(m, x, "f32"), O.gemv(W_ref, x)) <= TOL["f32"]
+
+
+def test_repeated_runs_are_bit_identical():
+    rng = np.random.default_rng(99)
+    rows, cols, C, P = 1024, 4096, 8, 3
+    s, c, e = _random_records(rng, rows, cols, C, P, (-12, -6))
+    m = _pack(s, c, e, rows, cols, C, P)
+    x = rng.standard_normal((1, cols)).astype(np.float16)
+    ys = [_gemv_gpu(m, x, "f16") for _ in range(3)]
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+
+
+def _sample_rows(rows, rng, n=16):
+    picks = set(range(min(4, rows))) | set(range(max(0, rows - 4), rows))
+    picks |= set(int(v) for v in rng.choice(rows, size=min(n, rows), replace=False))
+    return np.array(sorted(picks))
+
+
+FULL = []
+for cid in (1, 2, 3, 4):
+    cfg = CONFIGS[cid]
+    for mid, mat in enumerate(cfg.matrices):
+        FULL.append((cid, mid))
+
+
+@pytest.mark.parametrize("cid,mid", FULL,
+                         ids=[f"c{c}_{CONFIGS[c].matrices[m].name}" for c, m in FULL])
+def test_full_size_sampled_parity(cid, mid):
+    cfg = CONFIGS[cid]
+    mat = cfg.matrices[mid]
+    rows, cols, C, P = mat.rows, mat.cols, cfg.C, cfg.P
+    s, c, e = gen_records(cid, mid, rows, cols, C, P)
+    m = _pack(s, c, e, rows, cols, C, P)
+    rng = np.random.default_rng([cid, mid, 777])
+    pick = _sample_rows(rows, rng)
+    W_ref = O.decode_rows(s[pick], c[pick], e[pick], cols, C, P)
+    _say(f"full decode c{cid} {mat.name} {rows}x{cols}")
+    W = _decode_gpu(m, rows, cols)
+    Wp = W[torch.from_numpy(pick).to(W.device)].cpu().numpy()
+    del W
+    assert np.array_equal(Wp, W_ref.astype(np.float32)), "decode must be bit-exact"
+    ydt = cfg.x_dtype
+    for batch in cfg.batches:
+        x = gen_x(cid, mid, batch, cols, cfg.x_dtype)
+        _say(f"full gemv c{cid} {mat.name} {rows}x{cols} batch={batch}")
+        y = _gemv_gpu(m, x, ydt)
+        y_ref = O.gemv(W_ref, x)
+        assert O.normwise_error(y[:, pick], y_ref) <= TOL[ydt], (cid, mat.name, batch)
+
+
+def test_fp16_gemv_baseline_against_torch_fp32():
+    dev = _dev()
+    S = _S()
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for rows, cols, batch in ((4096, 4096, 1), (1024, 8192, 8), (300, 520, 3)):
+        W = torch.randn(rows, cols, generator=g).half()
+        x = torch.randn(batch, cols, generator=g).half()
+        ref = (x.float() @ W.float().T).numpy()
+        Wd, xd = W.to(dev), x.to(dev)
+        y = torch.empty(batch, rows, dtype=torch.float16, device=dev)
+        _say(f"fp16 gemv {rows}x{cols} b{batch}")
+        S.seedlm_fp16_gemv(Wd, xd, y, batch=batch)
+        torch.cuda.synchronize()
+        assert O.normwise_error(y.float().cpu().numpy(), ref) <= TOL["f16"]

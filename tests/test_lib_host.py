@@ -1,0 +1,103 @@
+"""CPU-only tests of the C-ABI library: it loads, exports every symbol the
+header declares, and its host packer writes exactly the layout the oracle's
+own writer produces (and rejects bad records with the documented status)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    import prng_seeded_decode_amd as S
+
+    return S
+
+
+def test_library_exports_every_declared_symbol():
+    S = _lib()
+    header = open(os.path.join(ROOT, "include", "seedlm.h")).read()
+    names = re.findall(r"SEEDLM_API\s+[\w\s\*]+?\b(seedlm_\w+)\s*\(", header)
+    assert len(names) >= 10
+    L = S.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(S._binding.EXPORTED)
+
+
+def test_status_strings():
+    S = _lib()
+    for code in (S.OK, S.E_INVALID, S.E_UNSUPPORTED, S.E_NOMEM, S.E_DEVICE):
+        assert S.status_string(code) not in ("", "unknown status")
+    assert S.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("C,P,rows,cols", [
+    (8, 3, 1, 1), (8, 3, 5, 320), (8, 3, 9, 8 * 77 + 3), (12, 4, 6, 401), (12, 4, 4, 12 * 64),
+])
+def test_host_packer_matches_oracle_writer_and_reader(C, P, rows, cols):
+    S = _lib()
+    from oracle import seedlm_oracle as O
+
+    rng = np.random.default_rng(rows * 1000 + cols)
+    nb = -(-cols // C)
+    s = rng.integers(1, 65536, (rows, nb)).astype(np.uint16)
+    c = rng.integers(-8, 8, (rows, nb, P)).astype(np.int8)
+    e = rng.integers(-15, 1, (rows, nb)).astype(np.int8)
+    buf = S.seedlm_pack_host(s, c, e, rows, cols, C, P)
+    assert buf == O.write_packed(s, c, e, rows, cols, C, P)
+    s2, c2, e2 = O.read_packed(buf, rows, cols, C, P)
+    assert (s2 == s).all() and (c2 == c).all() and (e2 == e).all()
+
+
+def test_host_packer_rejects_bad_records():
+    S = _lib()
+    rows, cols = 3, 20
+    s = np.ones((rows, 3), np.uint16)
+    c = np.zeros((rows, 3, 3), np.int8)
+    e = np.zeros((rows, 3), np.int8)
+    assert S.pack_host_status(s, c, e, rows, cols, 8, 3) == S.OK
+    bad = s.copy(); bad[1, 2] = 0
+    assert S.pack_host_status(bad, c, e, rows, cols, 8, 3) == S.E_INVALID
+    bad = c.copy(); bad[0, 0, 1] = 8
+    assert S.pack_host_status(s, bad, e, rows, cols, 8, 3) == S.E_INVALID
+    bad = c.copy(); bad[0, 0, 1] = -9
+    assert S.pack_host_status(s, bad, e, rows, cols, 8, 3) == S.E_INVALID
+    bad = e.copy(); bad[2, 0] = 1
+    assert S.pack_host_status(s, c, bad, rows, cols, 8, 3) == S.E_INVALID
+    bad = e.copy(); bad[2, 0] = -16
+    assert S.pack_host_status(s, c, bad, rows, cols, 8, 3) == S.E_INVALID
+    assert S.pack_host_status(s, c, e, 0, cols, 8, 3) == S.E_INVALID
+    assert S.pack_host_status(s, c, e, rows, 0, 8, 3) == S.E_INVALID
+    assert S.pack_host_status(s, c, e, rows, cols, 8, 3, K=12) == S.E_UNSUPPORTED
+    assert S.pack_host_status(s, c, e, rows, cols, 8, 4) == S.E_UNSUPPORTED
+    assert S.pack_host_status(s, c, e, rows, cols, 16, 3) == S.E_UNSUPPORTED
+    # null pointers and a too-small destination
+    L = S.lib()
+    n = ctypes.c_size_t(0)
+    assert L.seedlm_pack_host(None, None, None, rows, cols, 8, 3, 16, None, ctypes.byref(n)) == S.E_INVALID
+    sp = s.ctypes.data_as(ctypes.c_void_p)
+    cp = c.ctypes.data_as(ctypes.c_void_p)
+    ep = e.ctypes.data_as(ctypes.c_void_p)
+    assert L.seedlm_pack_host(sp, cp, ep, rows, cols, 8, 3, 16, None, None) == S.E_INVALID
+    assert L.seedlm_pack_host(sp, cp, ep, rows, cols, 8, 3, 16, None, ctypes.byref(n)) == S.OK
+    assert n.value == 4 * 4 * 3
+    small = ctypes.create_string_buffer(8)
+    n2 = ctypes.c_size_t(8)
+    assert L.seedlm_pack_host(sp, cp, ep, rows, cols, 8, 3, 16, ctypes.cast(small, ctypes.c_void_p),
+                              ctypes.byref(n2)) == S.E_INVALID
+
+
+def test_device_entry_points_reject_null_handles_without_touching_the_gpu():
+    S = _lib()
+    L = S.lib()
+    x = ctypes.c_void_p(16)
+    assert L.seedlm_gemv(None, x, x, 1, S.F16, S.F16, None) == S.E_INVALID
+    assert L.seedlm_decode(None, x, None) == S.E_INVALID
+    assert L.seedlm_destroy(None) == S.OK
+    assert L.seedlm_info(None, None) == S.E_INVALID
+    assert L.seedlm_fp16_gemv(None, x, x, 4, 8, 1, None) == S.E_INVALID
+    assert L.seedlm_fp16_gemv(x, x, x, 4, 12, 1, None) == S.E_INVALID
