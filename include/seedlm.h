@@ -29,13 +29,16 @@
  *             24..27 t2 (two's-complement nibbles);
  *             (C,P)=(8,3):  bits 28..31 g = e + 15;
  *             (C,P)=(12,4): bits 28..31 t3, and g sits in a nibble array.
- *   panels    rows padded to Mp = 4*ceil(rows/4) (padding words = 0x00000001),
- *             blocks grouped in panels of 32; word (r, b) with p = b/32,
- *             q = b%32, Qp = width of panel p, quad = r/4, r4 = r%4 is at
- *             index p*Mp*32 + (quad*Qp + q)*4 + r4.  For (12,4) the exponent
- *             nibble of (r, b) is nibble r4 of uint16 number
- *             p*(Mp/4)*32 + quad*Qp + q of an array starting at byte
- *             align256(4*Mp*nb) of the same buffer.
+ *   panels    rows are padded to Mp = 8*ceil(rows/8); blocks are grouped in
+ *             panels of 32: panel p holds blocks 32p .. 32p+Wp-1,
+ *             Wp = min(32, nb-32p), stored Wp' = 4*ceil(Wp/4) slots wide.
+ *             Padding (rows >= rows, slots >= Wp) holds pad words 0x00000001
+ *             (seed 1, t = 0, g = 0).  Panel p starts at word p*Mp*32 and stores
+ *             its Mp rows one after another, Wp' words each; slot q of row r
+ *             sits at 4*(q/4) + ((q-r) mod 4) of the row (groups of four slots
+ *             rotated by the row index).  For (12,4) the exponent of (r, b) is
+ *             nibble ((q-r) mod 4) of uint16 number p*Mp*8 + r*(Wp'/4) + q/4
+ *             of an array starting at byte align256(4 * total words).
  *   Supported (C, P, K): (8, 3, 16) -- 4 bits per weight; (12, 4, 16) -- 3 bits
  *   per weight (36 bits per 12-weight block).
  *
@@ -79,7 +82,7 @@ typedef struct seedlm_info_t {
   int64_t cols;             /* N */
   int32_t C, P, K;
   int64_t blocks_per_row;   /* nb = ceil(N / C) */
-  int64_t padded_rows;      /* Mp = 4 * ceil(M / 4) */
+  int64_t stored_blocks_per_row; /* nb with the last panel padded to 4 slots */
   int64_t compressed_bytes; /* size of the packed buffer, padding included */
 } seedlm_info_t;
 

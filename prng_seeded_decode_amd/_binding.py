@@ -54,7 +54,7 @@ class _Info(ctypes.Structure):
         ("P", ctypes.c_int32),
         ("K", ctypes.c_int32),
         ("blocks_per_row", ctypes.c_int64),
-        ("padded_rows", ctypes.c_int64),
+        ("stored_blocks_per_row", ctypes.c_int64),
         ("compressed_bytes", ctypes.c_int64),
     ]
 
@@ -168,7 +168,7 @@ class SeedLMMatrix:
         self.cols = info.cols
         self.C, self.P, self.K = info.C, info.P, info.K
         self.blocks_per_row = info.blocks_per_row
-        self.padded_rows = info.padded_rows
+        self.stored_blocks_per_row = info.stored_blocks_per_row
         self.compressed_bytes = info.compressed_bytes
 
     @property

@@ -63,7 +63,17 @@ int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch, int 
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
     case SEEDLM_VARIANT_AUTO:
+      if (batch == 1 && h->C == 8) return launch_gemv_lut(h, x, y, x_dtype, y_dtype, false, s);
       return launch_gemv_simple(h, x, y, batch, x_dtype, y_dtype, s);
+    case SEEDLM_VARIANT_LUT:
+      if (batch != 1) return SEEDLM_E_UNSUPPORTED;
+      return launch_gemv_lut(h, x, y, x_dtype, y_dtype, false, s);
+    case SEEDLM_VARIANT_TABLE: {
+      if (batch != 1 || h->C != 8) return SEEDLM_E_UNSUPPORTED;
+      st = build_ext_table(h);
+      if (st != SEEDLM_OK) return st;
+      return launch_gemv_lut(h, x, y, x_dtype, y_dtype, true, s);
+    }
     case SEEDLM_VARIANT_SIMPLE:
       return launch_gemv_simple(h, x, y, batch, x_dtype, y_dtype, s);
     default:

@@ -28,7 +28,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint32_t* __restrict_
   if constexpr (P == 3) {
     g = (int)(w >> 28);
   } else {
-    g = (exps[exp_index(r, b, Mp, nb)] >> (4 * (r % kQuadRows))) & 0xF;
+    g = (exps[exp_index(r, b, Mp, nb)] >> (4 * exp_nibble(r, b))) & 0xF;
   }
   const uint64_t stream = lfsr_stream<C * P + 15>(w);
   int t[P];

@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(256) gemv_simple_kernel(const uint32_t* __rest
     if constexpr (P == 3) {
       g = (int)(w >> 28);
     } else {
-      g = (exps[exp_index(r, b, Mp, nb)] >> (4 * (r % kQuadRows))) & 0xF;
+      g = (exps[exp_index(r, b, Mp, nb)] >> (4 * exp_nibble(r, b))) & 0xF;
     }
     const uint64_t stream = lfsr_stream<C * P + 15>(w);
     int t[P];

@@ -2,8 +2,8 @@
 //
 // The packed buffer holds one 32-bit word per block {seed, coefficients,
 // biased shared exponent} (4-bit format) or {seed, coefficients} plus a nibble
-// array of exponents (3-bit format), grouped into 32-block panels and 4-row
-// quads.  The record itself is the pages' {seed s, coefficients t, shared
+// array of exponents (3-bit format), grouped into 32-block panels whose rows
+// hold groups of four slots rotated by the row index.  The record itself is the pages' {seed s, coefficients t, shared
 // exponent} (atlas.scime.ai "Approach"; paperhub.cn rebuttal on shared
 // exponents); the bit positions and the panel order are this library's.
 #include <stdlib.h>
@@ -23,22 +23,23 @@ bool supported(int C, int P, int K) {
 }
 
 struct Layout {
-  int64_t nb, Mp, np, nwords;
+  int64_t nb, nbs, np, Mp, nwords;
   size_t exp_off, bytes;
 };
 
 Layout make_layout(int64_t rows, int64_t cols, int C, int P) {
   Layout L;
   L.nb = (cols + C - 1) / C;
-  L.Mp = (rows + kQuadRows - 1) / kQuadRows * kQuadRows;
   L.np = (L.nb + kPanelBlocks - 1) / kPanelBlocks;
-  L.nwords = L.Mp * L.nb;
+  L.nbs = (L.np - 1) * kPanelBlocks + panel_stored_width(L.np - 1, L.nb);
+  L.Mp = padded_rows(rows);
+  L.nwords = L.Mp * L.nbs;
   if (P == 3) {
     L.exp_off = 0;
     L.bytes = (size_t)L.nwords * 4;
   } else {
     L.exp_off = ((size_t)L.nwords * 4 + 255) / 256 * 256;
-    L.bytes = L.exp_off + (size_t)(L.Mp / kQuadRows) * L.nb * 2;
+    L.bytes = L.exp_off + (size_t)(L.nwords / kGroup) * 2;
   }
   return L;
 }
@@ -81,7 +82,7 @@ void write_layout(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exp
       if (P == 3) {
         w |= g << 28;
       } else {
-        ex[exp_index(r, b, L.Mp, L.nb)] |= (uint16_t)(g << (4 * (r % kQuadRows)));
+        ex[exp_index(r, b, L.Mp, L.nb)] |= (uint16_t)(g << (4 * exp_nibble(r, b)));
       }
       words[word_index(r, b, L.Mp, L.nb)] = w;
     }
@@ -147,8 +148,10 @@ int seedlm_pack(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps,
   h->P = P;
   h->K = K;
   h->nb = L.nb;
-  h->Mp = L.Mp;
+  h->nbs = L.nbs;
   h->np = L.np;
+  h->Mp = L.Mp;
+  h->nwords = L.nwords;
   h->bytes = L.bytes;
   h->exp_off = L.exp_off;
   // Partials of the split reduction: one float per (batch column, panel, row).
@@ -188,7 +191,7 @@ int seedlm_info(seedlm_handle h, seedlm_info_t* info) {
   info->P = h->P;
   info->K = h->K;
   info->blocks_per_row = h->nb;
-  info->padded_rows = h->Mp;
+  info->stored_blocks_per_row = h->nbs;
   info->compressed_bytes = (int64_t)h->bytes;
   return SEEDLM_OK;
 }

@@ -12,7 +12,7 @@ namespace seedlm {
 
 // Packed layout constants (documented in include/seedlm.h).
 constexpr int kPanelBlocks = 32;  // blocks per panel
-constexpr int kQuadRows = 4;      // rows per quad
+constexpr int kGroup = 4;         // slots per rotated group (one 16-byte load)
 constexpr int kStateBits = 16;    // K
 constexpr uint32_t kHalf = 1u << (kStateBits - 1);
 constexpr uint32_t kPadWord = 0x00000001u;  // seed 1, t = 0, g = 0
@@ -24,8 +24,10 @@ struct seedlm_matrix {
   int64_t rows = 0, cols = 0;
   int C = 0, P = 0, K = 0;
   int64_t nb = 0;       // blocks per row
-  int64_t Mp = 0;       // rows padded to a multiple of 4
+  int64_t nbs = 0;      // stored blocks per row (last panel padded to 4 slots)
   int64_t np = 0;       // panels per row: ceil(nb / 32)
+  int64_t Mp = 0;       // rows padded to a multiple of 8
+  int64_t nwords = 0;   // Mp * nbs
   size_t bytes = 0;     // packed buffer size
   size_t exp_off = 0;   // byte offset of the exponent nibble array (P == 4)
   int device = 0;
@@ -37,24 +39,36 @@ struct seedlm_matrix {
 
 namespace seedlm {
 
-// Layout helpers (host and device).
+// Layout helpers (host and device).  Rows are padded to Mp = 8*ceil(rows/8).
+// Panel p holds blocks 32p .. 32p+Wp-1; its stored width is Wp rounded up to a
+// multiple of 4.  Panel p starts at word p*Mp*32 and stores its Mp rows one
+// after another; inside a row, slot q sits at 4*(q/4) + ((q - r) mod 4), so the
+// four words of one 16-byte load hold the group's slots rotated by the row.
 __host__ __device__ inline int64_t panel_width(int64_t p, int64_t nb) {
   int64_t w = nb - (int64_t)kPanelBlocks * p;
   return w < kPanelBlocks ? w : kPanelBlocks;
 }
 
-__host__ __device__ inline int64_t word_index(int64_t r, int64_t b, int64_t Mp, int64_t nb) {
-  int64_t p = b / kPanelBlocks, q = b % kPanelBlocks;
-  int64_t Qp = panel_width(p, nb);
-  int64_t quad = r / kQuadRows, r4 = r % kQuadRows;
-  return p * Mp * kPanelBlocks + (quad * Qp + q) * kQuadRows + r4;
+__host__ __device__ inline int64_t panel_stored_width(int64_t p, int64_t nb) {
+  return (panel_width(p, nb) + kGroup - 1) / kGroup * kGroup;
 }
 
+__host__ __device__ inline int64_t padded_rows(int64_t rows) { return (rows + 7) / 8 * 8; }
+
+__host__ __device__ inline int64_t word_index(int64_t r, int64_t b, int64_t Mp, int64_t nb) {
+  const int64_t p = b / kPanelBlocks, q = b % kPanelBlocks;
+  return p * Mp * kPanelBlocks + r * panel_stored_width(p, nb) + (q & ~(int64_t)3) +
+         ((q - r) & 3);
+}
+
+// Index of the uint16 that holds the exponent nibbles of (r, b)'s group, and the
+// nibble number inside it (3-bit format).
 __host__ __device__ inline int64_t exp_index(int64_t r, int64_t b, int64_t Mp, int64_t nb) {
-  int64_t p = b / kPanelBlocks, q = b % kPanelBlocks;
-  int64_t Qp = panel_width(p, nb);
-  int64_t quad = r / kQuadRows;
-  return p * (Mp / kQuadRows) * kPanelBlocks + quad * Qp + q;
+  const int64_t p = b / kPanelBlocks, q = b % kPanelBlocks;
+  return p * Mp * (kPanelBlocks / kGroup) + r * (panel_stored_width(p, nb) / kGroup) + q / kGroup;
+}
+__host__ __device__ inline int exp_nibble(int64_t r, int64_t b) {
+  return (int)(((b % kPanelBlocks) - r) & 3);
 }
 
 // Launch wrappers implemented in the .hip files.  All return a status code.

@@ -84,7 +84,7 @@ def test_host_packer_rejects_bad_records():
     ep = e.ctypes.data_as(ctypes.c_void_p)
     assert L.seedlm_pack_host(sp, cp, ep, rows, cols, 8, 3, 16, None, None) == S.E_INVALID
     assert L.seedlm_pack_host(sp, cp, ep, rows, cols, 8, 3, 16, None, ctypes.byref(n)) == S.OK
-    assert n.value == 4 * 4 * 3
+    assert n.value == 4 * 4 * 8  # 3 rows padded to 8, 3 blocks padded to 4 slots
     small = ctypes.create_string_buffer(8)
     n2 = ctypes.c_size_t(8)
     assert L.seedlm_pack_host(sp, cp, ep, rows, cols, 8, 3, 16, ctypes.cast(small, ctypes.c_void_p),

@@ -13,10 +13,10 @@ def test_golden_word(golden):
     coeffs = np.array([[[int(v) for v in g["t"]]]], np.int8)
     exps = np.array([[int(g["e"][0])]], np.int8)
     buf = O.write_packed(seeds, coeffs, exps, 1, 8, 8, 3)
-    # one real row + 3 padding rows of one block each
-    assert len(buf) == 16
+    # one row, one block; rows are padded to 8 and the panel to 4 slots
+    assert len(buf) == 4 * 8 * 4
     assert int.from_bytes(buf[0:4], "little") == int(g["word"][0], 16)
-    for k in (1, 2, 3):
+    for k in range(1, 32):
         assert int.from_bytes(buf[4 * k:4 * k + 4], "little") == 1
     s, c, e = O.read_packed(buf, 1, 8, 8, 3)
     assert (s == seeds).all() and (c == coeffs).all() and (e == exps).all()
@@ -32,40 +32,55 @@ def _unique_records(rows, nb, P):
 
 def test_word_positions_worked_by_hand_4bit():
     # rows=5 -> Mp=8; cols=320 -> nb=40: panel 0 has 32 blocks, panel 1 has 8.
+    # word(r, b) = p*8*32 + r*Wp' + 4*(q//4) + ((q - r) mod 4)
     rows, cols = 5, 320
     seeds, coeffs, exps = _unique_records(rows, 40, 3)
     buf = O.write_packed(seeds, coeffs, exps, rows, cols, 8, 3)
-    assert len(buf) == 4 * 8 * 40
+    assert len(buf) == 4 * (8 * 32 + 8 * 8)
 
     def seed_at(k):
         return int.from_bytes(buf[4 * k:4 * k + 2], "little")
 
-    # (r, b) -> word index, by hand from p*Mp*32 + (quad*Qp + q)*4 + r4
-    cases = {(0, 0): 0, (3, 1): 7, (4, 0): 128, (2, 33): 262, (4, 39): 316, (1, 31): 125}
+    cases = {(0, 0): 0, (3, 1): 98, (4, 0): 128, (2, 33): 275, (4, 39): 295, (1, 31): 62}
     for (r, b), k in cases.items():
         assert seed_at(k) == seeds[r, b], (r, b, k)
-    # padding rows (r = 5..7) hold the word 0x00000001
-    for r4 in (1, 2, 3):
-        assert int.from_bytes(buf[4 * (128 + r4):4 * (128 + r4) + 4], "little") == 1
+    # padding rows 5..7 of panel 0 start at word 5*32 = 160
+    assert all(int.from_bytes(buf[4 * k:4 * k + 4], "little") == 1 for k in range(160, 256))
     assert O.padding_words_ok(buf, rows, cols, 8, 3)
 
 
+def test_narrow_last_panel_is_padded_to_four_slots():
+    # rows = 3 -> Mp = 8; cols = 8*37 -> nb = 37: panel 1 has 5 blocks, padded to 8 slots.
+    rows, cols = 3, 8 * 37
+    seeds, coeffs, exps = _unique_records(rows, 37, 3)
+    buf = O.write_packed(seeds, coeffs, exps, rows, cols, 8, 3)
+    assert len(buf) == 4 * (8 * 32 + 8 * 8)
+    assert O.padding_words_ok(buf, rows, cols, 8, 3)
+    # row 2, block 36 (panel 1, q=4): 256 + 2*8 + 4 + ((4-2) mod 4) = 278
+    assert int.from_bytes(buf[4 * 278:4 * 278 + 2], "little") == seeds[2, 36]
+    # row 1, slot 6 is padding: position 4 + ((6-1) mod 4) = 5 -> word 256 + 8 + 5 = 269
+    assert int.from_bytes(buf[4 * 269:4 * 269 + 4], "little") == 1
+
+
 def test_exponent_positions_worked_by_hand_3bit():
-    # rows=5 -> Mp=8; cols=36 -> nb=3 (one panel of width 3); 24 words = 96 B;
-    # the exponent array starts at byte 256 and holds (8/4)*3 = 6 uint16.
+    # rows=5 -> Mp=8; cols=36 -> nb=3: one panel, width 3 padded to 4; 32 words
+    # = 128 B; the exponent array starts at byte 256 and holds 8 uint16 (one per row).
     rows, cols = 5, 36
     seeds, coeffs, exps = _unique_records(rows, 3, 4)
     buf = O.write_packed(seeds, coeffs, exps, rows, cols, 12, 4)
-    assert len(buf) == 256 + 12
-    # (r=4, b=2): quad 1, q 2 -> uint16 number 1*3 + 2 = 5, nibble 0
-    v = int.from_bytes(buf[256 + 10:256 + 12], "little")
-    assert (v & 0xF) == exps[4, 2] + 15 and (v >> 4) == 0
-    # (r=1, b=0): quad 0, q 0 -> uint16 number 0, nibble 1
-    v = int.from_bytes(buf[256:258], "little")
-    assert ((v >> 4) & 0xF) == exps[1, 0] + 15
-    # the word of (r=1, b=0) holds t3 in bits 28..31
-    w = int.from_bytes(buf[4:8], "little")
-    assert w & 0xFFFF == seeds[1, 0]
+    assert len(buf) == 256 + 16
+    assert O.padding_words_ok(buf, rows, cols, 12, 4)
+    # (r=4, b=2): word 4*4 + ((2-4) mod 4) = 18; exponent uint16 number 4, nibble 2
+    assert int.from_bytes(buf[4 * 18:4 * 18 + 2], "little") == seeds[4, 2]
+    v = int.from_bytes(buf[256 + 8:256 + 10], "little")
+    assert ((v >> 8) & 0xF) == exps[4, 2] + 15
+    # (r=1, b=0): word 4 + ((0-1) mod 4) = 7; exponent uint16 number 1, nibble 3
+    assert int.from_bytes(buf[28:30], "little") == seeds[1, 0]
+    v = int.from_bytes(buf[256 + 2:256 + 4], "little")
+    assert ((v >> 12) & 0xF) == exps[1, 0] + 15
+    # (r=1, pad slot q=3): position (3-1) mod 4 = 2 -> word 6, pad word with g nibble 0
+    assert int.from_bytes(buf[24:28], "little") == 1
+    assert ((v >> 8) & 0xF) == 0
 
 
 @pytest.mark.parametrize("C,P,rows,cols", [(8, 3, 7, 8 * 70), (12, 4, 6, 12 * 33 + 5), (8, 3, 4, 3)])
