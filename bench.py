@@ -126,10 +126,19 @@ def main():
                      "bytes": copies[0].compressed_bytes})
     torch.cuda.synchronize()
 
-    def run_step(k):
-        for d in mats:
-            S.seedlm_gemv(d["copies"][k % args.copies], d["x"], d["y"], batch=batch,
-                          stream=stream, variant=args.variant)
+    xs_all = [d["x"] for d in mats]
+    ys_all = [d["y"] for d in mats]
+
+    def run_step(k, phase="all"):
+        # One step = the whole layer through seedlm_gemv_many (grouped launch);
+        # --variant != 0 times per-matrix seedlm_gemv calls of that variant.
+        if args.variant == 0:
+            S.seedlm_gemv_many([d["copies"][k % args.copies] for d in mats], xs_all, ys_all,
+                               batch=batch, stream=stream, phase=phase)
+        else:
+            for d in mats:
+                S.seedlm_gemv(d["copies"][k % args.copies], d["x"], d["y"], batch=batch,
+                              stream=stream, variant=args.variant)
 
     # ---- whole-step timing ----
     for k in range(args.warmup):
@@ -144,7 +153,7 @@ def main():
     ev1.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- per-launch timing (events bracket every launch on the launch stream) ----
+    # ---- per-matrix timing: one seedlm_gemv per matrix, events around each ----
     per = {d["mat"].name: [] for d in mats}
     evs = []
     for k in range(args.steps):
@@ -160,6 +169,22 @@ def main():
     for name, a, b in evs:
         per[name].append(a.elapsed_time(b))
 
+    # ---- the dominant kernel alone: events around the fused decode-GEMV launch
+    # of each step (seedlm_gemv_many_begin), the panel reduction outside them ----
+    kern_ms = []
+    if args.variant == 0:
+        kev = []
+        for k in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run_step(k, "begin")
+            b.record(stream)
+            run_step(k, "end")
+            kev.append((a, b))
+        torch.cuda.synchronize()
+        kern_ms = [a.elapsed_time(b) for a, b in kev]
+
     layer_weights = sum(d["mat"].rows * d["mat"].cols for d in mats)
     layer_bytes = sum(d["bytes"] for d in mats)
     act_bytes = sum(batch * (d["mat"].cols + d["mat"].rows) * (2 if ydt == torch.float16 else 4)
@@ -174,10 +199,16 @@ def main():
             "compressed_GBps": round(d["bytes"] / t / 1e9, 1),
             "weights_per_s": d["mat"].rows * d["mat"].cols / t,
         }
-    # Dominant kernel: the fused decode-GEMV; its launches over one step.
-    launch_s = [np.mean(per[d["mat"].name]) * 1e-3 for d in mats]
-    alg_bytes = [d["bytes"] + batch * (d["mat"].cols + d["mat"].rows) * 2 for d in mats]
-    achieved = (np.mean(alg_bytes) / np.mean(launch_s)) / 1e9
+    # Roofline of the dominant kernel (the fused decode-GEMV launch of a step):
+    # algorithmic bytes = the layer's packed words (0.5 B per weight, padding
+    # included) + the activations x it reads, over the launch's mean duration.
+    x_bytes = sum(batch * d["mat"].cols * (2 if xdt == torch.float16 else 4) for d in mats)
+    if kern_ms:
+        alg_bytes = layer_bytes + x_bytes
+        achieved = alg_bytes / (float(np.mean(kern_ms)) * 1e-3) / 1e9
+    else:
+        alg_bytes = layer_bytes / len(mats)
+        achieved = alg_bytes / (float(np.mean([np.mean(per[d["mat"].name]) for d in mats])) * 1e-3) / 1e9
     t_step = ms_per_step * 1e-3
 
     # ---- fp16 baselines on the same shapes ----
@@ -243,6 +274,8 @@ def main():
         "pct_hbm_peak": round(100 * layer_bytes / t_step / 1e9 / HBM_PEAK_GBPS, 2),
         "activation_bytes_per_step": act_bytes,
         "per_matrix": per_matrix,
+        "kernel_us_per_launch": round(float(np.mean(kern_ms)) * 1e3, 2) if kern_ms else None,
+        "kernel_alg_bytes_per_launch": int(alg_bytes),
         "roofline": {
             "bound": "hbm",
             "achieved": round(float(achieved), 1),

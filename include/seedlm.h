@@ -135,6 +135,37 @@ SEEDLM_API int seedlm_gemv(seedlm_handle h, const void* x, void* y, int batch,
                            int x_dtype, int y_dtype, void* stream);
 
 /*
+ * seedlm_gemv_many -- y[i] = W_i x[i] for n matrices, same result as n calls
+ * of seedlm_gemv on `stream`.  Consecutive batch-1 4-bit matrices are run
+ * together (up to 8 per launch) so that small matrices share the GPU and the
+ * per-launch cost is paid once; a decoder layer's q/k/v/o/gate/up/down is the
+ * intended use (the pages' inference step, applied to every weight matrix:
+ * paperhub.cn rebuttal text before Eq. (1)).
+ *   handles  host array of n distinct handles (each call uses its handle's
+ *            workspace, so a handle may appear only once)
+ *   x, y     host arrays of n device pointers, layouts as for seedlm_gemv
+ * Errors: as seedlm_gemv; SEEDLM_E_INVALID for a repeated handle.
+ */
+SEEDLM_API int seedlm_gemv_many(const seedlm_handle* handles, const void* const* x,
+                                void* const* y, int n, int batch, int x_dtype, int y_dtype,
+                                void* stream);
+
+/*
+ * seedlm_gemv_many_begin / seedlm_gemv_many_end -- seedlm_gemv_many split in
+ * its two launches: _begin runs the fused decode-GEMV kernel (per-panel row
+ * partials into the handles' workspaces), _end adds the partials into y.  Called
+ * back to back with identical arguments they equal seedlm_gemv_many; the split
+ * lets a caller time or overlap the two halves.  Between the two calls the
+ * handles must not be used by any other call.
+ */
+SEEDLM_API int seedlm_gemv_many_begin(const seedlm_handle* handles, const void* const* x,
+                                      void* const* y, int n, int batch, int x_dtype,
+                                      int y_dtype, void* stream);
+SEEDLM_API int seedlm_gemv_many_end(const seedlm_handle* handles, const void* const* x,
+                                    void* const* y, int n, int batch, int x_dtype, int y_dtype,
+                                    void* stream);
+
+/*
  * seedlm_decode -- write the dense weights W[rows][cols] as fp32 (row-major,
  * caller-owned device memory).  Bit-exact: the block's integer sum times a
  * power of two is exact in fp32.  Asynchronous on `stream`.

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     seedlm_export,
     seedlm_fp16_gemv,
     seedlm_gemv,
+    seedlm_gemv_many,
     seedlm_pack,
     seedlm_pack_host,
     status_string,

@@ -31,6 +31,9 @@ EXPORTED = (
     "seedlm_pack",
     "seedlm_gemv",
     "seedlm_gemv_variant",
+    "seedlm_gemv_many",
+    "seedlm_gemv_many_begin",
+    "seedlm_gemv_many_end",
     "seedlm_decode",
     "seedlm_destroy",
     "seedlm_info",
@@ -77,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.seedlm_pack.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, ctypes.POINTER(vp)]
     L.seedlm_gemv.argtypes = [vp, vp, vp, i32, i32, i32, vp]
     L.seedlm_gemv_variant.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    L.seedlm_gemv_many.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    L.seedlm_gemv_many_begin.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    L.seedlm_gemv_many_end.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
     L.seedlm_decode.argtypes = [vp, vp, vp]
     L.seedlm_destroy.argtypes = [vp]
     L.seedlm_info.argtypes = [vp, ctypes.POINTER(_Info)]
@@ -211,6 +217,33 @@ def seedlm_gemv(m: SeedLMMatrix, x, y, batch=None, stream=None, variant=VARIANT_
                                      _dtype_code(y), variant, _stream_ptr(stream)),
            "seedlm_gemv")
     return y
+
+
+def seedlm_gemv_many(mats, xs, ys, batch=1, stream=None, phase="all"):
+    """ys[i] = W_i xs[i] for several packed matrices, in as few launches as possible.
+
+    phase "begin" / "end" runs only seedlm_gemv_many_begin / _end."""
+    n = len(mats)
+    if not (len(xs) == n and len(ys) == n):
+        raise ValueError("mats, xs and ys must have the same length")
+    for m, x, y in zip(mats, xs, ys):
+        if x.numel() != batch * m.cols or y.numel() != batch * m.rows:
+            raise ValueError("x must hold batch*cols and y batch*rows elements")
+        if not (x.is_cuda and y.is_cuda and x.is_contiguous() and y.is_contiguous()):
+            raise ValueError("x and y must be contiguous device tensors")
+        if x.dtype != xs[0].dtype or y.dtype != ys[0].dtype:
+            raise ValueError("all x (and all y) must share one dtype")
+    H = (ctypes.c_void_p * n)(*[m.handle.value for m in mats])
+    X = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    xdt = _dtype_code(xs[0]) if n else F16
+    ydt = _dtype_code(ys[0]) if n else F16
+    fn = {"all": lib().seedlm_gemv_many, "begin": lib().seedlm_gemv_many_begin,
+          "end": lib().seedlm_gemv_many_end}[phase]
+    _check(fn(ctypes.cast(H, ctypes.c_void_p), ctypes.cast(X, ctypes.c_void_p),
+              ctypes.cast(Y, ctypes.c_void_p), n, batch, xdt, ydt, _stream_ptr(stream)),
+           "seedlm_gemv_many")
+    return ys
 
 
 def seedlm_decode(m: SeedLMMatrix, W_out, stream=None):

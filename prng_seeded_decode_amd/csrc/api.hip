@@ -86,6 +86,64 @@ int seedlm_gemv(seedlm_handle h, const void* x, void* y, int batch, int x_dtype,
   return seedlm_gemv_variant(h, x, y, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, stream);
 }
 
+namespace {
+
+// Shared body of seedlm_gemv_many{,_begin,_end}: phases & 1 runs the main
+// kernels, phases & 2 the panel reductions.  Matrices outside the grouped
+// batch-1 4-bit path run their whole seedlm_gemv in phase 1.
+int gemv_many_phases(const seedlm_handle* handles, const void* const* x, void* const* y, int n,
+                     int batch, int x_dtype, int y_dtype, void* stream, int phases) {
+  if (!handles || !x || !y || n < 0) return SEEDLM_E_INVALID;
+  for (int i = 0; i < n; ++i) {
+    const int st = check_common(handles[i], x[i], y[i], batch, x_dtype, y_dtype);
+    if (st != SEEDLM_OK) return st;
+    for (int j = 0; j < i; ++j)
+      if (handles[j] == handles[i]) return SEEDLM_E_INVALID;  // shared workspace
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int i = 0;
+  while (i < n) {
+    // Group consecutive batch-1 4-bit matrices (up to 8) into one launch pair.
+    int k = 0;
+    while (batch == 1 && i + k < n && k < 8 && handles[i + k]->C == 8 &&
+           handles[i + k]->bytes < 0x80000000ull)
+      ++k;
+    if (k >= 1) {
+      const seedlm_matrix* hs[8];
+      for (int j = 0; j < k; ++j) hs[j] = handles[i + j];
+      const int st =
+          launch_gemv_lut_group(hs, x + i, y + i, k, x_dtype, y_dtype, false, s, phases);
+      if (st != SEEDLM_OK) return st;
+      i += k;
+    } else {
+      if (phases & 1) {
+        const int st = seedlm_gemv_variant(handles[i], x[i], y[i], batch, x_dtype, y_dtype,
+                                           SEEDLM_VARIANT_AUTO, stream);
+        if (st != SEEDLM_OK) return st;
+      }
+      ++i;
+    }
+  }
+  return SEEDLM_OK;
+}
+
+}  // namespace
+
+int seedlm_gemv_many(const seedlm_handle* handles, const void* const* x, void* const* y, int n,
+                     int batch, int x_dtype, int y_dtype, void* stream) {
+  return gemv_many_phases(handles, x, y, n, batch, x_dtype, y_dtype, stream, 3);
+}
+
+int seedlm_gemv_many_begin(const seedlm_handle* handles, const void* const* x, void* const* y,
+                           int n, int batch, int x_dtype, int y_dtype, void* stream) {
+  return gemv_many_phases(handles, x, y, n, batch, x_dtype, y_dtype, stream, 1);
+}
+
+int seedlm_gemv_many_end(const seedlm_handle* handles, const void* const* x, void* const* y,
+                         int n, int batch, int x_dtype, int y_dtype, void* stream) {
+  return gemv_many_phases(handles, x, y, n, batch, x_dtype, y_dtype, stream, 2);
+}
+
 int seedlm_decode(seedlm_handle h, float* W_out, void* stream) {
   if (!h || !W_out) return SEEDLM_E_INVALID;
   return launch_decode(h, W_out, static_cast<hipStream_t>(stream));

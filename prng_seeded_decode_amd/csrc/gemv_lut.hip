@@ -38,6 +38,8 @@
 // reduce_panels_kernel adds the panels in a fixed order (deterministic).
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
 #include "lfsr_device.h"
 #include "seedlm_internal.h"
 
@@ -53,10 +55,38 @@ struct Smem {
   uint32_t B[256][64];  // [T0 (32 copies) | L2 (32 slots)]
   float xs[256];
   float c7x2[32];
+  uint32_t gf2[512];    // T0 then T1, staged before replication
 };
 constexpr uint32_t kRegionB = 65536;  // byte offset of B inside Smem
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Up to kMaxGroup matrices share one launch; their work items are numbered one
+// after another (matrix-major, then panel, then 8-row slab).
+constexpr int kMaxGroup = 8;
+struct LutMatrix {
+  const uint32_t* words;
+  const void* x;
+  float* partial;
+  void* y;
+  uint32_t words_bytes;
+  int Mp, rows, cols, nb, np;
+  int64_t item_begin;  // first global work item of this matrix
+  int row_begin;       // first row of this matrix in the concatenated output
+};
+constexpr int kMaxWorkgroups = 512;
+struct LutGroup {
+  LutMatrix m[kMaxGroup];
+  int n;
+  int total_rows;
+  int grid;
+  // Workgroup w processes global work items [bounds[w], bounds[w+1]).
+  int32_t bounds[kMaxWorkgroups + 1];
+};
+
+// Cost model of the work split: a panel's table build costs about as much as
+// kBuildCost slabs of 8 rows.
+constexpr int64_t kBuildCost = 24;
 
 template <typename XT>
 __device__ inline float ldx(const XT* p);
@@ -139,22 +169,30 @@ __device__ void build_panel_lut(Smem& sm, const XT* __restrict__ x, int64_t cols
 
 template <typename XT, bool kGlobalTable>
 __global__ void __launch_bounds__(kThreads, 1)
-    gemv_lut_kernel(const uint32_t* __restrict__ words, uint32_t words_bytes,
-                    const XT* __restrict__ x, float* __restrict__ partial,
-                    const uint32_t* __restrict__ ext_table, int64_t Mp, int64_t cols,
-                    int64_t nb, int64_t np) {
+    gemv_lut_kernel(const LutGroup grp, const uint32_t* __restrict__ ext_table) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rho = lane >> 3, g = lane & 7;
   const uint8_t* lds = reinterpret_cast<const uint8_t*>(&sm);
 
-  // Per-slot copies of the GF(2) tables (built once per launch).
-  if (!kGlobalTable && tid < 512) {
-    const uint32_t u = tid & 255;
-    const uint32_t val = tid < 256 ? ext_bits<uint32_t>(u) : ext_bits<uint32_t>(u << 8);
-    uint4* dst = reinterpret_cast<uint4*>(tid < 256 ? &sm.B[u][0] : &sm.A[u][32]);
+  // Per-slot copies of the GF(2) tables (built once per launch): 512 values
+  // staged, then replicated with 16-byte writes where consecutive lanes write
+  // consecutive addresses (no bank conflicts).
+  if (!kGlobalTable) {
+    if (tid < 512) {
+      const uint32_t u = tid & 255;
+      sm.gf2[tid] = tid < 256 ? ext_bits<uint32_t>(u) : ext_bits<uint32_t>(u << 8);
+    }
+    __syncthreads();
+    // 2 tables x 256 rows x 8 uint4 (32 copies) = 4096 uint4 stores.
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dst[k] = make_uint4(val, val, val, val);
+    for (int k = 0; k < 4096 / kThreads; ++k) {
+      const int e = tid + k * kThreads;
+      const int tab = e >> 11, u = (e >> 3) & 255, part = e & 7;
+      const uint32_t val = sm.gf2[tab * 256 + u];
+      uint4* dst = reinterpret_cast<uint4*>(tab == 0 ? &sm.B[u][0] : &sm.A[u][32]);
+      dst[part] = make_uint4(val, val, val, val);
+    }
   }
 
   // Slots of this lane's four words: slot_j = 4g + ((j + row) & 3); slabs start
@@ -168,27 +206,30 @@ __global__ void __launch_bounds__(kThreads, 1)
     lcB[j] = lcA[j] | kRegionB;
   }
 
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)words, 0, (int)words_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t prsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)partial, 0, (int)(np * Mp * 4), 0x00020000);
-
-  // Work items: (panel, 8-row slab), panel-major; each workgroup takes one
-  // contiguous range.
-  const int slabs = (int)(Mp / 8);
-  const int64_t total = np * slabs;
-  const int64_t G = gridDim.x;
-  const int64_t begin = (int64_t)blockIdx.x * total / G;
-  const int64_t end = ((int64_t)blockIdx.x + 1) * total / G;
+  // Each workgroup takes one contiguous range of the group's work items; the
+  // host split them so that every range has about the same cost.
+  const int64_t begin = grp.bounds[blockIdx.x];
+  const int64_t end = grp.bounds[blockIdx.x + 1];
 
   for (int64_t it = begin; it < end;) {
-    const int64_t p = it / slabs;
-    const int sa = (int)(it - p * slabs);
-    const int64_t seg_end = (p + 1) * slabs < end ? (p + 1) * slabs : end;
-    const int sb = (int)(seg_end - p * slabs);
-    const int Wp = (int)panel_stored_width(p, nb);
+    int mi = 0;
+    while (mi + 1 < grp.n && it >= grp.m[mi + 1].item_begin) ++mi;
+    const LutMatrix& M = grp.m[mi];
+    const int64_t Mp = M.Mp, np = M.np;
+    const int slabs = M.Mp / 8;
+    const int64_t local = it - M.item_begin;
+    const int64_t p = local / slabs;
+    const int sa = (int)(local - p * slabs);
+    const int64_t seg_stop = M.item_begin + (p + 1) * slabs;
+    const int64_t seg_end = seg_stop < end ? seg_stop : end;
+    const int sb = (int)(seg_end - M.item_begin - p * slabs);
+    const int Wp = (int)panel_stored_width(p, M.nb);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)M.words, 0, (int)M.words_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t prsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)M.partial, 0, (int)(np * Mp * 4), 0x00020000);
     __syncthreads();  // previous panel's tables no longer in use
-    build_panel_lut<XT>(sm, x, cols, p);
+    build_panel_lut<XT>(sm, static_cast<const XT*>(M.x), M.cols, p);
     __syncthreads();
     float c7j[4];
 #pragma unroll
@@ -275,70 +316,140 @@ __device__ inline void store_y<float>(float* p, float v) { *p = v; }
 template <>
 __device__ inline void store_y<__half>(__half* p, float v) { *p = __float2half_rn(v); }
 
-// y[r] = sum over panels of partial[p][r]: four lanes per row each add the
-// panels p = part, part+4, part+8, ... (four loads issued at once), then the
-// four sums combine as (0+1) + (2+3) with two DPP steps.  Fixed order for a
-// given panel count, so repeated calls give identical results.
+// y[r] = sum over panels of partial[p][r]: eight lanes per row; lane `part`
+// adds panels part, part+8, part+16, ... with up to 16 loads in flight, then
+// the eight sums combine with three DPP steps ((0+1)+(2+3)) + ((4+5)+(6+7)).
+// Fixed order for a given panel count, so repeated calls give identical
+// results.  Rows of the group's matrices are numbered one after another.
 template <typename YT>
-__global__ void __launch_bounds__(256) reduce_panels_kernel(const float* __restrict__ partial,
-                                                            YT* __restrict__ y, int64_t rows,
-                                                            int64_t Mp, int64_t np) {
-  const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 2;
-  const int part = threadIdx.x & 3;
-  const bool ok = r < rows;
+__global__ void __launch_bounds__(256) reduce_panels_kernel(const LutGroup grp) {
+  const int rg = (int)(((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3);
+  const int part = threadIdx.x & 7;
+  int mi = 0;
+  while (mi + 1 < grp.n && rg >= grp.m[mi + 1].row_begin) ++mi;
+  const LutMatrix& M = grp.m[mi];
+  const int r = rg - M.row_begin;
+  const bool ok = rg < grp.total_rows;
+  const int rr = ok ? r : 0;  // keep loads in bounds; no store below
+  const float* __restrict__ partial = M.partial;
+  const int64_t Mp = M.Mp, np = M.np;
   float s = 0.f;
-  int64_t p = part;
-  for (; p + 12 < np; p += 16) {
-    float v[4];
+  for (int64_t p0 = part; p0 < np; p0 += 8 * 16) {
+    float v[16];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = ok ? partial[(p + 4 * k) * Mp + r] : 0.f;
+    for (int k = 0; k < 16; ++k) {
+      const int64_t p = p0 + 8 * k;
+      v[k] = p < np ? partial[p * Mp + rr] : 0.f;
+    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) s += v[k];
+    for (int k = 0; k < 16; ++k) s += v[k];
   }
-  for (; p < np; p += 4) s += ok ? partial[p * Mp + r] : 0.f;
-  s += dpp<0xB1>(s);  // lanes (0,1), (2,3)
-  s += dpp<0x4E>(s);  // (0+1) + (2+3)
-  if (ok && part == 0) store_y(y + r, s);
+  s += dpp<0xB1>(s);   // xor 1
+  s += dpp<0x4E>(s);   // xor 2
+  s += dpp<0x141>(s);  // mirror within 8 lanes
+  if (ok && part == 0) store_y(static_cast<YT*>(M.y) + r, s);
+}
+
+bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys, int n,
+                LutGroup& grp) {
+  if (n < 1 || n > kMaxGroup) return false;
+  grp = LutGroup{};
+  grp.n = n;
+  int64_t items = 0;
+  int64_t rows = 0;
+  for (int i = 0; i < n; ++i) {
+    const seedlm_matrix* h = hs[i];
+    if (h->C != 8 || h->P != 3 || h->bytes >= 0x80000000ull) return false;
+    if (h->Mp >= (1 << 28) || h->cols >= (1 << 30)) return false;
+    LutMatrix& M = grp.m[i];
+    M.words = static_cast<const uint32_t*>(h->d_buf);
+    M.x = xs[i];
+    M.partial = h->d_work;
+    M.y = ys[i];
+    M.words_bytes = (uint32_t)h->bytes;
+    M.Mp = (int)h->Mp;
+    M.rows = (int)h->rows;
+    M.cols = (int)h->cols;
+    M.nb = (int)h->nb;
+    M.np = (int)h->np;
+    M.item_begin = items;
+    M.row_begin = (int)rows;
+    items += h->np * (h->Mp / 8);
+    rows += h->rows;
+  }
+  if (rows >= (1LL << 30) || items >= (1LL << 31)) return false;
+  grp.total_rows = (int)rows;
+  // Split the items into G ranges of equal cost: one unit per 8-row slab plus
+  // kBuildCost per panel a range starts or enters (its table build).
+  int64_t G = device_cu_count();
+  if (G > kMaxWorkgroups) G = kMaxWorkgroups;
+  if (G > items) G = items;
+  // Costs accumulate panel by panel: a range that enters a panel pays the
+  // build once, then one unit per slab.  One sweep places every boundary.
+  int64_t total_cost = 0;
+  for (int i = 0; i < n; ++i) total_cost += (int64_t)grp.m[i].np * (grp.m[i].Mp / 8 + kBuildCost);
+  grp.bounds[0] = 0;
+  int64_t w = 1, acc = 0;
+  for (int i = 0; i < n && w < G; ++i) {
+    const int64_t slabs = grp.m[i].Mp / 8;
+    for (int64_t p = 0; p < grp.m[i].np && w < G; ++p) {
+      const int64_t start = grp.m[i].item_begin + p * slabs;
+      const int64_t next = acc + kBuildCost + slabs;  // cost before the next panel
+      for (; w < G && w * total_cost / G <= next; ++w) {
+        const int64_t t = w * total_cost / G;
+        const int64_t j = t <= acc ? 0 : std::max<int64_t>(1, t - acc - kBuildCost);
+        grp.bounds[w] = (int32_t)(start + j);
+      }
+      acc = next;
+    }
+  }
+  for (; w < G; ++w) grp.bounds[w] = (int32_t)items;
+  grp.bounds[G] = (int32_t)items;
+  grp.grid = (int)G;
+  return true;
 }
 
 template <typename XT, bool kGT>
-void launch_main(const seedlm_matrix* h, const void* x, const uint32_t* table, hipStream_t s) {
-  const int64_t total = h->np * (h->Mp / 8);
-  int64_t G = device_cu_count();
-  if (G > total) G = total;
-  hipLaunchKernelGGL((gemv_lut_kernel<XT, kGT>), dim3((unsigned)G), dim3(kThreads), 0, s,
-                     static_cast<const uint32_t*>(h->d_buf), (uint32_t)h->bytes,
-                     static_cast<const XT*>(x), h->d_work, table, h->Mp, h->cols, h->nb, h->np);
+void launch_main(const LutGroup& grp, const uint32_t* table, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_lut_kernel<XT, kGT>), dim3((unsigned)grp.grid), dim3(kThreads), 0, s,
+                     grp, table);
 }
 
 }  // namespace
 
+int launch_gemv_lut_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys,
+                          int n, int xdt, int ydt, bool global_table, hipStream_t s, int phases) {
+  LutGroup grp;
+  if (!fill_group(hs, xs, ys, n, grp)) return SEEDLM_E_UNSUPPORTED;
+  if (phases & 1) {
+    const uint32_t* table = nullptr;
+    if (global_table) {
+      if (n != 1 || !hs[0]->d_ext_table) return SEEDLM_E_INVALID;
+      table = hs[0]->d_ext_table;
+    }
+    if (xdt == SEEDLM_F32) {
+      if (global_table) launch_main<float, true>(grp, table, s);
+      else launch_main<float, false>(grp, table, s);
+    } else {
+      if (global_table) launch_main<__half, true>(grp, table, s);
+      else launch_main<__half, false>(grp, table, s);
+    }
+    SEEDLM_HIP_CHECK(hipGetLastError());
+  }
+  if (phases & 2) {
+    const int64_t grid = ((int64_t)grp.total_rows * 8 + 255) / 256;
+    if (ydt == SEEDLM_F32)
+      hipLaunchKernelGGL((reduce_panels_kernel<float>), dim3((unsigned)grid), dim3(256), 0, s, grp);
+    else
+      hipLaunchKernelGGL((reduce_panels_kernel<__half>), dim3((unsigned)grid), dim3(256), 0, s, grp);
+    SEEDLM_HIP_CHECK(hipGetLastError());
+  }
+  return SEEDLM_OK;
+}
+
 int launch_gemv_lut(const seedlm_matrix* h, const void* x, void* y, int xdt, int ydt,
                     bool global_table, hipStream_t s) {
-  if (h->C != 8 || h->P != 3) return SEEDLM_E_UNSUPPORTED;
-  if (h->bytes >= 0x80000000ull) return SEEDLM_E_UNSUPPORTED;  // 32-bit buffer offsets
-  const uint32_t* table = nullptr;
-  if (global_table) {
-    if (!h->d_ext_table) return SEEDLM_E_INVALID;
-    table = h->d_ext_table;
-  }
-  if (xdt == SEEDLM_F32) {
-    if (global_table) launch_main<float, true>(h, x, table, s);
-    else launch_main<float, false>(h, x, table, s);
-  } else {
-    if (global_table) launch_main<__half, true>(h, x, table, s);
-    else launch_main<__half, false>(h, x, table, s);
-  }
-  SEEDLM_HIP_CHECK(hipGetLastError());
-  const int64_t grid = (h->rows * 4 + 255) / 256;
-  if (ydt == SEEDLM_F32)
-    hipLaunchKernelGGL((reduce_panels_kernel<float>), dim3((unsigned)grid), dim3(256), 0, s,
-                       h->d_work, static_cast<float*>(y), h->rows, h->Mp, h->np);
-  else
-    hipLaunchKernelGGL((reduce_panels_kernel<__half>), dim3((unsigned)grid), dim3(256), 0, s,
-                       h->d_work, static_cast<__half*>(y), h->rows, h->Mp, h->np);
-  SEEDLM_HIP_CHECK(hipGetLastError());
-  return SEEDLM_OK;
+  return launch_gemv_lut_group(&h, &x, &y, 1, xdt, ydt, global_table, s, 3);
 }
 
 }  // namespace seedlm

@@ -77,6 +77,10 @@ int launch_gemv_simple(const seedlm_matrix* h, const void* x, void* y, int batch
                        int ydt, hipStream_t s);
 int launch_gemv_lut(const seedlm_matrix* h, const void* x, void* y, int xdt, int ydt,
                     bool global_table, hipStream_t s);
+// Up to 8 batch-1 4-bit matrices in one main launch (phases & 1: panel
+// partials into the handles' workspaces) and one reduce launch (phases & 2: y).
+int launch_gemv_lut_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys,
+                          int n, int xdt, int ydt, bool global_table, hipStream_t s, int phases);
 int launch_gemm_skinny(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt,
                        int ydt, hipStream_t s);
 int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,

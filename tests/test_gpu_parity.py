@@ -203,3 +203,71 @@ def test_fp16_gemv_baseline_against_torch_fp32():
         S.seedlm_fp16_gemv(Wd, xd, y, batch=batch)
         torch.cuda.synchronize()
         assert O.normwise_error(y.float().cpu().numpy(), ref) <= TOL["f16"]
+
+
+def test_gemv_many_matches_oracle_and_single_calls():
+    S = _S()
+    dev = _dev()
+    rng = np.random.default_rng(4242)
+    shapes = [(8, 3, 300, 1000), (8, 3, 64, 8 * 40 + 3), (12, 4, 50, 600), (8, 3, 1000, 256),
+              (8, 3, 17, 5000), (8, 3, 8, 8)]
+    mats, refs, xs = [], [], []
+    for C, P, rows, cols in shapes:
+        s, c, e = _random_records(rng, rows, cols, C, P)
+        mats.append(_pack(s, c, e, rows, cols, C, P))
+        refs.append(O.decode_rows(s, c, e, cols, C, P))
+        xs.append(rng.standard_normal((1, cols)).astype(np.float16))
+    xd = [torch.from_numpy(x).to(dev) for x in xs]
+    for ydt in ("f16", "f32"):
+        tdt = torch.float16 if ydt == "f16" else torch.float32
+        ys = [torch.empty((1, m.rows), dtype=tdt, device=dev) for m in mats]
+        _say(f"gemv_many {len(mats)} matrices -> {ydt}")
+        S.seedlm_gemv_many(mats, xd, ys)
+        torch.cuda.synchronize()
+        for y, W_ref, x in zip(ys, refs, xs):
+            assert O.normwise_error(y.float().cpu().numpy(), O.gemv(W_ref, x)) <= TOL[ydt]
+        # begin + end gives the same bits as the one-shot call and as single calls
+        ys2 = [torch.empty_like(y) for y in ys]
+        S.seedlm_gemv_many(mats, xd, ys2, phase="begin")
+        S.seedlm_gemv_many(mats, xd, ys2, phase="end")
+        ys3 = [torch.empty_like(y) for y in ys]
+        for m, x, y in zip(mats, xd, ys3):
+            S.seedlm_gemv(m, x, y)
+        torch.cuda.synchronize()
+        for a, b, c3 in zip(ys, ys2, ys3):
+            assert torch.equal(a, b) and torch.equal(a, c3)
+
+
+def test_gemv_many_rejects_a_repeated_handle():
+    S = _S()
+    dev = _dev()
+    rng = np.random.default_rng(1)
+    s, c, e = _random_records(rng, 16, 64, 8, 3)
+    m = _pack(s, c, e, 16, 64, 8, 3)
+    x = torch.zeros((1, 64), dtype=torch.float16, device=dev)
+    ys = [torch.empty((1, 16), dtype=torch.float16, device=dev) for _ in range(2)]
+    with pytest.raises(S.SeedLMError):
+        S.seedlm_gemv_many([m, m], [x, x], ys)
+
+
+def test_full_layer_gemv_many_sampled():
+    # The launch configuration the benchmark times: the 70B layer in one call.
+    S = _S()
+    dev = _dev()
+    cfg = CONFIGS[4]
+    mats, recs, xs, ys = [], [], [], []
+    for mid, mat in enumerate(cfg.matrices):
+        s, c, e = gen_records(4, mid, mat.rows, mat.cols, cfg.C, cfg.P)
+        mats.append(_pack(s, c, e, mat.rows, mat.cols, cfg.C, cfg.P))
+        rng = np.random.default_rng([4, mid, 888])
+        pick = _sample_rows(mat.rows, rng, n=8)
+        recs.append((pick, O.decode_rows(s[pick], c[pick], e[pick], mat.cols, cfg.C, cfg.P)))
+        x = gen_x(4, mid, 1, mat.cols, "f16")
+        xs.append(x)
+        ys.append(torch.empty((1, mat.rows), dtype=torch.float16, device=dev))
+    _say("gemv_many over the Llama-3-70B layer")
+    S.seedlm_gemv_many(mats, [torch.from_numpy(x).to(dev) for x in xs], ys)
+    torch.cuda.synchronize()
+    for (pick, W_ref), x, y in zip(recs, xs, ys):
+        yv = y.float().cpu().numpy()[:, pick]
+        assert O.normwise_error(yv, O.gemv(W_ref, x)) <= TOL["f16"]
