@@ -30,6 +30,26 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+LUT_SOURCE = os.path.join(ROOT, "prng_seeded_decode_amd", "csrc", "gemv_lut.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lut_kernel_llama3_70b_layer_4bit_traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused kernel from the committed counter summary,
+    or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(None, 1) for line in f
+                      if line.strip() and not line.startswith("#"))
+        with open(LUT_SOURCE, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if kv.get("source_sha256", "").strip() != digest:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
 METRIC = "effective weights/s + compressed HBM GB/s (% peak), 4-bit decode-GEMV bs=1"
 
 
@@ -45,6 +65,12 @@ def parse_args():
     p.add_argument("--no-fp16", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--per-matrix", action="store_true",
+                   help="also time one seedlm_gemv per matrix (extra launches of the same kernels)")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="run one plain fp32 copy kernel of this many MiB first (counter calibration)")
+    p.add_argument("--graph", type=int, default=0,
+                   help="1: replay each step as a captured HIP graph (one per rotated copy)")
     return p.parse_args()
 
 
@@ -126,19 +152,49 @@ def main():
                      "bytes": copies[0].compressed_bytes})
     torch.cuda.synchronize()
 
+    if args.calib_copy_mib:
+        # A plain copy of known size: its counter readings scale the kernel's.
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     xs_all = [d["x"] for d in mats]
     ys_all = [d["y"] for d in mats]
 
-    def run_step(k, phase="all"):
+    def eager_step(k, phase="all", st=None):
         # One step = the whole layer through seedlm_gemv_many (grouped launch);
         # --variant != 0 times per-matrix seedlm_gemv calls of that variant.
+        st = stream if st is None else st
         if args.variant == 0:
             S.seedlm_gemv_many([d["copies"][k % args.copies] for d in mats], xs_all, ys_all,
-                               batch=batch, stream=stream, phase=phase)
+                               batch=batch, stream=st, phase=phase)
         else:
             for d in mats:
                 S.seedlm_gemv(d["copies"][k % args.copies], d["x"], d["y"], batch=batch,
-                              stream=stream, variant=args.variant)
+                              stream=st, variant=args.variant)
+
+    graphs = []
+    if args.graph:
+        # Capture one step per rotated copy; the library's launches go to the
+        # capturing stream, so a replay runs the same kernels with no host work.
+        for k in range(args.copies):
+            eager_step(k)
+        torch.cuda.synchronize()
+        for k in range(args.copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                eager_step(k, st=torch.cuda.current_stream())
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_step(k, phase="all"):
+        if graphs and phase == "all":
+            graphs[k % args.copies].replay()
+        else:
+            eager_step(k, phase)
 
     # ---- whole-step timing ----
     for k in range(args.warmup):
@@ -156,7 +212,7 @@ def main():
     # ---- per-matrix timing: one seedlm_gemv per matrix, events around each ----
     per = {d["mat"].name: [] for d in mats}
     evs = []
-    for k in range(args.steps):
+    for k in range(args.steps if args.per_matrix else 0):
         for d in mats:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
@@ -190,7 +246,7 @@ def main():
     act_bytes = sum(batch * (d["mat"].cols + d["mat"].rows) * (2 if ydt == torch.float16 else 4)
                     for d in mats)
     per_matrix = {}
-    for d in mats:
+    for d in mats if args.per_matrix else []:
         n = d["mat"].name
         t = float(np.median(per[n])) * 1e-3
         per_matrix[n] = {
@@ -203,12 +259,11 @@ def main():
     # algorithmic bytes = the layer's packed words (0.5 B per weight, padding
     # included) + the activations x it reads, over the launch's mean duration.
     x_bytes = sum(batch * d["mat"].cols * (2 if xdt == torch.float16 else 4) for d in mats)
+    alg_bytes = layer_bytes + x_bytes
     if kern_ms:
-        alg_bytes = layer_bytes + x_bytes
         achieved = alg_bytes / (float(np.mean(kern_ms)) * 1e-3) / 1e9
-    else:
-        alg_bytes = layer_bytes / len(mats)
-        achieved = alg_bytes / (float(np.mean([np.mean(per[d["mat"].name]) for d in mats])) * 1e-3) / 1e9
+    else:  # per-matrix variants: the step's launches together
+        achieved = alg_bytes / (ms_per_step * 1e-3) / 1e9
     t_step = ms_per_step * 1e-3
 
     # ---- fp16 baselines on the same shapes ----
@@ -269,11 +324,12 @@ def main():
             "weights_per_step": layer_weights,
             "rotated_copies": args.copies,
             "variant": args.variant,
+            "graph": bool(graphs),
         },
         "compressed_GBps": round(layer_bytes / t_step / 1e9, 1),
         "pct_hbm_peak": round(100 * layer_bytes / t_step / 1e9 / HBM_PEAK_GBPS, 2),
         "activation_bytes_per_step": act_bytes,
-        "per_matrix": per_matrix,
+        "per_matrix": per_matrix or None,
         "kernel_us_per_launch": round(float(np.mean(kern_ms)) * 1e3, 2) if kern_ms else None,
         "kernel_alg_bytes_per_launch": int(alg_bytes),
         "roofline": {
@@ -282,7 +338,9 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(float(achieved) / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            # counters were taken on the default workload (Llama-3-70B layer, batch 1)
+            "traffic": (measured_traffic() if kern_ms and args.config == 4 and batch == 1
+                        else None),
         },
         "fp16_baseline": fp16,
     }

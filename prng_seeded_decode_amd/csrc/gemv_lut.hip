@@ -72,13 +72,13 @@ struct LutMatrix {
   uint32_t words_bytes;
   int Mp, rows, cols, nb, np;
   int64_t item_begin;  // first global work item of this matrix
-  int row_begin;       // first row of this matrix in the concatenated output
+  int red_begin;       // first reduce workgroup of this matrix (64 rows each)
 };
 constexpr int kMaxWorkgroups = 512;
 struct LutGroup {
   LutMatrix m[kMaxGroup];
   int n;
-  int total_rows;
+  int red_blocks;  // reduce workgroups over all matrices
   int grid;
   // Workgroup w processes global work items [bounds[w], bounds[w+1]).
   int32_t bounds[kMaxWorkgroups + 1];
@@ -316,38 +316,40 @@ __device__ inline void store_y<float>(float* p, float v) { *p = v; }
 template <>
 __device__ inline void store_y<__half>(__half* p, float v) { *p = __float2half_rn(v); }
 
-// y[r] = sum over panels of partial[p][r]: eight lanes per row; lane `part`
-// adds panels part, part+8, part+16, ... with up to 16 loads in flight, then
-// the eight sums combine with three DPP steps ((0+1)+(2+3)) + ((4+5)+(6+7)).
-// Fixed order for a given panel count, so repeated calls give identical
-// results.  Rows of the group's matrices are numbered one after another.
+// Panel reduction: y[r] = sum over panels p of partial[p][r].  A workgroup owns
+// 64 consecutive rows of one matrix (lane = row, so every load reads 256
+// contiguous bytes); wave w adds panels w, w+4, w+8, ... with up to 16 loads in
+// flight, and the four wave sums combine through LDS as (w0+w1)+(w2+w3).  The
+// order is fixed for a given panel count, so repeated calls give identical
+// results.
 template <typename YT>
 __global__ void __launch_bounds__(256) reduce_panels_kernel(const LutGroup grp) {
-  const int rg = (int)(((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3);
-  const int part = threadIdx.x & 7;
+  __shared__ float wsum[4][64];
   int mi = 0;
-  while (mi + 1 < grp.n && rg >= grp.m[mi + 1].row_begin) ++mi;
+  while (mi + 1 < grp.n && (int)blockIdx.x >= grp.m[mi + 1].red_begin) ++mi;
   const LutMatrix& M = grp.m[mi];
-  const int r = rg - M.row_begin;
-  const bool ok = rg < grp.total_rows;
-  const int rr = ok ? r : 0;  // keep loads in bounds; no store below
-  const float* __restrict__ partial = M.partial;
-  const int64_t Mp = M.Mp, np = M.np;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int r = ((int)blockIdx.x - M.red_begin) * 64 + lane;
+  const int rr = r < M.rows ? r : M.rows - 1;  // in-bounds load; no store below
+  const float* __restrict__ partial = M.partial + rr;
+  const int np = M.np;
+  const int64_t Mp = M.Mp;
   float s = 0.f;
-  for (int64_t p0 = part; p0 < np; p0 += 8 * 16) {
+  for (int p0 = wv; p0 < np; p0 += 4 * 16) {
     float v[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const int64_t p = p0 + 8 * k;
-      v[k] = p < np ? partial[p * Mp + rr] : 0.f;
+      const int p = p0 + 4 * k;
+      v[k] = p < np ? partial[p * Mp] : 0.f;
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) s += v[k];
   }
-  s += dpp<0xB1>(s);   // xor 1
-  s += dpp<0x4E>(s);   // xor 2
-  s += dpp<0x141>(s);  // mirror within 8 lanes
-  if (ok && part == 0) store_y(static_cast<YT*>(M.y) + r, s);
+  wsum[wv][lane] = s;
+  __syncthreads();
+  if (wv == 0 && r < M.rows)
+    store_y(static_cast<YT*>(M.y) + r, (wsum[0][lane] + wsum[1][lane]) + (wsum[2][lane] + wsum[3][lane]));
 }
 
 bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys, int n,
@@ -356,7 +358,7 @@ bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* con
   grp = LutGroup{};
   grp.n = n;
   int64_t items = 0;
-  int64_t rows = 0;
+  int64_t red = 0;
   for (int i = 0; i < n; ++i) {
     const seedlm_matrix* h = hs[i];
     if (h->C != 8 || h->P != 3 || h->bytes >= 0x80000000ull) return false;
@@ -373,12 +375,12 @@ bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* con
     M.nb = (int)h->nb;
     M.np = (int)h->np;
     M.item_begin = items;
-    M.row_begin = (int)rows;
+    M.red_begin = (int)red;
     items += h->np * (h->Mp / 8);
-    rows += h->rows;
+    red += (h->rows + 63) / 64;
   }
-  if (rows >= (1LL << 30) || items >= (1LL << 31)) return false;
-  grp.total_rows = (int)rows;
+  if (red >= (1LL << 30) || items >= (1LL << 31)) return false;
+  grp.red_blocks = (int)red;
   // Split the items into G ranges of equal cost: one unit per 8-row slab plus
   // kBuildCost per panel a range starts or enters (its table build).
   int64_t G = device_cu_count();
@@ -437,7 +439,7 @@ int launch_gemv_lut_group(const seedlm_matrix* const* hs, const void* const* xs,
     SEEDLM_HIP_CHECK(hipGetLastError());
   }
   if (phases & 2) {
-    const int64_t grid = ((int64_t)grp.total_rows * 8 + 255) / 256;
+    const int64_t grid = grp.red_blocks;
     if (ydt == SEEDLM_F32)
       hipLaunchKernelGGL((reduce_panels_kernel<float>), dim3((unsigned)grid), dim3(256), 0, s, grp);
     else

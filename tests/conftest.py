@@ -29,3 +29,21 @@ def read_golden(name):
 @pytest.fixture
 def golden():
     return read_golden
+
+
+def pytest_collection_modifyitems(config, items):
+    # Tests marked gpu need a visible device; without one they are skipped,
+    # never run against a CPU stand-in.
+    gpu_items = [it for it in items if it.get_closest_marker("gpu")]
+    if not gpu_items:
+        return
+    try:
+        import torch
+
+        ok = torch.cuda.is_available()
+    except Exception:
+        ok = False
+    if not ok:
+        skip = pytest.mark.skip(reason="no GPU visible")
+        for it in gpu_items:
+            it.add_marker(skip)
