@@ -189,17 +189,26 @@ SEEDLM_API int seedlm_export(seedlm_handle h, void* host, size_t* bytes);
 SEEDLM_API const char* seedlm_status_string(int status);
 
 /*
- * Kernel variants of the batch-1 path, for A/B measurement only.  The default
- * (SEEDLM_VARIANT_AUTO) is what seedlm_gemv runs.
- *   SEEDLM_VARIANT_LUT     basis bits from GF(2) byte tables in LDS, dot with x
- *                          through per-panel activation byte tables in LDS
- *   SEEDLM_VARIANT_TABLE   basis bits from a 2^16-entry table resident in L2
- *   SEEDLM_VARIANT_SIMPLE  one wave per row, per-lane LFSR stepping
+ * Kernel variants, for A/B measurement.  The default (SEEDLM_VARIANT_AUTO) is
+ * what seedlm_gemv runs: LUT for batch 1 of the 4-bit format, MFMA for every
+ * other fp16-x/fp16-y call, SIMPLE otherwise (fp32 x or fp32 y, where the
+ * 1e-5 bar needs fp32 weights).
+ *   SEEDLM_VARIANT_LUT     batch 1, 4-bit: basis bits from GF(2) byte tables in
+ *                          LDS, dot with x through per-panel activation byte
+ *                          tables in LDS
+ *   SEEDLM_VARIANT_TABLE   as LUT, basis bits from a 2^16-entry table in L2
+ *   SEEDLM_VARIANT_SIMPLE  any shape: one wave per row, per-lane LFSR stepping,
+ *                          fp32 weights
+ *   SEEDLM_VARIANT_MFMA    fp16 x and y, any batch: each block decoded once to
+ *                          fp16 (weights x 2^10) in MFMA operand registers,
+ *                          v_mfma_f32_16x16x32_f16 over the batch (padded to
+ *                          16); SEEDLM_E_UNSUPPORTED for other dtypes
  */
 #define SEEDLM_VARIANT_AUTO 0
 #define SEEDLM_VARIANT_LUT 1
 #define SEEDLM_VARIANT_TABLE 2
 #define SEEDLM_VARIANT_SIMPLE 3
+#define SEEDLM_VARIANT_MFMA 4
 SEEDLM_API int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch,
                                    int x_dtype, int y_dtype, int variant, void* stream);
 

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     MAX_BATCH,
     OK,
     VARIANT_AUTO,
+    VARIANT_MFMA,
     VARIANT_LUT,
     VARIANT_SIMPLE,
     VARIANT_TABLE,

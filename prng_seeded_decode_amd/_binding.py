@@ -25,6 +25,7 @@ VARIANT_AUTO = 0
 VARIANT_LUT = 1
 VARIANT_TABLE = 2
 VARIANT_SIMPLE = 3
+VARIANT_MFMA = 4
 
 EXPORTED = (
     "seedlm_pack_host",

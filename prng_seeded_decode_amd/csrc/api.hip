@@ -64,6 +64,8 @@ int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch, int 
   switch (variant) {
     case SEEDLM_VARIANT_AUTO:
       if (batch == 1 && h->C == 8) return launch_gemv_lut(h, x, y, x_dtype, y_dtype, false, s);
+      if (x_dtype == SEEDLM_F16 && y_dtype == SEEDLM_F16)
+        return launch_gemv_mfma(h, x, y, batch, x_dtype, y_dtype, s);
       return launch_gemv_simple(h, x, y, batch, x_dtype, y_dtype, s);
     case SEEDLM_VARIANT_LUT:
       if (batch != 1) return SEEDLM_E_UNSUPPORTED;
@@ -76,6 +78,8 @@ int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch, int 
     }
     case SEEDLM_VARIANT_SIMPLE:
       return launch_gemv_simple(h, x, y, batch, x_dtype, y_dtype, s);
+    case SEEDLM_VARIANT_MFMA:
+      return launch_gemv_mfma(h, x, y, batch, x_dtype, y_dtype, s);
     default:
       return SEEDLM_E_UNSUPPORTED;
   }

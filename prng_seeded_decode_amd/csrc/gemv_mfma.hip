@@ -1,0 +1,341 @@
+// Skinny decode-GEMM on the matrix cores: y[b][r] = sum_c W[r][c] x[b][c] for
+// batch 2..16 (any batch works), both packed formats, fp16 x and fp16 y.
+//
+// SeedLM rebuilds each block's weights from its seed and coefficients right
+// where they are used (paperhub.cn rebuttal text before Eq. (1); atlas.scime.ai
+// "Approach").  With several activation vectors the rebuilt block is shared by
+// all of them, so here every block is decoded exactly once, straight into the
+// operand registers of v_mfma_f32_16x16x32_f16, and the batch dimension (padded
+// to 16) is the MFMA's N.  The decode itself is the exact integer one of
+// seedlm_decode: I_i = sum_j t_j (z_{jC+i} - 2^15), w_i = I_i 2^(e-15); it then
+// enters the MFMA as fp16(w_i * 2^10) (|w * 2^10| <= 32767, so no overflow),
+// and the result is scaled back by 2^-10.  fp16 weights bound this path to the
+// fp16-output tolerance; fp32-output calls use the exact kernels.
+//
+// Operand layout of v_mfma_f32_16x16x32_f16 (wave64): lane l supplies 8
+// consecutive k values of A row (l % 16) and of B column (l % 16), the k group
+// being l / 16; the 16x16 fp32 result gives lane l rows 4*(l/16)+v, column l%16.
+// A 4-bit block is 8 columns, so one lane decodes one block per MFMA; a 3-bit
+// lane decodes the four blocks of its 16-byte load (48 weights) and feeds them
+// to six MFMAs, 8 weights each.  Any assignment of blocks to k groups is a
+// valid MFMA as long as A and B agree; B (x) is read from LDS to match.
+//
+// Rows: a wave owns 64 rows r0..r0+63 (r0 a multiple of 8) and runs four MFMA
+// row groups rho = 0..3 of 16 rows {r0 + rho + 4i}.  The packed layout rotates
+// each 4-slot group by (row mod 4); inside one row group that rotation is the
+// same for all 16 rows, so a k group holds the same block for every row and the
+// shared B operand is right.
+//
+// Work split: a workgroup (4 waves, 256 rows) takes a contiguous chunk of
+// panels; chunks write fp32 partials into the handle's workspace and
+// reduce_chunks_kernel adds them in a fixed order (deterministic).  With a
+// single chunk the kernel writes y directly.
+#include <hip/hip_fp16.h>
+
+#include "lfsr_device.h"
+#include "seedlm_internal.h"
+
+namespace seedlm {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRowsPerWave = 64;
+constexpr int kRowsPerTile = kRowsPerWave * kWaves;
+constexpr int kBatchPad = 16;
+
+template <int C>
+struct Fmt;
+template <>
+struct Fmt<8> {
+  static constexpr int P = 3;
+  static constexpr int kCols = 8 * kPanelBlocks;  // columns of a panel
+  static constexpr int kStride = kCols + 8;       // LDS row stride of x (halves)
+  using Ext = uint32_t;                           // stream bits 16..47
+};
+template <>
+struct Fmt<12> {
+  static constexpr int P = 4;
+  static constexpr int kCols = 12 * kPanelBlocks;
+  static constexpr int kStride = kCols + 8;
+  using Ext = uint64_t;  // stream bits 16..79 (63 needed)
+};
+
+struct MfmaArgs {
+  const uint32_t* words;
+  const __half* x;
+  float* partial;
+  __half* y;
+  uint32_t buf_bytes;  // whole packed buffer (words, then exponents)
+  uint32_t exp_off;    // byte offset of the 3-bit exponent nibbles
+  int rows, cols, Mp, nb, np, batch;
+  int tiles, chunk_panels, chunks;
+};
+
+__device__ inline uint32_t ubfe(uint32_t v, uint32_t off, uint32_t w) {
+  return __builtin_amdgcn_ubfe(v, off, w);
+}
+
+// 2^(g - 20) for g in [0, 15]: the block scale 2^(e - 15) = 2^(g - 30) times
+// the fp16 range factor 2^10.
+__device__ inline float block_scale(uint32_t g) { return __uint_as_float((g + 107u) << 23); }
+
+// Eight fp16 weights (x 2^10) of a 4-bit block, in column order.
+__device__ inline half8 decode_c8(uint32_t w, const uint32_t* T0, const uint32_t* T1) {
+  const uint32_t ext = T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];  // stream bits 16..47
+  const uint32_t lo = (w & 0xFFFFu) | (ext << 16);             // stream bits 0..31
+  const int t0 = ((int)(w << 12)) >> 28;
+  const int t1 = ((int)(w << 8)) >> 28;
+  const int t2 = ((int)(w << 4)) >> 28;
+  const int base = -32768 * (t0 + t1 + t2);
+  const float sc = block_scale(w >> 28);
+  half8 out;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int z0 = (int)ubfe(lo, i, 16);       // z_i
+    const int z1 = (int)ubfe(lo, 8 + i, 16);   // z_{8+i}
+    const int z2 = (int)ubfe(ext, i, 16);      // z_{16+i}
+    const int I = t0 * z0 + t1 * z1 + t2 * z2 + base;
+    out[i] = (_Float16)((float)I * sc);
+  }
+  return out;
+}
+
+// Twelve fp16 weights (x 2^10) of a 3-bit block, written to o[0..11].
+__device__ inline void decode_c12(uint32_t w, uint32_t g, const uint64_t* T0, const uint64_t* T1,
+                                  _Float16* o) {
+  const uint64_t ext = T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];  // stream bits 16..79
+  const uint32_t s0 = (w & 0xFFFFu) | ((uint32_t)ext << 16);    // bits 0..31
+  const uint32_t s1 = (uint32_t)ext;                            // bits 16..47
+  const uint32_t s2 = (uint32_t)(ext >> 16);                    // bits 32..63
+  int t[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t[j] = ((int)(w << (12 - 4 * j))) >> 28;
+  const int base = -32768 * (t[0] + t[1] + t[2] + t[3]);
+  const float sc = block_scale(g);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    int I = base;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = 12 * j + i;  // state index, window b[n .. n+15]
+      const int z = n <= 16 ? (int)ubfe(s0, n, 16)
+                            : (n <= 32 ? (int)ubfe(s1, n - 16, 16) : (int)ubfe(s2, n - 32, 16));
+      I += t[j] * z;
+    }
+    o[i] = (_Float16)((float)I * sc);
+  }
+}
+
+template <int C>
+__global__ void __launch_bounds__(kThreads) gemv_mfma_kernel(const MfmaArgs a) {
+  using F = Fmt<C>;
+  using Ext = typename F::Ext;
+  __shared__ Ext T0[256], T1[256];
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][kBatchPad * F::kStride];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int tile = (int)(blockIdx.x % (unsigned)a.tiles);
+  const int chunk = (int)(blockIdx.x / (unsigned)a.tiles);
+  const int pa = chunk * a.chunk_panels;
+  const int pb = min(a.np, pa + a.chunk_panels);
+  const int r0 = tile * kRowsPerTile + wave * kRowsPerWave;  // multiple of 8
+  const int64_t Mp = a.Mp;
+
+  for (int e = tid; e < 512; e += kThreads) {
+    const uint32_t u = (uint32_t)e & 255u;
+    if (e < 256) T0[u] = ext_bits<Ext>(u);
+    else T1[u] = ext_bits<Ext>(u << 8);
+  }
+
+  // x staging: panel p's columns for batch rows 0..15 (zero outside x).
+  constexpr int kPer = kBatchPad * F::kCols / kThreads;  // halves per thread
+  _Float16 xr[kPer];
+  auto fetch_x = [&](int p) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = tid + k * kThreads;
+      const int b = e / F::kCols, c = e % F::kCols;
+      const int64_t col = (int64_t)p * F::kCols + c;
+      xr[k] = (b < a.batch && col < a.cols)
+                  ? (_Float16)__half2float(a.x[(int64_t)b * a.cols + col])
+                  : (_Float16)0.f;
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = tid + k * kThreads;
+      xs[buf][(e / F::kCols) * F::kStride + e % F::kCols] = xr[k];
+    }
+  };
+  fetch_x(pa);
+  store_x(pa & 1);
+  __syncthreads();
+
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.words, 0, (int)a.buf_bytes, 0x00020000);
+  floatx4 acc[4];
+#pragma unroll
+  for (int rho = 0; rho < 4; ++rho) acc[rho] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int p = pa; p < pb; ++p) {
+    if (p + 1 < pb) fetch_x(p + 1);  // lands while this panel computes
+    const int Wp = (int)panel_stored_width(p, a.nb);
+    const _Float16* xp = xs[p & 1] + i16 * F::kStride;
+#pragma unroll
+    for (int rho = 0; rho < 4; ++rho) {
+      const int r = r0 + rho + 4 * i16;
+#pragma unroll
+      for (int h = 0; h < kPanelBlocks / 16; ++h) {
+        const int g = 4 * h + q;  // slot group of this lane: slots 4g .. 4g+3
+        const bool ok = r < a.Mp && 4 * g < Wp;
+        const uint32_t off =
+            ok ? (uint32_t)(((int64_t)p * Mp * kPanelBlocks + (int64_t)r * Wp + 4 * g) * 4)
+               : 0x80000000u;
+        const v4u wd = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+        if constexpr (C == 8) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            // word n of the group holds slot 4g + ((n + row) & 3), row = rho mod 4
+            const int slot = 4 * g + ((n + rho) & 3);
+            const half8 A = decode_c8(wd[n], T0, T1);
+            const half8 B = *reinterpret_cast<const half8*>(xp + 8 * slot);
+            acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rho], 0, 0, 0);
+          }
+        } else {
+          const uint32_t eoff =
+              ok ? a.exp_off + (uint32_t)(((int64_t)p * Mp * (kPanelBlocks / 4) +
+                                           (int64_t)r * (Wp / 4) + g) * 2)
+                 : 0x80000000u;
+          const uint32_t ev = __builtin_amdgcn_raw_buffer_load_b16(rsrc, eoff, 0, 0);
+          _Float16 wv[48];
+#pragma unroll
+          for (int n = 0; n < 4; ++n) decode_c12(wd[n], (ev >> (4 * n)) & 0xFu, T0, T1, wv + 12 * n);
+#pragma unroll
+          for (int m = 0; m < 6; ++m) {
+            half8 A, B;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) A[u] = wv[8 * m + u];
+            // x columns of weights 8m .. 8m+7: two runs of four inside blocks
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int u = 8 * m + 4 * hh;
+              const int slot = 4 * g + ((u / 12 + rho) & 3);
+              const half4 xv = *reinterpret_cast<const half4*>(xp + 12 * slot + u % 12);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) B[4 * hh + k] = xv[k];
+            }
+            acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rho], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (p + 1 < pb) {
+      store_x((p + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // Result: lane holds rows 4*q + v of each row group, batch column i16.
+  const int b = i16;
+  if (b < a.batch) {
+#pragma unroll
+    for (int rho = 0; rho < 4; ++rho) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = r0 + rho + 4 * (4 * q + v);
+        if (r < a.rows) {
+          const float val = acc[rho][v] * 0x1p-10f;
+          if (a.chunks == 1)
+            a.y[(int64_t)b * a.rows + r] = __float2half_rn(val);
+          else
+            a.partial[((int64_t)chunk * a.batch + b) * Mp + r] = val;
+        }
+      }
+    }
+  }
+}
+
+// y[b][r] = sum over chunks c of partial[c][b][r]; a workgroup owns 64 rows of
+// one batch column, lane = row, wave w adds chunks w, w+4, ... (16 loads in
+// flight), the four sums combine as (w0+w1)+(w2+w3).  Fixed order.
+__global__ void __launch_bounds__(256) reduce_chunks_kernel(const float* __restrict__ partial,
+                                                            __half* __restrict__ y, int rows,
+                                                            int Mp, int batch, int chunks) {
+  __shared__ float wsum[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int b = (int)blockIdx.y;
+  const int r = (int)blockIdx.x * 64 + lane;
+  const int rr = r < rows ? r : rows - 1;  // in-bounds load; no store below
+  const float* __restrict__ src = partial + (int64_t)b * Mp + rr;
+  const int64_t cstride = (int64_t)batch * Mp;
+  float s = 0.f;
+  for (int c0 = wv; c0 < chunks; c0 += 4 * 16) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int c = c0 + 4 * k;
+      v[k] = c < chunks ? src[c * cstride] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s += v[k];
+  }
+  wsum[wv][lane] = s;
+  __syncthreads();
+  if (wv == 0 && r < rows)
+    y[(int64_t)b * rows + r] =
+        __float2half_rn((wsum[0][lane] + wsum[1][lane]) + (wsum[2][lane] + wsum[3][lane]));
+}
+
+}  // namespace
+
+int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
+                     hipStream_t s) {
+  if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
+  if (batch < 1 || batch > kBatchPad) return SEEDLM_E_INVALID;
+  if (h->bytes >= 0x80000000ull || h->Mp >= (1 << 30) || h->cols >= (1LL << 31))
+    return SEEDLM_E_UNSUPPORTED;
+  MfmaArgs a{};
+  a.words = static_cast<const uint32_t*>(h->d_buf);
+  a.x = static_cast<const __half*>(x);
+  a.partial = h->d_work;
+  a.y = static_cast<__half*>(y);
+  a.buf_bytes = (uint32_t)h->bytes;
+  a.exp_off = (uint32_t)h->exp_off;
+  a.rows = (int)h->rows;
+  a.cols = (int)h->cols;
+  a.Mp = (int)h->Mp;
+  a.nb = (int)h->nb;
+  a.np = (int)h->np;
+  a.batch = batch;
+  a.tiles = (int)((h->Mp + kRowsPerTile - 1) / kRowsPerTile);
+  // Split the panels so that there are about four workgroups per CU.
+  const int64_t want = 4LL * device_cu_count();
+  int64_t chunks = (want + a.tiles - 1) / a.tiles;
+  if (chunks < 1) chunks = 1;
+  if (chunks > a.np) chunks = a.np;
+  a.chunk_panels = (int)((a.np + chunks - 1) / chunks);
+  a.chunks = (a.np + a.chunk_panels - 1) / a.chunk_panels;
+  if ((size_t)a.chunks * batch * h->Mp * sizeof(float) > h->work_bytes) return SEEDLM_E_INVALID;
+  const dim3 grid((unsigned)(a.tiles * a.chunks));
+  if (h->C == 8)
+    hipLaunchKernelGGL(gemv_mfma_kernel<8>, grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(gemv_mfma_kernel<12>, grid, dim3(kThreads), 0, s, a);
+  SEEDLM_HIP_CHECK(hipGetLastError());
+  if (a.chunks > 1) {
+    hipLaunchKernelGGL(reduce_chunks_kernel, dim3((unsigned)((a.rows + 63) / 64), (unsigned)batch),
+                       dim3(256), 0, s, a.partial, a.y, a.rows, a.Mp, batch, a.chunks);
+    SEEDLM_HIP_CHECK(hipGetLastError());
+  }
+  return SEEDLM_OK;
+}
+
+}  // namespace seedlm

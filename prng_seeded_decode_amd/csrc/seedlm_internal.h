@@ -81,8 +81,9 @@ int launch_gemv_lut(const seedlm_matrix* h, const void* x, void* y, int xdt, int
 // partials into the handles' workspaces) and one reduce launch (phases & 2: y).
 int launch_gemv_lut_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys,
                           int n, int xdt, int ydt, bool global_table, hipStream_t s, int phases);
-int launch_gemm_skinny(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt,
-                       int ydt, hipStream_t s);
+// Matrix-core path (fp16 x and y only; E_UNSUPPORTED otherwise).
+int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
+                     hipStream_t s);
 int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,
                      int batch, hipStream_t s);
 int build_ext_table(seedlm_matrix* h);
