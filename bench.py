@@ -69,6 +69,8 @@ def parse_args():
                    help="also time one seedlm_gemv per matrix (extra launches of the same kernels)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one plain fp32 copy kernel of this many MiB first (counter calibration)")
+    p.add_argument("--decode", action="store_true",
+                   help="also time seedlm_decode (dense fp32 W) on the largest matrix")
     p.add_argument("--graph", type=int, default=0,
                    help="1: replay each step as a captured HIP graph (one per rotated copy)")
     return p.parse_args()
@@ -302,6 +304,31 @@ def main():
                 "speedup_vs_best_fp16": round(best / ms_per_step, 3)}
         del Ws
 
+    decode = None
+    if args.decode:
+        # seedlm_decode of the largest matrix into a dense fp32 W: reads the packed
+        # words, writes 4 bytes per weight (HBM-write bound).
+        big = max(mats, key=lambda d: d["mat"].rows * d["mat"].cols)
+        W = torch.empty((big["mat"].rows, big["mat"].cols), dtype=torch.float32, device=dev)
+        for k in range(3):
+            S.seedlm_decode(big["copies"][k % args.copies], W, stream=stream)
+        torch.cuda.synchronize()
+        dev_ms = []
+        for k in range(max(5, args.steps // 2)):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            S.seedlm_decode(big["copies"][k % args.copies], W, stream=stream)
+            b.record(stream)
+            dev_ms.append((a, b))
+        torch.cuda.synchronize()
+        t = float(np.mean([a.elapsed_time(b) for a, b in dev_ms])) * 1e-3
+        moved = big["bytes"] + 4 * big["mat"].rows * big["mat"].cols
+        decode = {"matrix": big["mat"].name, "shape": [big["mat"].rows, big["mat"].cols],
+                  "us": round(t * 1e6, 2), "GBps_read_plus_write": round(moved / t / 1e9, 1),
+                  "pct_hbm_peak": round(100 * moved / t / 1e9 / HBM_PEAK_GBPS, 2)}
+        del W
+
     out = {
         "metric": METRIC,
         "value": layer_weights / t_step,
@@ -344,6 +371,8 @@ def main():
         },
         "fp16_baseline": fp16,
     }
+    if decode:
+        out["decode"] = decode
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(out), flush=True)
