@@ -25,7 +25,8 @@ namespace {
 
 __global__ void ext_table_kernel(uint32_t* __restrict__ table) {
   const uint32_t s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s < 65536u) table[s] = ext_bits<uint32_t>(s);
+  // extension bits 16..39 in the low three bytes, the seed's high byte on top
+  if (s < 65536u) table[s] = (ext_bits<uint32_t>(s) & 0x00FFFFFFu) | ((s >> 8) << 24);
 }
 
 bool dtype_ok(int d) { return d == SEEDLM_F32 || d == SEEDLM_F16; }

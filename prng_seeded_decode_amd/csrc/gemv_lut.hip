@@ -23,10 +23,23 @@
 // replicated per slot for the same reason, or -- TABLE variant -- from a
 // 2^16-entry table of extension bits in global memory (L2/MALL resident).
 //
-// LDS: region A row v = [L0[v] for slots 0..31 | T1[v] x32], region B row v =
-// [T0[v] x32 | L2[v] for slots 0..31]; 256 B per row, so one v_perm_b32 turns a
-// stream byte and a per-lane constant into a row/column address, and
-// L0[B1] + T1[B1] come back from a single ds_read2_b32.
+// LDS: region A row v = [L0'[v] for slots 0..31 | T1[v] x32], region B row v =
+// [T0[v] x16 | TC[v] x16 | L2[v] for slots 0..31]; 256 B per row, so one
+// v_perm_b32 turns a byte and a per-lane constant into a row/column address, and
+// L0'[B1] + T1[B1] come back from a single ds_read2_b32.  The 16-copy tables
+// cost a 2-way bank conflict, which LDS bandwidth has room for.
+//
+// Per block the arithmetic is arranged to keep VALU work low:
+//   * TC[v] is the coefficient byte v = (t1 << 4 | t0) as the fp16 pair
+//     (t0, t1), used directly by v_fma_mix_f32 and v_dot2_f32_f16;
+//   * T1[v] carries v in its top byte, so ext = T0[B0] ^ T1[B1] holds
+//     (B2, B3, B4, B1) and one v_perm_b32 makes the fp16 pair
+//     (1024 + B1, 1024 + B2) (0x64 is the fp16 exponent of 1024); then
+//     t0 (1024 + B1) + t1 (1024 + B2) is one exact v_dot2_f32_f16, and
+//     t2 (1024 + B3) one v_fma_mix_f32;
+//   * L0' = L0 - 2048 c_7 removes the 1024 offsets again:
+//     sum_j t_j D_j = sum_j t_j (L0'[B_j] + L2[B_{j+2}])
+//                     + 2 c_7 sum_j t_j (1024 + B_{j+1}).
 //
 // Lane mapping: lane = 8*rho + g; the lane owns row r0+rho and slot group g
 // (slots 4g..4g+3) and reads the group's four words with one 16-byte load.  The
@@ -48,15 +61,20 @@ namespace {
 
 constexpr int kThreads = 1024;  // 16 waves: 4 per SIMD
 constexpr int kWaves = kThreads / 64;
-constexpr int kPrefetch = 2;    // 16-byte loads in flight per lane
+#ifndef SEEDLM_LUT_NS
+#define SEEDLM_LUT_NS 1
+#endif
+constexpr int kNS = SEEDLM_LUT_NS;  // slabs per processing call (1 or 2)
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 struct Smem {
-  uint32_t A[256][64];  // [L0 (32 slots) | T1 (32 copies)]
-  uint32_t B[256][64];  // [T0 (32 copies) | L2 (32 slots)]
+  uint32_t A[256][64];  // [L0' (32 slots) | T1 (32 copies)]
+  uint32_t B[256][64];  // [T0 (16 copies) | TC (16 copies) | L2 (32 slots)]
   float xs[256];
   float c7x2[32];
   uint32_t gf2[512];    // T0 then T1, staged before replication
 };
+constexpr int kColT0 = 0, kColTC = 16, kColL2 = 32;  // column bases in region B
 constexpr uint32_t kRegionB = 65536;  // byte offset of B inside Smem
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -86,7 +104,7 @@ struct LutGroup {
 
 // Cost model of the work split: a panel's table build costs about as much as
 // kBuildCost slabs of 8 rows.
-constexpr int64_t kBuildCost = 24;
+constexpr int64_t kBuildCost = 51;
 
 template <typename XT>
 __device__ inline float ldx(const XT* p);
@@ -112,13 +130,10 @@ __device__ inline float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-template <typename XT>
-__device__ void build_panel_lut(Smem& sm, const XT* __restrict__ x, int64_t cols, int64_t p) {
+__device__ void build_panel_lut(Smem& sm, float xval) {
+  // xval: this thread's x value of the panel (threads 0..255), loaded ahead.
   const int tid = threadIdx.x;
-  if (tid < 256) {
-    const int64_t c = p * 256 + tid;
-    sm.xs[tid] = c < cols ? ldx(x + c) : 0.f;
-  }
+  if (tid < 256) sm.xs[tid] = xval;
   __syncthreads();
   // Thread -> (slot, value group): kNV consecutive table rows per thread; the
   // low kLB bits of the row index come from small tables built by doubling,
@@ -142,7 +157,7 @@ __device__ void build_panel_lut(Smem& sm, const XT* __restrict__ x, int64_t cols
   float S = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) S += xv[i];
-  float B0 = -32768.f * S, B2 = 0.f;
+  float B0 = -32768.f * S - 2048.f * c[7], B2 = 0.f;
 #pragma unroll
   for (int k = kLB; k < 8; ++k) {
     if ((vg >> (k - kLB)) & 1) {
@@ -162,7 +177,7 @@ __device__ void build_panel_lut(Smem& sm, const XT* __restrict__ x, int64_t cols
   for (int n = 0; n < kNV; ++n) {
     const int v = vg * kNV + n;
     sm.A[v][slot] = __float_as_uint(A0[n] + B0);
-    sm.B[v][32 + slot] = __float_as_uint(A2[n] + B2);
+    sm.B[v][kColL2 + slot] = __float_as_uint(A2[n] + B2);
   }
   if (vg == 0) sm.c7x2[slot] = 2.f * c[7];
 }
@@ -175,41 +190,85 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int rho = lane >> 3, g = lane & 7;
   const uint8_t* lds = reinterpret_cast<const uint8_t*>(&sm);
 
-  // Per-slot copies of the GF(2) tables (built once per launch): 512 values
+  // Each workgroup takes one contiguous range of the group's work items; the
+  // host split them so that every range has about the same cost.
+  const int64_t begin = grp.bounds[blockIdx.x];
+  const int64_t end = grp.bounds[blockIdx.x + 1];
+  // The x of a segment's panel is loaded one segment ahead (threads 0..255
+  // hold one raw value each) with a buffer load whose out-of-range offset
+  // reads zero, so no branch or select follows the load and nothing waits on
+  // it until the table build that uses it.
+  auto fetch_x = [&](int64_t item) -> uint32_t {
+    int m2 = 0;
+    while (m2 + 1 < grp.n && item >= grp.m[m2 + 1].item_begin) ++m2;
+    const LutMatrix& N = grp.m[m2];
+    const int64_t c = (item - N.item_begin) / (N.Mp / 8) * 256 + tid;
+    const uint32_t off = (item < end && tid < 256 && c < N.cols) ? (uint32_t)c * sizeof(XT)
+                                                                  : 0x80000000u;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)N.x, 0, (int)(N.cols * sizeof(XT)), 0x00020000);
+    if constexpr (sizeof(XT) == 2)
+      return __builtin_amdgcn_raw_buffer_load_b16(xr, off, 0, 0);
+    else
+      return __builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
+  };
+  auto x_value = [](uint32_t raw) -> float {
+    if constexpr (sizeof(XT) == 2)
+      return __half2float(__ushort_as_half((unsigned short)raw));
+    else
+      return __uint_as_float(raw);
+  };
+  uint32_t x_next = fetch_x(begin);
+
+  // Copies of the GF(2) tables and of TC (built once per launch): values
   // staged, then replicated with 16-byte writes where consecutive lanes write
-  // consecutive addresses (no bank conflicts).
-  if (!kGlobalTable) {
-    if (tid < 512) {
-      const uint32_t u = tid & 255;
-      sm.gf2[tid] = tid < 256 ? ext_bits<uint32_t>(u) : ext_bits<uint32_t>(u << 8);
-    }
-    __syncthreads();
-    // 2 tables x 256 rows x 8 uint4 (32 copies) = 4096 uint4 stores.
+  // consecutive addresses (no bank conflicts).  T1's top byte is its index.
+  if (tid < 512) {
+    const uint32_t u = tid & 255;
+    sm.gf2[tid] = tid < 256 ? ext_bits<uint32_t>(u) & 0x00FFFFFFu
+                            : (ext_bits<uint32_t>(u << 8) & 0x00FFFFFFu) | (u << 24);
+  }
+  __syncthreads();
+  // T1: 256 rows x 8 uint4 (32 copies); T0 and TC: 256 rows x 4 uint4 each.
 #pragma unroll
-    for (int k = 0; k < 4096 / kThreads; ++k) {
-      const int e = tid + k * kThreads;
-      const int tab = e >> 11, u = (e >> 3) & 255, part = e & 7;
-      const uint32_t val = sm.gf2[tab * 256 + u];
-      uint4* dst = reinterpret_cast<uint4*>(tab == 0 ? &sm.B[u][0] : &sm.A[u][32]);
-      dst[part] = make_uint4(val, val, val, val);
+  for (int k = 0; k < 4096 / kThreads; ++k) {
+    const int e = tid + k * kThreads;  // k < 2: T1; k >= 2: T0 and TC
+    uint32_t val;
+    uint4* dst;
+    if (e < 2048) {
+      const int u = e >> 3, part = e & 7;
+      val = sm.gf2[256 + u];
+      dst = reinterpret_cast<uint4*>(&sm.A[u][32]) + part;
+    } else {
+      const int f = e - 2048, u = f >> 3, part = f & 7;
+      if (part < 4) {
+        val = sm.gf2[u];
+        dst = reinterpret_cast<uint4*>(&sm.B[u][kColT0]) + part;
+      } else {  // (t0, t1) of the coefficient byte u, as an fp16 pair
+        const int lo = u & 15, hi = u >> 4;
+        const __half h0 = __int2half_rn(lo - ((lo & 8) << 1));
+        const __half h1 = __int2half_rn(hi - ((hi & 8) << 1));
+        val = (uint32_t)__half_as_ushort(h0) | ((uint32_t)__half_as_ushort(h1) << 16);
+        dst = reinterpret_cast<uint4*>(&sm.B[u][kColTC]) + (part - 4);
+      }
     }
+    *dst = make_uint4(val, val, val, val);
   }
 
   // Slots of this lane's four words: slot_j = 4g + ((j + row) & 3); slabs start
   // at multiples of 8 rows, so row & 3 == rho & 3.
-  uint32_t lcA[4], lcB[4];
+  uint32_t lcA[4], lcB[4], lcT0[4], lcTC[4];
   int slotj[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     slotj[j] = 4 * g + ((j + rho) & 3);
     lcA[j] = (uint32_t)slotj[j] * 4u;
-    lcB[j] = lcA[j] | kRegionB;
+    lcB[j] = ((uint32_t)(kColL2 + slotj[j]) * 4u) | kRegionB;
+    lcT0[j] = ((uint32_t)(kColT0 + (slotj[j] & 15)) * 4u) | kRegionB;
+    lcTC[j] = ((uint32_t)(kColTC + (slotj[j] & 15)) * 4u) | kRegionB;
   }
 
-  // Each workgroup takes one contiguous range of the group's work items; the
-  // host split them so that every range has about the same cost.
-  const int64_t begin = grp.bounds[blockIdx.x];
-  const int64_t end = grp.bounds[blockIdx.x + 1];
+
 
   for (int64_t it = begin; it < end;) {
     int mi = 0;
@@ -228,8 +287,21 @@ __global__ void __launch_bounds__(kThreads, 1)
         __builtin_amdgcn_make_buffer_rsrc((void*)M.words, 0, (int)M.words_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t prsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)M.partial, 0, (int)(np * Mp * 4), 0x00020000);
+    const uint32_t lane_base =
+        4 * g < Wp ? (uint32_t)(p * Mp * kPanelBlocks + rho * Wp + 4 * g) * 4u : 0x80000000u;
+    const uint32_t slab_stride = 8u * (uint32_t)Wp * 4u;
+    auto load = [&](int sl) {
+      return __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_base + (uint32_t)sl * slab_stride,
+                                                   0, 0);
+    };
+    // This wave's slabs are s_first, s_first + 16, ...; the first two loads
+    // go out before the table build so that their latency overlaps it.
+    const int s_first = sa + wave;
+    v4u A[2] = {load(s_first), load(s_first + kWaves)};
+    const uint32_t x_this = x_next;
+    x_next = fetch_x(seg_end);
     __syncthreads();  // previous panel's tables no longer in use
-    build_panel_lut<XT>(sm, static_cast<const XT*>(M.x), M.cols, p);
+    build_panel_lut(sm, x_value(x_this));
     __syncthreads();
     float c7j[4];
 #pragma unroll
@@ -238,71 +310,103 @@ __global__ void __launch_bounds__(kThreads, 1)
     // Lanes outside the panel's width get an out-of-range base: their loads
     // return zero words (t = 0, no contribution).  Offsets grow by one slab
     // stride per step, so no per-load bounds logic is needed.
-    const uint32_t lane_base =
-        4 * g < Wp ? (uint32_t)(p * Mp * kPanelBlocks + rho * Wp + 4 * g) * 4u : 0x80000000u;
-    const uint32_t slab_stride = 8u * (uint32_t)Wp * 4u;
     const uint32_t pstore = g == 0 ? (uint32_t)(p * Mp + rho) * 4u : 0x80000000u;
 
-    v4u buf[kPrefetch];
-    const int s_first = sa + wave;
+    // kNS slabs per call (4*kNS blocks per lane): each stage issues the LDS
+    // reads of all the call's blocks before the first use.  Each slab's row sum
+    // is reduced over its 8 lanes and stored as the panel partial of that row.
+    auto run = [&](const v4u (&q)[kNS], int sl0, int nvalid) {
+      constexpr int NB = 4 * kNS;
+      uint32_t w[NB];
 #pragma unroll
-    for (int d = 0; d < kPrefetch; ++d)
-      buf[d] = __builtin_amdgcn_raw_buffer_load_b128(
-          rsrc, lane_base + (uint32_t)(s_first + d * kWaves) * slab_stride, 0, 0);
+      for (int k = 0; k < NB; ++k) w[k] = q[k >> 2][k & 3];
+      // Stage 1: GF(2) halves, coefficient pairs and the seed-byte L0' values.
+      float l0b0[NB], l0b1[NB];
+      uint32_t ext[NB], tcv[NB];
+      if (kGlobalTable) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          l0b0[k] = lds_at<float>(lds, lut_addr<0>(w[k], lcA[k & 3]));
+          l0b1[k] = lds_at<float>(lds, lut_addr<1>(w[k], lcA[k & 3]));
+          tcv[k] = lds_at<uint32_t>(lds, lut_addr<2>(w[k], lcTC[k & 3]));
+          ext[k] = ext_table[w[k] & 0xFFFFu];
+        }
+      } else {
+        uint32_t t0v[NB], t1v[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          const uint32_t a1 = lut_addr<1>(w[k], lcA[k & 3]);
+          l0b0[k] = lds_at<float>(lds, lut_addr<0>(w[k], lcA[k & 3]));
+          t0v[k] = lds_at<uint32_t>(lds, lut_addr<0>(w[k], lcT0[k & 3]));
+          l0b1[k] = lds_at<float>(lds, a1);
+          t1v[k] = lds_at<uint32_t>(lds, a1 + 128);
+          tcv[k] = lds_at<uint32_t>(lds, lut_addr<2>(w[k], lcTC[k & 3]));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all stage-1 reads issue before any use
+#pragma unroll
+        for (int k = 0; k < NB; ++k) ext[k] = t0v[k] ^ t1v[k];
+      }
+      // Stage 2: table values of the extension bytes B_2..B_4.
+      float l0b2[NB], l2b2[NB], l2b3[NB], l2b4[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        l0b2[k] = lds_at<float>(lds, lut_addr<0>(ext[k], lcA[k & 3]));
+        l2b2[k] = lds_at<float>(lds, lut_addr<0>(ext[k], lcB[k & 3]));
+        l2b3[k] = lds_at<float>(lds, lut_addr<1>(ext[k], lcB[k & 3]));
+        l2b4[k] = lds_at<float>(lds, lut_addr<2>(ext[k], lcB[k & 3]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Stage 3: arithmetic.
+      float acc[kNS];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int j = k & 3;
+        const uint32_t wk = w[k];
+        const half2v tc = __builtin_bit_cast(half2v, tcv[k]);  // (t0, t1)
+        // (1024 + B1, 1024 + B2) and (1024 + B3, 0) as fp16 pairs
+        const half2v p12 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ext[k], 0x64646464u, 0x01040007u));
+        const half2v p3 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ext[k], 0x64646464u, 0x0C0C0005u));
+        const float t2 = (float)(((int)(wk << 4)) >> 28);
+        const float mid = __builtin_amdgcn_fdot2(tc, p12, t2 * (float)p3[0], false);
+        float V = t2 * (l0b2[k] + l2b4[k]);
+        V = fmaf((float)tc[0], l0b0[k] + l2b2[k], V);
+        V = fmaf((float)tc[1], l0b1[k] + l2b3[k], V);
+        V = fmaf(c7j[j], mid, V);
+        const float part = ldexpf(V, (int)(wk >> 28));
+        acc[k >> 2] = j == 0 ? part : acc[k >> 2] + part;
+      }
+      // Sum each row over its 8 lanes (xor 1, xor 2, then mirror within 8).
+#pragma unroll
+      for (int h = 0; h < kNS; ++h) {
+        acc[h] += dpp<0xB1>(acc[h]);
+        acc[h] += dpp<0x4E>(acc[h]);
+        acc[h] += dpp<0x141>(acc[h]);
+        if (h < nvalid)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[h] * 0x1p-30f), prsrc,
+                                                pstore + (uint32_t)(sl0 + h * kWaves) * 32u, 0, 0);
+      }
+    };
 
-    for (int s0 = s_first; s0 < sb; s0 += kWaves * kPrefetch) {
-#pragma unroll
-      for (int d = 0; d < kPrefetch; ++d) {
-        const int sl = s0 + d * kWaves;
-        const v4u q = buf[d];
-        buf[d] = __builtin_amdgcn_raw_buffer_load_b128(
-            rsrc, lane_base + (uint32_t)(sl + kWaves * kPrefetch) * slab_stride, 0, 0);
-
-        // Stage 1: GF(2) halves and the seed-byte L0 values of all four blocks.
-        float l0b0[4], l0b1[4];
-        uint32_t ext[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t a0 = lut_addr<0>(q[j], lcA[j]);
-          const uint32_t a1 = lut_addr<1>(q[j], lcA[j]);
-          l0b0[j] = lds_at<float>(lds, a0);
-          l0b1[j] = lds_at<float>(lds, a1);
-          if (kGlobalTable) {
-            ext[j] = ext_table[q[j] & 0xFFFFu];
-          } else {
-            ext[j] = lds_at<uint32_t>(lds, a0 + kRegionB) ^ lds_at<uint32_t>(lds, a1 + 128);
-          }
-        }
-        // Stage 2: table values of the extension bytes B_2..B_4.
-        float l0b2[4], l2b2[4], l2b3[4], l2b4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          l0b2[j] = lds_at<float>(lds, lut_addr<0>(ext[j], lcA[j]));
-          l2b2[j] = lds_at<float>(lds, lut_addr<0>(ext[j], lcB[j]) + 128);
-          l2b3[j] = lds_at<float>(lds, lut_addr<1>(ext[j], lcB[j]) + 128);
-          l2b4[j] = lds_at<float>(lds, lut_addr<2>(ext[j], lcB[j]) + 128);
-        }
-        // Stage 3: arithmetic.
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = q[j];
-          const float E0 = fmaf(c7j[j], (float)((w >> 8) & 0xFFu), l0b0[j] + l2b2[j]);
-          const float E1 = fmaf(c7j[j], (float)(ext[j] & 0xFFu), l0b1[j] + l2b3[j]);
-          const float E2 = fmaf(c7j[j], (float)((ext[j] >> 8) & 0xFFu), l0b2[j] + l2b4[j]);
-          const float t0 = (float)(((int)(w << 12)) >> 28);
-          const float t1 = (float)(((int)(w << 8)) >> 28);
-          const float t2 = (float)(((int)(w << 4)) >> 28);
-          const float V = fmaf(t2, E2, fmaf(t1, E1, t0 * E0));
-          const float part = ldexpf(V, (int)(w >> 28));
-          acc = j == 0 ? part : acc + part;
-        }
-        // Sum the row over its 8 lanes (xor 1, xor 2, then mirror within 8).
-        acc += dpp<0xB1>(acc);
-        acc += dpp<0x4E>(acc);
-        acc += dpp<0x141>(acc);
-        const uint32_t so = sl < sb ? pstore + (uint32_t)sl * 32u : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc * 0x1p-30f), prsrc, so, 0, 0);
+    // Two register sets alternate (A: slabs 0, 1 of each group of four, B:
+    // slabs 2, 3), each load issued two slabs ahead of its use; nothing is
+    // copied at the back edge, so a wait never covers a load younger than the
+    // one it needs.  Loads past the panel read harmless words (or zeros past
+    // the buffer) and are not used.
+    for (int s0 = s_first; s0 < sb; s0 += 4 * kWaves) {
+      v4u Bq[2] = {load(s0 + 2 * kWaves), load(s0 + 3 * kWaves)};
+      const int n0 = min(4, (sb - s0 + kWaves - 1) / kWaves);  // valid slabs of the group
+      if constexpr (kNS == 2) {
+        run(A, s0, min(n0, 2));
+        A[0] = load(s0 + 4 * kWaves);
+        A[1] = load(s0 + 5 * kWaves);
+        if (n0 > 2) run(Bq, s0 + 2 * kWaves, n0 - 2);
+      } else {
+        run({A[0]}, s0, 1);
+        A[0] = load(s0 + 4 * kWaves);
+        if (n0 > 1) run({A[1]}, s0 + kWaves, 1);
+        A[1] = load(s0 + 5 * kWaves);
+        if (n0 > 2) run({Bq[0]}, s0 + 2 * kWaves, 1);
+        if (n0 > 3) run({Bq[1]}, s0 + 3 * kWaves, 1);
       }
     }
     it = seg_end;
