@@ -205,8 +205,14 @@ __global__ void __launch_bounds__(kThreads, 1)
     const int64_t c = (item - N.item_begin) / (N.Mp / 8) * 256 + tid;
     const uint32_t off = (item < end && tid < 256 && c < N.cols) ? (uint32_t)c * sizeof(XT)
                                                                   : 0x80000000u;
+    // The matrix is the same for the whole workgroup: say so, so that the
+    // descriptor lives in scalar registers.
+    const uint64_t xp = (uint64_t)N.x;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)xp);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(xp >> 32));
+    const int nbytes = __builtin_amdgcn_readfirstlane((int)(N.cols * sizeof(XT)));
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)N.x, 0, (int)(N.cols * sizeof(XT)), 0x00020000);
+        (void*)(((uint64_t)hi << 32) | lo), 0, nbytes, 0x00020000);
     if constexpr (sizeof(XT) == 2)
       return __builtin_amdgcn_raw_buffer_load_b16(xr, off, 0, 0);
     else
