@@ -428,7 +428,7 @@ __device__ inline void store_y<__half>(__half* p, float v) { *p = __float2half_r
 
 // Panel reduction: y[r] = sum over panels p of partial[p][r].  A workgroup owns
 // 64 consecutive rows of one matrix (lane = row, so every load reads 256
-// contiguous bytes); wave w adds panels w, w+4, w+8, ... with up to 16 loads in
+// contiguous bytes); wave w adds panels w, w+4, w+8, ... with up to 32 loads in
 // flight, and the four wave sums combine through LDS as (w0+w1)+(w2+w3).  The
 // order is fixed for a given panel count, so repeated calls give identical
 // results.
@@ -446,15 +446,15 @@ __global__ void __launch_bounds__(256) reduce_panels_kernel(const LutGroup grp) 
   const int np = M.np;
   const int64_t Mp = M.Mp;
   float s = 0.f;
-  for (int p0 = wv; p0 < np; p0 += 4 * 16) {
-    float v[16];
+  for (int p0 = wv; p0 < np; p0 += 4 * 32) {
+    float v[32];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < 32; ++k) {
       const int p = p0 + 4 * k;
       v[k] = p < np ? partial[p * Mp] : 0.f;
     }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) s += v[k];
+    for (int k = 0; k < 32; ++k) s += v[k];
   }
   wsum[wv][lane] = s;
   __syncthreads();
