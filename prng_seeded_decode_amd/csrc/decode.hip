@@ -4,78 +4,153 @@
 // emits; paperdance.org abstract, atlas.scime.ai "Approach"):
 //   I_i = sum_j t_j * (z_{j*C+i} - 2^15)      exact int32, |I_i| < 2^24
 //   w_i = I_i * 2^(e-15) = I_i * 2^(g-30)     exact in fp32 (power-of-two scale)
-// The kernel is bound by the 4-byte-per-weight writes; one thread rebuilds one
-// block and writes it with 16-byte stores where the row allows.
+// The kernel is bound by the 4-byte-per-weight writes, so the thread mapping
+// follows the output: thread k of a row writes columns 4k .. 4k+3 with one
+// 16-byte nontemporal store (the output is not re-read here), and consecutive
+// lanes write consecutive 16-byte chunks (C is a multiple of 4, so a chunk
+// never straddles two blocks).  The stream bits
+// past the seed come from two GF(2) byte tables in LDS (ext(s) = T0[s & 255] ^
+// T1[s >> 8]); z_n is the 16-bit window of the stream at bit n.
 #include "lfsr_device.h"
 #include "seedlm_internal.h"
 
 namespace seedlm {
 namespace {
 
+constexpr int kThreads = 256;
+typedef float f4 __attribute__((ext_vector_type(4)));
+
 __device__ inline float pow2f(int k) { return __int_as_float((k + 127) << 23); }
 
-template <int C, int P>
-__global__ void __launch_bounds__(256) decode_kernel(const uint32_t* __restrict__ words,
-                                                     const uint16_t* __restrict__ exps,
-                                                     float* __restrict__ W, int64_t rows,
-                                                     int64_t cols, int64_t nb, int64_t Mp,
-                                                     bool vec_ok) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= rows * nb) return;
-  const int64_t r = gid / nb, b = gid - r * nb;
-  const uint32_t w = words[word_index(r, b, Mp, nb)];
-  int g;
-  if constexpr (P == 3) {
-    g = (int)(w >> 28);
-  } else {
-    g = (exps[exp_index(r, b, Mp, nb)] >> (4 * exp_nibble(r, b))) & 0xF;
+template <int C>
+struct DecFmt;
+template <>
+struct DecFmt<8> {
+  static constexpr int P = 3;
+  using Ext = uint32_t;  // stream bits 16..47
+};
+template <>
+struct DecFmt<12> {
+  static constexpr int P = 4;
+  using Ext = uint64_t;  // stream bits 16..79 (63 used)
+};
+
+template <int C>
+__global__ void __launch_bounds__(kThreads) decode_kernel(const uint32_t* __restrict__ words,
+                                                          const uint16_t* __restrict__ exps,
+                                                          float* __restrict__ W, int rows,
+                                                          int cols, int nb, int Mp, bool vec_ok) {
+  using Ext = typename DecFmt<C>::Ext;
+  constexpr int P = DecFmt<C>::P;
+  __shared__ Ext T0[256], T1[256];
+  for (int e = threadIdx.x; e < 512; e += kThreads) {
+    const uint32_t u = (uint32_t)e & 255u;
+    if (e < 256) T0[u] = ext_bits<Ext>(u);
+    else T1[u] = ext_bits<Ext>(u << 8);
   }
-  const uint64_t stream = lfsr_stream<C * P + 15>(w);
-  int t[P];
+  __syncthreads();
+  const int col0 = 4 * (blockIdx.x * kThreads + threadIdx.x);
+  if (col0 >= cols) return;
+  const int b = col0 / C, i0 = col0 - b * C;  // block, first weight inside it
+  const int p = b / kPanelBlocks, q = b % kPanelBlocks;
+  const int Wp = (int)panel_stored_width(p, nb);
+  const int valid = cols - col0;  // >= 1
+  // Rows y, y + gy, ...: the record words of the next kRing rows are loaded
+  // ahead (clamped to a valid row, so no load is conditional) to keep enough
+  // reads in flight; each thread reads only 4 bytes per row.
+  const int gy = (int)gridDim.y;
+  const int64_t wbase = (int64_t)p * Mp * kPanelBlocks + (q & ~3);
+  const int64_t ebase = (int64_t)p * Mp * (kPanelBlocks / 4) + q / 4;
+  auto word_at = [&](int r) { return words[wbase + (int64_t)r * Wp + ((q - r) & 3)]; };
+  auto exp_at = [&](int r) -> uint32_t {
+    if constexpr (P == 3) return 0u;
+    else return exps[ebase + (int64_t)r * (Wp / 4)];
+  };
+  constexpr int kRing = 4;
+  uint32_t wr[kRing], er[kRing];
 #pragma unroll
-  for (int j = 0; j < P; ++j) t[j] = ((int)(w << (12 - 4 * j))) >> 28;  // sign-extend nibble
-  const float scale = pow2f(g - 30);
-  float out[C];
+  for (int k = 0; k < kRing; ++k) {
+    const int rr = min((int)blockIdx.y + k * gy, rows - 1);
+    wr[k] = word_at(rr);
+    er[k] = exp_at(rr);
+  }
+  for (int r0 = blockIdx.y; r0 < rows; r0 += kRing * gy) {
 #pragma unroll
-  for (int i = 0; i < C; ++i) {
-    int I = 0;
+    for (int k = 0; k < kRing; ++k) {
+      const int r = r0 + k * gy;
+      if (r >= rows) break;
+      const uint32_t w = wr[k];
+      const uint32_t ev = er[k];
+      {
+        const int rn = min(r + kRing * gy, rows - 1);
+        wr[k] = word_at(rn);
+        er[k] = exp_at(rn);
+      }
+      int g;
+      if constexpr (P == 3) {
+        g = (int)(w >> 28);
+      } else {
+        g = (int)(ev >> (4 * ((q - r) & 3))) & 0xF;
+      }
+      const Ext ext = T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];
+      // stream bits 0..63, shifted so that bit 0 is window i0's first bit
+      const uint64_t S = ((uint64_t)(w & 0xFFFFu) | ((uint64_t)ext << 16)) >> i0;
+      const uint32_t s0 = (uint32_t)S, s1 = (uint32_t)(S >> 16), s2 = (uint32_t)(S >> 32);
+      int t[P];
+      int base = 0;
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int z = (int)((stream >> (j * C + i)) & 0xFFFFu);
-      I += t[j] * (z - (int)kHalf);
+      for (int j = 0; j < P; ++j) {
+        t[j] = ((int)(w << (12 - 4 * j))) >> 28;  // sign-extend nibble
+        base -= t[j] * (int)kHalf;
+      }
+      const float scale = pow2f(g - 30);
+      float out[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int I = base;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          const int n = j * C + u;  // window offset from bit i0
+          const uint32_t z = n <= 16 ? __builtin_amdgcn_ubfe(s0, n, 16)
+                                     : (n <= 32 ? __builtin_amdgcn_ubfe(s1, n - 16, 16)
+                                                : __builtin_amdgcn_ubfe(s2, n - 32, 16));
+          I += t[j] * (int)z;
+        }
+        out[u] = (float)I * scale;
+      }
+      float* dst = W + (int64_t)r * cols + col0;
+      if (vec_ok && valid >= 4) {
+        __builtin_nontemporal_store(f4{out[0], out[1], out[2], out[3]}, reinterpret_cast<f4*>(dst));
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (u < valid) dst[u] = out[u];
+      }
     }
-    out[i] = (float)I * scale;
-  }
-  float* dst = W + r * cols + b * C;
-  const int64_t valid = cols - b * C;
-  if (vec_ok && valid >= C) {
-#pragma unroll
-    for (int i = 0; i < C; i += 4)
-      *reinterpret_cast<float4*>(dst + i) = make_float4(out[i], out[i + 1], out[i + 2], out[i + 3]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < C; ++i)
-      if (i < valid) dst[i] = out[i];
   }
 }
 
 }  // namespace
 
 int launch_decode(const seedlm_matrix* h, float* W, hipStream_t s) {
-  const int64_t n = h->rows * h->nb;
-  const int threads = 256;
-  const int64_t grid = (n + threads - 1) / threads;
-  if (grid > 0x7FFFFFFF) return SEEDLM_E_INVALID;
+  if (h->rows >= (1LL << 31) || h->cols >= (1LL << 31) - 4 || h->Mp >= (1LL << 31))
+    return SEEDLM_E_UNSUPPORTED;
+  const int64_t chunks = (h->cols + 3) / 4;
+  const int64_t gx = (chunks + kThreads - 1) / kThreads;
+  // Up to 2048 row slots; a workgroup handles rows y, y + 2048, ... (its GF(2)
+  // tables are built once for all of them).
+  const int64_t gy = h->rows < 2048 ? h->rows : 2048;
   const bool vec_ok = (h->cols % 4 == 0) && ((uintptr_t)W % 16 == 0);
   const uint32_t* words = static_cast<const uint32_t*>(h->d_buf);
   const uint16_t* exps =
       reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(h->d_buf) + h->exp_off);
+  const dim3 grid((unsigned)gx, (unsigned)gy);
   if (h->C == 8)
-    hipLaunchKernelGGL((decode_kernel<8, 3>), dim3((unsigned)grid), dim3(threads), 0, s, words,
-                       exps, W, h->rows, h->cols, h->nb, h->Mp, vec_ok);
+    hipLaunchKernelGGL(decode_kernel<8>, grid, dim3(kThreads), 0, s, words, exps, W,
+                       (int)h->rows, (int)h->cols, (int)h->nb, (int)h->Mp, vec_ok);
   else
-    hipLaunchKernelGGL((decode_kernel<12, 4>), dim3((unsigned)grid), dim3(threads), 0, s, words,
-                       exps, W, h->rows, h->cols, h->nb, h->Mp, vec_ok);
+    hipLaunchKernelGGL(decode_kernel<12>, grid, dim3(kThreads), 0, s, words, exps, W,
+                       (int)h->rows, (int)h->cols, (int)h->nb, (int)h->Mp, vec_ok);
   SEEDLM_HIP_CHECK(hipGetLastError());
   return SEEDLM_OK;
 }
