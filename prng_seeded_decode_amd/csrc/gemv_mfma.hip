@@ -133,7 +133,8 @@ __device__ inline void decode_c12(uint32_t w, uint32_t g, const uint64_t* T0, co
 }
 
 template <int C>
-__global__ void __launch_bounds__(kThreads) gemv_mfma_kernel(const MfmaArgs a) {
+__global__ void __launch_bounds__(kThreads)
+gemv_mfma_kernel(const MfmaArgs a) {
   using F = Fmt<C>;
   using Ext = typename F::Ext;
   __shared__ Ext T0[256], T1[256];
@@ -185,57 +186,77 @@ __global__ void __launch_bounds__(kThreads) gemv_mfma_kernel(const MfmaArgs a) {
 #pragma unroll
   for (int rho = 0; rho < 4; ++rho) acc[rho] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // Load unit k = 2*rho + h of panel p: the 16-byte record group (slots
+  // 4g .. 4g+3, g = 4h + q) of row r0 + rho + 4*i16, and its exponent nibbles
+  // (3-bit).  Units are loaded two ahead into a 4-slot ring; the ring crosses
+  // panel boundaries, and loads past the last panel read zeros.
+  auto unit_load = [&](int p, int k, v4u& wd, uint32_t& ev) {
+    const int rho = k >> 1, h = k & 1;
+    const int r = r0 + rho + 4 * i16;
+    const int g = 4 * h + q;
+    const int Wp = (int)panel_stored_width(p, a.nb);
+    const bool ok = p < pb && r < a.Mp && 4 * g < Wp;
+    const uint32_t off =
+        ok ? (uint32_t)(((int64_t)p * Mp * kPanelBlocks + (int64_t)r * Wp + 4 * g) * 4)
+           : 0x80000000u;
+    wd = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+    if constexpr (C == 12) {
+      const uint32_t eoff =
+          ok ? a.exp_off + (uint32_t)(((int64_t)p * Mp * (kPanelBlocks / 4) +
+                                       (int64_t)r * (Wp / 4) + g) * 2)
+             : 0x80000000u;
+      ev = __builtin_amdgcn_raw_buffer_load_b16(rsrc, eoff, 0, 0);
+    } else {
+      ev = 0u;
+    }
+  };
+  auto unit_compute = [&](const _Float16* xp, int k, const v4u wd, uint32_t ev) {
+    const int rho = k >> 1, h = k & 1;
+    const int g = 4 * h + q;  // slot group of this lane: slots 4g .. 4g+3
+    if constexpr (C == 8) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        // word n of the group holds slot 4g + ((n + row) & 3), row = rho mod 4
+        const int slot = 4 * g + ((n + rho) & 3);
+        const half8 A = decode_c8(wd[n], T0, T1);
+        const half8 B = *reinterpret_cast<const half8*>(xp + 8 * slot);
+        acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rho], 0, 0, 0);
+      }
+    } else {
+      _Float16 wv[48];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) decode_c12(wd[n], (ev >> (4 * n)) & 0xFu, T0, T1, wv + 12 * n);
+#pragma unroll
+      for (int m = 0; m < 6; ++m) {
+        half8 A, B;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) A[u] = wv[8 * m + u];
+        // x columns of weights 8m .. 8m+7: two runs of four inside blocks
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int u = 8 * m + 4 * hh;
+          const int slot = 4 * g + ((u / 12 + rho) & 3);
+          const half4 xv = *reinterpret_cast<const half4*>(xp + 12 * slot + u % 12);
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2) B[4 * hh + k2] = xv[k2];
+        }
+        acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rho], 0, 0, 0);
+      }
+    }
+  };
+
+  v4u ring[4];
+  uint32_t eRing[4];
+  unit_load(pa, 0, ring[0], eRing[0]);
+  unit_load(pa, 1, ring[1], eRing[1]);
   for (int p = pa; p < pb; ++p) {
     if (p + 1 < pb) fetch_x(p + 1);  // lands while this panel computes
-    const int Wp = (int)panel_stored_width(p, a.nb);
     const _Float16* xp = xs[p & 1] + i16 * F::kStride;
 #pragma unroll
-    for (int rho = 0; rho < 4; ++rho) {
-      const int r = r0 + rho + 4 * i16;
-#pragma unroll
-      for (int h = 0; h < kPanelBlocks / 16; ++h) {
-        const int g = 4 * h + q;  // slot group of this lane: slots 4g .. 4g+3
-        const bool ok = r < a.Mp && 4 * g < Wp;
-        const uint32_t off =
-            ok ? (uint32_t)(((int64_t)p * Mp * kPanelBlocks + (int64_t)r * Wp + 4 * g) * 4)
-               : 0x80000000u;
-        const v4u wd = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
-        if constexpr (C == 8) {
-#pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            // word n of the group holds slot 4g + ((n + row) & 3), row = rho mod 4
-            const int slot = 4 * g + ((n + rho) & 3);
-            const half8 A = decode_c8(wd[n], T0, T1);
-            const half8 B = *reinterpret_cast<const half8*>(xp + 8 * slot);
-            acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rho], 0, 0, 0);
-          }
-        } else {
-          const uint32_t eoff =
-              ok ? a.exp_off + (uint32_t)(((int64_t)p * Mp * (kPanelBlocks / 4) +
-                                           (int64_t)r * (Wp / 4) + g) * 2)
-                 : 0x80000000u;
-          const uint32_t ev = __builtin_amdgcn_raw_buffer_load_b16(rsrc, eoff, 0, 0);
-          _Float16 wv[48];
-#pragma unroll
-          for (int n = 0; n < 4; ++n) decode_c12(wd[n], (ev >> (4 * n)) & 0xFu, T0, T1, wv + 12 * n);
-#pragma unroll
-          for (int m = 0; m < 6; ++m) {
-            half8 A, B;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) A[u] = wv[8 * m + u];
-            // x columns of weights 8m .. 8m+7: two runs of four inside blocks
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int u = 8 * m + 4 * hh;
-              const int slot = 4 * g + ((u / 12 + rho) & 3);
-              const half4 xv = *reinterpret_cast<const half4*>(xp + 12 * slot + u % 12);
-#pragma unroll
-              for (int k = 0; k < 4; ++k) B[4 * hh + k] = xv[k];
-            }
-            acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rho], 0, 0, 0);
-          }
-        }
-      }
+    for (int k = 0; k < 8; ++k) {
+      const int kn = k + 2;
+      unit_load(kn < 8 ? p : p + 1, kn & 7, ring[kn & 3], eRing[kn & 3]);
+      unit_compute(xp, k, ring[k & 3], eRing[k & 3]);
     }
     if (p + 1 < pb) {
       store_x((p + 1) & 1);
