@@ -351,3 +351,32 @@ def test_gemv_many_graph_replays_match_eager():
         torch.cuda.synchronize()
         for a, b, o in zip(ys, ref, other):
             assert torch.equal(a, b) and torch.equal(o, b)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gemv_many_more_than_one_group(batch):
+    # Eleven matrices (more than one grouped launch), mixed formats, batch 1 and
+    # 4 (the matrix-core path): every output against the oracle and against a
+    # single seedlm_gemv call.
+    S = _S()
+    dev = _dev()
+    rng = np.random.default_rng(31 + batch)
+    shapes = [(8, 3, 40 + 16 * k, 8 * (20 + 7 * k) + (k % 3)) for k in range(9)]
+    shapes += [(12, 4, 50, 12 * 30 + 5), (8, 3, 8, 8)]
+    mats, refs, xs = [], [], []
+    for C, P, rows, cols in shapes:
+        s, c, e = _random_records(rng, rows, cols, C, P)
+        mats.append(_pack(s, c, e, rows, cols, C, P))
+        refs.append(O.decode_rows(s, c, e, cols, C, P))
+        xs.append(rng.standard_normal((batch, cols)).astype(np.float16))
+    xd = [torch.from_numpy(x).to(dev) for x in xs]
+    ys = [torch.empty((batch, m.rows), dtype=torch.float16, device=dev) for m in mats]
+    _say(f"gemv_many {len(mats)} matrices batch={batch}")
+    S.seedlm_gemv_many(mats, xd, ys, batch=batch)
+    single = [torch.empty_like(y) for y in ys]
+    for m, x, y in zip(mats, xd, single):
+        S.seedlm_gemv(m, x, y, batch=batch)
+    torch.cuda.synchronize()
+    for y, y1, W_ref, x in zip(ys, single, refs, xs):
+        assert O.normwise_error(y.float().cpu().numpy(), O.gemv(W_ref, x)) <= TOL["f16"]
+        assert torch.equal(y, y1)
