@@ -222,6 +222,55 @@ SEEDLM_API int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int 
 SEEDLM_API int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t rows,
                                 int64_t cols, int batch, void* stream);
 
+/*
+ * Seed search (compression).  SeedLM picks, for every block w of C weights, the
+ * seed s, coefficients t and shared exponent e that make 2^e U(s) t closest to
+ * w, searching all seeds (atlas.scime.ai "Approach"), with the pseudo-inverses
+ * of every seed computed once and cached and the search run in parallel over
+ * blocks and seeds (paperhub.cn rebuttal on compression cost).  The rule this
+ * library applies per seed: t* = pinv(U(s)) w; e = the smallest exponent in
+ * [-15, 0] at which every round-half-even(t*_j / 2^e) lies in [-8, 7] (0 if
+ * none); t = clamp(round-half-even(t* / 2^e), -8, 7); score ||w - 2^e U t||^2;
+ * the lowest score wins, the smaller seed on ties.  Scores are computed in
+ * fp32, so near-ties between seeds may resolve differently from an exact
+ * computation; the chosen record is always a valid one whose fp32 score is the
+ * minimum over all 65535 seeds.
+ */
+typedef struct seedlm_encoder* seedlm_encoder_handle;
+
+/*
+ * seedlm_encoder_create -- build, on the current device, the per-seed table of
+ * format (C, P, K) the search reads: the thin QR factors of U(s) for all 65535
+ * seeds (12 MiB for (8,3,16), 23 MiB for (12,4,16)).  Synchronous.  The
+ * handle owns the table.
+ * Errors: SEEDLM_E_INVALID (null out), SEEDLM_E_UNSUPPORTED ((C,P,K) not
+ * supported), SEEDLM_E_NOMEM, SEEDLM_E_DEVICE.
+ */
+SEEDLM_API int seedlm_encoder_create(int C, int P, int K, seedlm_encoder_handle* out);
+
+/* seedlm_encoder_destroy -- free the encoder's table; NULL is a no-op. */
+SEEDLM_API int seedlm_encoder_destroy(seedlm_encoder_handle e);
+
+/*
+ * seedlm_encode -- exhaustive seed search for every block of a dense matrix.
+ *   W      device bf16 [rows][cols] (raw bf16 bit patterns, row-major), cols a
+ *          multiple of C; 16-byte aligned for C = 8, 8-byte aligned for C = 12;
+ *          finite values
+ *   seeds  device uint16 [rows][nb], nb = cols / C     (out)
+ *   coeffs device int8   [rows][nb][P]                 (out)
+ *   exps   device int8   [rows][nb]                    (out)
+ *   err    device float  [rows][nb], the fp32 score of the chosen record, or
+ *          NULL                                        (out)
+ * The outputs are the record arrays seedlm_pack takes (after a copy to host).
+ * All buffers are caller-owned.  Asynchronous on `stream`; the encoder must have
+ * been created on the current device.  Calls sharing an encoder may overlap.
+ * Errors: SEEDLM_E_INVALID (null pointer, shape, alignment, other device),
+ * SEEDLM_E_UNSUPPORTED (grid too large), SEEDLM_E_DEVICE (launch failure).
+ */
+SEEDLM_API int seedlm_encode(seedlm_encoder_handle e, const void* W, int64_t rows,
+                             int64_t cols, uint16_t* seeds, int8_t* coeffs, int8_t* exps,
+                             float* err, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,11 +19,13 @@ from ._binding import (  # noqa: F401
     VARIANT_LUT,
     VARIANT_SIMPLE,
     VARIANT_TABLE,
+    SeedLMEncoder,
     SeedLMError,
     SeedLMMatrix,
     lib,
     pack_host_status,
     seedlm_decode,
+    seedlm_encode,
     seedlm_export,
     seedlm_fp16_gemv,
     seedlm_gemv,

@@ -41,6 +41,9 @@ EXPORTED = (
     "seedlm_export",
     "seedlm_status_string",
     "seedlm_fp16_gemv",
+    "seedlm_encoder_create",
+    "seedlm_encoder_destroy",
+    "seedlm_encode",
 )
 
 
@@ -91,6 +94,9 @@ def lib() -> ctypes.CDLL:
     L.seedlm_status_string.argtypes = [i32]
     L.seedlm_status_string.restype = ctypes.c_char_p
     L.seedlm_fp16_gemv.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    L.seedlm_encoder_create.argtypes = [i32, i32, i32, ctypes.POINTER(vp)]
+    L.seedlm_encoder_destroy.argtypes = [vp]
+    L.seedlm_encode.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp]
     for name in EXPORTED:
         if name != "seedlm_status_string":
             getattr(L, name).restype = i32
@@ -278,3 +284,68 @@ def seedlm_fp16_gemv(W, x, y, batch=None, stream=None):
                                   ctypes.c_void_p(y.data_ptr()), rows, cols, batch,
                                   _stream_ptr(stream)), "seedlm_fp16_gemv")
     return y
+
+
+class SeedLMEncoder:
+    """A seed-search encoder for one format on the current device (owns its table)."""
+
+    def __init__(self, C=8, P=3, K=16):
+        h = ctypes.c_void_p()
+        _check(lib().seedlm_encoder_create(C, P, K, ctypes.byref(h)), "seedlm_encoder_create")
+        self._h = h
+        self.C, self.P, self.K = C, P, K
+
+    @property
+    def handle(self):
+        if self._h is None or not self._h.value:
+            raise ValueError("encoder has been destroyed")
+        return self._h
+
+    def destroy(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(lib().seedlm_encoder_destroy(self._h), "seedlm_encoder_destroy")
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def seedlm_encode(enc: SeedLMEncoder, W, seeds=None, coeffs=None, exps=None, err=None,
+                  stream=None):
+    """Seed search for every block of W (bf16 device tensor [rows][cols]).
+
+    Returns device tensors seeds [rows][nb] (torch.int16 holding the uint16 bit
+    patterns), coeffs [rows][nb][P] int8, exps [rows][nb] int8 and err [rows][nb]
+    float32 (the fp32 score of each chosen record).  Preallocated outputs may be
+    passed in."""
+    import torch
+
+    if W.dtype != torch.bfloat16 or W.dim() != 2 or not (W.is_cuda and W.is_contiguous()):
+        raise ValueError("W must be a contiguous 2-D bfloat16 device tensor")
+    rows, cols = W.shape
+    if cols % enc.C:
+        raise ValueError("cols must be a multiple of C")
+    nb = cols // enc.C
+    dev = W.device
+    if seeds is None:
+        seeds = torch.empty((rows, nb), dtype=torch.int16, device=dev)
+    if coeffs is None:
+        coeffs = torch.empty((rows, nb, enc.P), dtype=torch.int8, device=dev)
+    if exps is None:
+        exps = torch.empty((rows, nb), dtype=torch.int8, device=dev)
+    if err is None:
+        err = torch.empty((rows, nb), dtype=torch.float32, device=dev)
+    for t, n in ((seeds, rows * nb), (coeffs, rows * nb * enc.P), (exps, rows * nb),
+                 (err, rows * nb)):
+        if t.numel() != n or not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("output tensors have the wrong size or are not contiguous")
+    _check(lib().seedlm_encode(enc.handle, ctypes.c_void_p(W.data_ptr()), rows, cols,
+                               ctypes.c_void_p(seeds.data_ptr()),
+                               ctypes.c_void_p(coeffs.data_ptr()),
+                               ctypes.c_void_p(exps.data_ptr()),
+                               ctypes.c_void_p(err.data_ptr()), _stream_ptr(stream)),
+           "seedlm_encode")
+    return seeds, coeffs, exps, err

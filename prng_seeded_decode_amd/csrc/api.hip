@@ -1,5 +1,6 @@
 // C-ABI entry points that launch kernels: argument checks and kernel choice.
 #include <mutex>
+#include <new>
 
 #include "lfsr_device.h"
 #include "seedlm_internal.h"
@@ -159,6 +160,56 @@ int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_
   if (!W || !x || !y || rows <= 0 || cols <= 0 || cols % 8 != 0) return SEEDLM_E_INVALID;
   if (batch < 1 || batch > SEEDLM_MAX_BATCH) return SEEDLM_E_INVALID;
   return launch_fp16_gemv(W, x, y, rows, cols, batch, static_cast<hipStream_t>(stream));
+}
+
+int seedlm_encoder_create(int C, int P, int K, seedlm_encoder_handle* out) {
+  if (!out) return SEEDLM_E_INVALID;
+  *out = nullptr;
+  if (!((C == 8 && P == 3 && K == 16) || (C == 12 && P == 4 && K == 16)))
+    return SEEDLM_E_UNSUPPORTED;
+  seedlm_encoder* e = new (std::nothrow) seedlm_encoder;
+  if (!e) return SEEDLM_E_NOMEM;
+  e->C = C;
+  e->P = P;
+  e->K = K;
+  e->table_bytes = encoder_table_bytes(C);
+  int rc = SEEDLM_OK;
+  if (hipGetDevice(&e->device) != hipSuccess) rc = SEEDLM_E_DEVICE;
+  if (rc == SEEDLM_OK && hipMalloc(&e->d_table, e->table_bytes) != hipSuccess) {
+    e->d_table = nullptr;
+    rc = SEEDLM_E_NOMEM;
+  }
+  if (rc == SEEDLM_OK) rc = launch_seed_table(C, e->d_table, nullptr);
+  if (rc == SEEDLM_OK && hipStreamSynchronize(nullptr) != hipSuccess) rc = SEEDLM_E_DEVICE;
+  if (rc != SEEDLM_OK) {
+    if (e->d_table) (void)hipFree(e->d_table);
+    delete e;
+    return rc;
+  }
+  *out = e;
+  return SEEDLM_OK;
+}
+
+int seedlm_encoder_destroy(seedlm_encoder_handle e) {
+  if (!e) return SEEDLM_OK;
+  int rc = SEEDLM_OK;
+  if (e->d_table && hipFree(e->d_table) != hipSuccess) rc = SEEDLM_E_DEVICE;
+  delete e;
+  return rc;
+}
+
+int seedlm_encode(seedlm_encoder_handle e, const void* W, int64_t rows, int64_t cols,
+                  uint16_t* seeds, int8_t* coeffs, int8_t* exps, float* err, void* stream) {
+  if (!e || !W || !seeds || !coeffs || !exps) return SEEDLM_E_INVALID;
+  if (rows <= 0 || cols <= 0 || cols % e->C != 0) return SEEDLM_E_INVALID;
+  const uintptr_t align = e->C == 8 ? 16 : 8;
+  if ((uintptr_t)W % align != 0) return SEEDLM_E_INVALID;
+  if (rows > INT64_MAX / cols) return SEEDLM_E_INVALID;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SEEDLM_E_DEVICE;
+  if (dev != e->device) return SEEDLM_E_INVALID;
+  return launch_encode(e->C, e->d_table, W, rows * (cols / e->C), seeds, coeffs, exps, err,
+                       static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,502 @@
+// seedlm_encode: exhaustive seed search on the matrix cores.
+//
+// SeedLM compresses a block w of C weights by finding, over every K-bit seed s,
+// the P coefficients and the shared exponent that bring 2^e U(s) t closest to w,
+// and storing the best seed with them (atlas.scime.ai "Approach").  The
+// pseudo-inverses of all seeds are computed once and cached, and the error
+// minimisation runs in parallel over blocks and seeds (paperhub.cn rebuttal on
+// compression cost).  For one seed the score is fixed as follows: least squares
+// t* = pinv(U) w; e = the smallest exponent in [-15, 0] at which every
+// round-half-even(t*_j / 2^e) lies in [-8, 7] (e = 0 if none does);
+// t = clamp(round-half-even(t* / 2^e), -8, 7); score ||w - 2^e U t||^2.  The
+// lowest score wins, the smaller seed on ties.
+//
+// How the kernels get there.  Per seed, U = Q R is a thin QR factorisation (Q
+// is C x P with orthonormal columns, R is upper triangular); seed_table_kernel
+// builds it once per encoder in fp64 (pinv(U) = R^-1 Q^T).  Then for any w
+//   c = Q^T w,   t* = R^-1 c,   ||w||^2 - ||c||^2 = least-squares residual,
+//   ||w - U tau||^2 = (||w||^2 - ||c||^2) + ||c - R tau||^2        (Pythagoras)
+// The least-squares residual is a lower bound on the score of every
+// quantisation, so a seed whose residual is not below the block's best score so
+// far cannot win and is dropped after three FMAs; only the rest (well under one
+// seed in a thousand on Gaussian blocks) is quantised and scored.  The score is
+// computed as residual + ||c - R tau||^2, which in fp32 can never come out
+// below the residual (rounding is monotone), so the dropping is exact for the
+// kernel's own arithmetic: the result is the exhaustive minimum of its fp32
+// scores.
+//
+// c = Q^T w for 16 seeds x 16 blocks is one MFMA per column j of Q:
+// v_mfma_f32_16x16x32_bf16 with A = the 16 seeds' column j (rows = seeds) and
+// B = 16 blocks (columns = blocks).  Weights come in as bf16, exact in the
+// operand.  Each Q entry is stored as the sum of three bf16 parts (hi + mid +
+// lo, about 24 significant bits) laid out along K, with the block's weights
+// repeated along K to match, so every product is exact and the sum is
+// accumulated in fp32.  For C = 8 the three parts fill K slots 0..23 of one
+// MFMA; for C = 12 hi and mid fill slots 0..23 of a 16x16x32 MFMA and lo slots
+// 0..11 of a v_mfma_f32_16x16x16_bf16, whose result is added on the VALU.  K
+// slots 24..31 (lanes 48..63) carry zero weights, so whatever finite A values
+// those lanes hold do not matter.
+//
+// Operand layout (wave64): lane l supplies K slots 8*(l/16) .. 8*(l/16)+7
+// (4*(l/16) .. +3 for the 16x16x16 form) of A row l%16 and of B column l%16;
+// the result gives lane l rows 4*(l/16)+v (v = 0..3) of column l%16.  So lane
+// l sees block (l%16) of the tile against seeds 4*(l/16) .. 4*(l/16)+3.
+//
+// Work split: a wave owns kTiles tiles of 16 consecutive blocks for the whole
+// search and keeps, per block, the best score, seed and record in registers;
+// the four lanes that share a block merge their bests after every tile step in
+// which any of them found a candidate.  A workgroup (4 waves) streams the seed
+// table through LDS in stages of a few 16-seed tiles, double-buffered, one
+// barrier per stage.
+#include <hip/hip_runtime.h>
+
+#include "seedlm_internal.h"
+
+namespace seedlm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSeedTiles = 4096;  // 16-seed tiles: seeds 1 .. 65536 (65536 is padding)
+constexpr int kEncThreads = 256;  // 4 waves
+constexpr int kLastSeed = 65535;
+
+template <int C>
+struct EncFmt;
+template <>
+struct EncFmt<8> {
+  static constexpr int P = 3;
+  static constexpr int kQBytes = 768;   // one column j of a tile: 48 lanes x 16 B
+  static constexpr int kTiles = 8;      // block tiles per wave
+  static constexpr int kStage = 8;      // seed tiles per LDS stage
+};
+template <>
+struct EncFmt<12> {
+  static constexpr int P = 4;
+  static constexpr int kQBytes = 1152;  // 48 lanes x 16 B (hi, mid) + 48 x 8 B (lo)
+  static constexpr int kTiles = 4;
+  static constexpr int kStage = 4;
+};
+
+template <int C>
+struct EncLayout {
+  static constexpr int P = EncFmt<C>::P;
+  static constexpr int NR = P * (P + 1) / 2;           // entries of an upper triangle
+  static constexpr int kRBytes = 2 * NR * 4;           // R^-1 then R, fp32, per seed
+  static constexpr int kTileBytes = P * EncFmt<C>::kQBytes + 16 * kRBytes;
+  static constexpr int kStageBytes = EncFmt<C>::kStage * kTileBytes;
+  static constexpr int kStages = kSeedTiles / EncFmt<C>::kStage;
+  static constexpr int kChunks = kStageBytes / 16;     // 16-byte pieces per stage
+  static constexpr int kChunksPerThread = (kChunks + kEncThreads - 1) / kEncThreads;
+  static constexpr int kBlocksPerWave = 16 * EncFmt<C>::kTiles;
+  static constexpr int kBlocksPerGroup = 4 * kBlocksPerWave;
+};
+static_assert(EncLayout<8>::kStageBytes % 16 == 0 && EncLayout<12>::kStageBytes % 16 == 0, "");
+static_assert(kSeedTiles % EncFmt<8>::kStage == 0 && kSeedTiles % EncFmt<12>::kStage == 0, "");
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ inline uint16_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ inline double bf16_value(uint16_t h) {
+  return (double)__uint_as_float((uint32_t)h << 16);
+}
+
+// One thread per seed: U(s) from the LFSR, thin QR by Gram-Schmidt with one
+// re-orthogonalisation pass (fp64), R^-1 by back substitution; Q's columns go
+// out as three bf16 parts each in the MFMA operand layout, R^-1 and R as fp32
+// upper triangles (row-major).  Seed 65536 (padding of the last tile) gets
+// zeros; the search never accepts it.
+template <int C>
+__global__ void __launch_bounds__(256) seed_table_kernel(uint8_t* __restrict__ table) {
+  using L = EncLayout<C>;
+  constexpr int P = L::P, NR = L::NR;
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= 16 * kSeedTiles) return;
+  const int seed = m + 1, tile = m >> 4, n = m & 15;
+  double Q[C][P], R[P][P], Ri[P][P];
+  for (int i = 0; i < P; ++i)
+    for (int j = 0; j < P; ++j) R[i][j] = Ri[i][j] = 0.0;
+  if (seed <= kLastSeed) {
+    uint32_t z = (uint32_t)seed;
+    for (int k = 0; k < C * P; ++k) {  // column-major fill: U[i][j] = v_{jC+i}
+      Q[k % C][k / C] = ((double)z - 32768.0) / 32768.0;
+      const uint32_t f = (z ^ (z >> 2) ^ (z >> 3) ^ (z >> 5)) & 1u;
+      z = (z >> 1) | (f << 15);
+    }
+    for (int j = 0; j < P; ++j) {
+      for (int pass = 0; pass < 2; ++pass)
+        for (int k = 0; k < j; ++k) {
+          double r = 0.0;
+          for (int i = 0; i < C; ++i) r += Q[i][k] * Q[i][j];
+          for (int i = 0; i < C; ++i) Q[i][j] -= r * Q[i][k];
+          R[k][j] += r;
+        }
+      double nn = 0.0;
+      for (int i = 0; i < C; ++i) nn += Q[i][j] * Q[i][j];
+      R[j][j] = sqrt(nn);
+      for (int i = 0; i < C; ++i) Q[i][j] /= R[j][j];
+    }
+    for (int i = P - 1; i >= 0; --i) {
+      Ri[i][i] = 1.0 / R[i][i];
+      for (int j = i + 1; j < P; ++j) {
+        double s = 0.0;
+        for (int k = i; k < j; ++k) s += Ri[i][k] * R[k][j];
+        Ri[i][j] = -s / R[j][j];
+      }
+    }
+  } else {
+    for (int i = 0; i < C; ++i)
+      for (int j = 0; j < P; ++j) Q[i][j] = 0.0;
+  }
+  uint8_t* tb = table + (size_t)tile * L::kTileBytes;
+  for (int j = 0; j < P; ++j) {
+    uint16_t part[3][C];
+    for (int i = 0; i < C; ++i) {
+      const double q = Q[i][j];
+      part[0][i] = bf16_bits((float)q);
+      const double r1 = q - bf16_value(part[0][i]);
+      part[1][i] = bf16_bits((float)r1);
+      const double r2 = r1 - bf16_value(part[1][i]);
+      part[2][i] = bf16_bits((float)r2);
+    }
+    uint8_t* col = tb + j * EncFmt<C>::kQBytes;
+    // K slot k (0..23) of the 32-wide operand holds part k / C, entry k % C:
+    // hi, mid, lo for C = 8; hi, mid for C = 12 (lo goes to the 16-wide one).
+    for (int qg = 0; qg < 3; ++qg) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(col + (16 * qg + n) * 16);
+      for (int u = 0; u < 8; ++u) {
+        const int k = 8 * qg + u;
+        dst[u] = part[k / C][k % C];
+      }
+    }
+    if (C == 12) {  // lo part: K slots 0..11 of the 16-wide operand
+      for (int qg = 0; qg < 3; ++qg) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(col + 768 + (16 * qg + n) * 8);
+        for (int u = 0; u < 4; ++u) dst[u] = part[2][4 * qg + u];
+      }
+    }
+  }
+  float* rd = reinterpret_cast<float*>(tb + P * EncFmt<C>::kQBytes + n * L::kRBytes);
+  int o = 0;
+  for (int i = 0; i < P; ++i)
+    for (int j = i; j < P; ++j, ++o) {
+      rd[o] = (float)Ri[i][j];
+      rd[NR + o] = (float)R[i][j];
+    }
+}
+
+struct EncArgs {
+  const uint8_t* table;
+  const uint16_t* W;  // bf16 bits, nblk blocks of C
+  int64_t nblk;
+  uint16_t* seeds;
+  int8_t* coeffs;
+  int8_t* exps;
+  float* err;  // may be null
+};
+
+// The block's weights as the B operand(s) of the MFMAs, and its squared norm.
+template <int C>
+struct BlockOps;
+template <>
+struct BlockOps<8> {
+  bf16x8 b1;
+  __device__ void load(const uint16_t* W, int64_t b, bool valid, int qg, float& wn) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) v = *reinterpret_cast<const uint4*>(W + b * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = __uint_as_float(((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
+      s = fmaf(x, x, s);
+    }
+    wn = s;
+    if (qg == 3) v = make_uint4(0u, 0u, 0u, 0u);  // K slots 24..31 are unused
+    b1 = __builtin_bit_cast(bf16x8, v);
+  }
+};
+template <>
+struct BlockOps<12> {
+  bf16x8 b1;
+  s16x4 b2;
+  __device__ void load(const uint16_t* W, int64_t b, bool valid, int qg, float& wn) {
+    uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+    if (valid) {
+      const uint2* p = reinterpret_cast<const uint2*>(W + b * 12);
+#pragma unroll
+      for (int h = 0; h < 3; ++h) {
+        const uint2 v = p[h];
+        w[2 * h] = v.x;
+        w[2 * h + 1] = v.y;
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      const float x = __uint_as_float(((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
+      s = fmaf(x, x, s);
+    }
+    wn = s;
+    // 32-wide operand: slots 0..11 and 12..23 both hold w0..w11 (against hi
+    // and mid); lane group qg holds slots 8qg .. 8qg+7, i.e. words
+    // (4qg .. 4qg+3) mod 6.  16-wide operand: slots 0..11 hold w0..w11 (lo).
+    uint4 v1 = make_uint4(0u, 0u, 0u, 0u);
+    uint2 v2 = make_uint2(0u, 0u);
+    if (qg < 3) {
+      v1 = make_uint4(w[(4 * qg) % 6], w[(4 * qg + 1) % 6], w[(4 * qg + 2) % 6],
+                      w[(4 * qg + 3) % 6]);
+      v2 = make_uint2(w[2 * qg], w[2 * qg + 1]);
+    }
+    b1 = __builtin_bit_cast(bf16x8, v1);
+    b2 = __builtin_bit_cast(s16x4, v2);
+  }
+};
+
+template <int P>
+__device__ inline uint32_t pack_record(const float (&t)[P], int e) {
+  uint32_t r = (uint32_t)(e + 15) << 16;
+#pragma unroll
+  for (int j = 0; j < P; ++j) r |= ((uint32_t)(int)t[j] & 15u) << (4 * j);
+  return r;
+}
+
+template <int C>
+__global__ void __launch_bounds__(kEncThreads, 2) encode_kernel(const EncArgs a) {
+  using L = EncLayout<C>;
+  using F = EncFmt<C>;
+  constexpr int P = L::P, NR = L::NR, NT = F::kTiles, G = F::kStage;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][L::kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, qg = lane >> 4;
+  const int64_t block0 = ((int64_t)blockIdx.x * 4 + wave) * L::kBlocksPerWave;
+
+  BlockOps<C> ops[NT];
+  float nwn[NT], best[NT];
+  int bseed[NT];
+  uint32_t brec[NT];
+#pragma unroll
+  for (int T = 0; T < NT; ++T) {
+    const int64_t b = block0 + 16 * T + n;
+    float wn;
+    ops[T].load(a.W, b, b < a.nblk, qg, wn);
+    nwn[T] = -wn;
+    best[T] = __builtin_inff();
+    bseed[T] = 0;
+    brec[T] = 0u;
+  }
+
+  // Stage s of the table: bytes s*kStageBytes .. (s+1)*kStageBytes, copied by
+  // the workgroup in 16-byte pieces (piece c by thread c % 256).
+  uint4 pre[L::kChunksPerThread];
+  auto fetch = [&](int s) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.table + (size_t)s * L::kStageBytes);
+#pragma unroll
+    for (int r = 0; r < L::kChunksPerThread; ++r) {
+      const int c = tid + r * kEncThreads;
+      if (c < L::kChunks) pre[r] = src[c];
+    }
+  };
+  auto put = [&](int buf) {
+    uint4* dst = reinterpret_cast<uint4*>(stage[buf]);
+#pragma unroll
+    for (int r = 0; r < L::kChunksPerThread; ++r) {
+      const int c = tid + r * kEncThreads;
+      if (c < L::kChunks) dst[c] = pre[r];
+    }
+  };
+  fetch(0);
+  put(0);
+  __syncthreads();
+
+  const int alane = lane % 48;  // lanes 48..63 re-read lanes 0..15 (their B is zero)
+  for (int st = 0; st < L::kStages; ++st) {
+    if (st + 1 < L::kStages) fetch(st + 1);
+    const uint8_t* sb = stage[st & 1];
+    for (int s = 0; s < G; ++s) {
+      const uint8_t* tb = sb + s * L::kTileBytes;
+      bf16x8 A1[P];
+      s16x4 A2[P];
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        A1[j] = *reinterpret_cast<const bf16x8*>(tb + j * F::kQBytes + alane * 16);
+        if constexpr (C == 12)
+          A2[j] = *reinterpret_cast<const s16x4*>(tb + j * F::kQBytes + 768 + alane * 8);
+      }
+      const int seed_base = (st * G + s) * 16 + 1 + 4 * qg;  // seed of this lane's row v = 0
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        f32x4 acc[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[j], ops[T].b1, zero, 0, 0, 0);
+          if constexpr (C == 12) {
+            // The lo part gets an accumulator of its own: chaining this MFMA onto
+            // the 16x16x32 result (a different opcode) read a stale accumulator
+            // when the two were issued back to back, and the compiler does not
+            // separate them.
+            const f32x4 lo = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A2[j], ops[T].b2, zero, 0, 0, 0);
+            acc[j] += lo;
+          }
+        }
+        // -(least-squares residual) = ||c||^2 - ||w||^2; a seed is a candidate
+        // when its residual is below the best score.
+        float Lv[4];
+        bool any = false;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float s2 = fmaf(acc[0][v], acc[0][v], nwn[T]);
+#pragma unroll
+          for (int j = 1; j < P; ++j) s2 = fmaf(acc[j][v], acc[j][v], s2);
+          Lv[v] = s2;
+          any |= s2 > -best[T];
+        }
+        if (!__builtin_amdgcn_ballot_w64(any)) continue;
+        // Candidate path (rare): quantise and score, lane by lane.
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const bool cand = Lv[v] > -best[T];
+          if (!__builtin_amdgcn_ballot_w64(cand)) continue;
+          const int seed = seed_base + v;
+          const float* rd =
+              reinterpret_cast<const float*>(tb + P * F::kQBytes + (4 * qg + v) * L::kRBytes);
+          float Ri[NR], Rm[NR];
+#pragma unroll
+          for (int o = 0; o < NR; ++o) {
+            Ri[o] = rd[o];
+            Rm[o] = rd[NR + o];
+          }
+          float c[P], ts[P];
+#pragma unroll
+          for (int j = 0; j < P; ++j) c[j] = acc[j][v];
+          // t* = R^-1 c (upper triangular, row-major packed)
+          {
+            int o = 0;
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+              float s = Ri[o] * c[i];
+              ++o;
+#pragma unroll
+              for (int k = i + 1; k < P; ++k, ++o) s = fmaf(Ri[o], c[k], s);
+              ts[i] = s;
+            }
+          }
+          float hi = ts[0], lo = ts[0];
+#pragma unroll
+          for (int j = 1; j < P; ++j) {
+            hi = fmaxf(hi, ts[j]);
+            lo = fminf(lo, ts[j]);
+          }
+          // Smallest e with hi * 2^-e < 7.5 and lo * 2^-e >= -8.5 (the range that
+          // rounds half-to-even into [-8, 7]): with hi = f 2^k, f in [0.5, 1),
+          // e = k - 3 when f < 15/16, else k - 2; with -lo = g 2^k, e = k - 4 when
+          // g <= 17/32, else k - 3.
+          int e_hi = -64, e_lo = -64;
+          if (hi > 0.f) {
+            int k;
+            const float f = frexpf(hi, &k);
+            e_hi = k - 3 + (f >= 0.9375f ? 1 : 0);
+          }
+          if (lo < 0.f) {
+            int k;
+            const float g = frexpf(-lo, &k);
+            e_lo = k - 4 + (g > 0.53125f ? 1 : 0);
+          }
+          const int e = min(max(max(e_hi, e_lo), -15), 0);
+          float t[P], tau[P];
+#pragma unroll
+          for (int j = 0; j < P; ++j) {
+            t[j] = fminf(fmaxf(rintf(ldexpf(ts[j], -e)), -8.f), 7.f);
+            tau[j] = ldexpf(t[j], e);
+          }
+          // score = residual + ||c - R tau||^2
+          float q2 = 0.f;
+          {
+            int o = 0;
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+              float d = c[i];
+#pragma unroll
+              for (int k = i; k < P; ++k, ++o) d = fmaf(-Rm[o], tau[k], d);
+              q2 = fmaf(d, d, q2);
+            }
+          }
+          const float score = fmaxf(q2 - Lv[v], 0.f);
+          if (cand && seed <= kLastSeed && score < best[T]) {
+            best[T] = score;
+            bseed[T] = seed;
+            brec[T] = pack_record<P>(t, e);
+          }
+        }
+        // Merge the four lanes that share the block (lane groups qg = 0..3).
+#pragma unroll
+        for (int off = 16; off <= 32; off *= 2) {
+          const float ob = __shfl_xor(best[T], off);
+          const int os = __shfl_xor(bseed[T], off);
+          const uint32_t orc = (uint32_t)__shfl_xor((int)brec[T], off);
+          if (ob < best[T] || (ob == best[T] && os < bseed[T])) {
+            best[T] = ob;
+            bseed[T] = os;
+            brec[T] = orc;
+          }
+        }
+      }
+    }
+    if (st + 1 < L::kStages) put((st + 1) & 1);
+    __syncthreads();
+  }
+
+  if (qg == 0) {
+#pragma unroll
+    for (int T = 0; T < NT; ++T) {
+      const int64_t b = block0 + 16 * T + n;
+      if (b >= a.nblk) continue;
+      a.seeds[b] = (uint16_t)bseed[T];
+      a.exps[b] = (int8_t)((int)(brec[T] >> 16) - 15);
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const int nib = (int)((brec[T] >> (4 * j)) & 15u);
+        a.coeffs[b * P + j] = (int8_t)(nib - ((nib & 8) << 1));
+      }
+      if (a.err) a.err[b] = best[T];
+    }
+  }
+}
+
+}  // namespace
+
+size_t encoder_table_bytes(int C) {
+  return (size_t)kSeedTiles * (C == 8 ? EncLayout<8>::kTileBytes : EncLayout<12>::kTileBytes);
+}
+
+int launch_seed_table(int C, void* table, hipStream_t s) {
+  const dim3 grid(16 * kSeedTiles / 256), block(256);
+  if (C == 8)
+    hipLaunchKernelGGL(seed_table_kernel<8>, grid, block, 0, s, static_cast<uint8_t*>(table));
+  else
+    hipLaunchKernelGGL(seed_table_kernel<12>, grid, block, 0, s, static_cast<uint8_t*>(table));
+  SEEDLM_HIP_CHECK(hipGetLastError());
+  return SEEDLM_OK;
+}
+
+int launch_encode(int C, const void* table, const void* W, int64_t nblk, uint16_t* seeds,
+                  int8_t* coeffs, int8_t* exps, float* err, hipStream_t s) {
+  const int64_t per = C == 8 ? EncLayout<8>::kBlocksPerGroup : EncLayout<12>::kBlocksPerGroup;
+  const int64_t groups = (nblk + per - 1) / per;
+  if (groups > 0x7FFFFFFF) return SEEDLM_E_UNSUPPORTED;
+  EncArgs a{static_cast<const uint8_t*>(table), static_cast<const uint16_t*>(W), nblk, seeds,
+            coeffs, exps, err};
+  if (C == 8)
+    hipLaunchKernelGGL(encode_kernel<8>, dim3((unsigned)groups), dim3(kEncThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(encode_kernel<12>, dim3((unsigned)groups), dim3(kEncThreads), 0, s, a);
+  SEEDLM_HIP_CHECK(hipGetLastError());
+  return SEEDLM_OK;
+}
+
+}  // namespace seedlm

@@ -37,6 +37,14 @@ struct seedlm_matrix {
   uint32_t* d_ext_table = nullptr;  // 2^16-entry extension table (variant TABLE)
 };
 
+// An encoder: the per-seed table of one format on one device.
+struct seedlm_encoder {
+  int C = 0, P = 0, K = 0;
+  int device = 0;
+  void* d_table = nullptr;
+  size_t table_bytes = 0;
+};
+
 namespace seedlm {
 
 // Layout helpers (host and device).  Rows are padded to Mp = 8*ceil(rows/8).
@@ -87,6 +95,11 @@ int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, 
 int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,
                      int batch, hipStream_t s);
 int build_ext_table(seedlm_matrix* h);
+// Seed search: per-seed QR table (bytes for format C) and the search itself.
+size_t encoder_table_bytes(int C);
+int launch_seed_table(int C, void* table, hipStream_t s);
+int launch_encode(int C, const void* table, const void* W, int64_t nblk, uint16_t* seeds,
+                  int8_t* coeffs, int8_t* exps, float* err, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -104,3 +104,25 @@ def gen_gaussian_matrix(config_id: int, matrix_id: int, rows: int, cols: int):
     """A dense N(0,1) float64 matrix (the encoder self-check input)."""
     rng = np.random.default_rng([config_id, matrix_id])
     return rng.standard_normal((rows, cols))
+
+
+def gen_bf16_weights(config_id: int, matrix_id: int, rows: int, cols: int, scale: float = 1.0):
+    """Dense N(0, scale^2) weights rounded to bf16 (round to nearest even).
+
+    Returns the raw bf16 bit patterns (uint16 [rows][cols]); LLM checkpoints hold
+    their weights in this format, and it is the encoder's input type.
+    """
+    rng = np.random.default_rng([config_id, matrix_id, 7])
+    return to_bf16_bits(rng.standard_normal((rows, cols)) * scale)
+
+
+def to_bf16_bits(a) -> np.ndarray:
+    """bf16 bit patterns of float values (via fp32, round to nearest even; finite)."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def bf16_to_float64(bits: np.ndarray) -> np.ndarray:
+    """The float64 values of bf16 bit patterns (exact)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
