@@ -45,9 +45,9 @@
 // Work split: a wave owns kTiles tiles of 16 consecutive blocks for the whole
 // search and keeps, per block, the best score, seed and record in registers;
 // the four lanes that share a block merge their bests after every tile step in
-// which any of them found a candidate.  A workgroup (4 waves) streams the seed
-// table through LDS in stages of a few 16-seed tiles, double-buffered, one
-// barrier per stage.
+// which any of them improved.  A workgroup (8 waves) streams the seed table
+// through LDS in stages of a few 16-seed tiles, double-buffered, one barrier per
+// stage; two workgroups share a CU (four waves per SIMD).
 #include <hip/hip_runtime.h>
 
 #include "seedlm_internal.h"
@@ -60,7 +60,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSeedTiles = 4096;  // 16-seed tiles: seeds 1 .. 65536 (65536 is padding)
-constexpr int kEncThreads = 256;  // 4 waves
+constexpr int kEncThreads = 512;  // 8 waves
 constexpr int kLastSeed = 65535;
 
 template <int C>
@@ -91,10 +91,12 @@ struct EncLayout {
   static constexpr int kChunks = kStageBytes / 16;     // 16-byte pieces per stage
   static constexpr int kChunksPerThread = (kChunks + kEncThreads - 1) / kEncThreads;
   static constexpr int kBlocksPerWave = 16 * EncFmt<C>::kTiles;
-  static constexpr int kBlocksPerGroup = 4 * kBlocksPerWave;
+  static constexpr int kBlocksPerGroup = (kEncThreads / 64) * kBlocksPerWave;
 };
 static_assert(EncLayout<8>::kStageBytes % 16 == 0 && EncLayout<12>::kStageBytes % 16 == 0, "");
 static_assert(kSeedTiles % EncFmt<8>::kStage == 0 && kSeedTiles % EncFmt<12>::kStage == 0, "");
+static_assert(EncLayout<8>::kChunks % 64 == 0 && EncLayout<12>::kChunks % 64 == 0,
+              "a stage splits into whole 1 KiB wave pieces");
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ inline uint16_t bf16_bits(float f) {
@@ -266,14 +268,17 @@ __device__ inline uint32_t pack_record(const float (&t)[P], int e) {
 }
 
 template <int C>
-__global__ void __launch_bounds__(kEncThreads, 2) encode_kernel(const EncArgs a) {
+__global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a) {
   using L = EncLayout<C>;
   using F = EncFmt<C>;
   constexpr int P = L::P, NR = L::NR, NT = F::kTiles, G = F::kStage;
-  __shared__ __attribute__((aligned(16))) uint8_t stage[2][L::kStageBytes];
+  // Two stage buffers as separate objects, so that the compiler can tell that
+  // reads of one never wait for the copy into the other.
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[L::kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[L::kStageBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, qg = lane >> 4;
-  const int64_t block0 = ((int64_t)blockIdx.x * 4 + wave) * L::kBlocksPerWave;
+  const int64_t block0 = ((int64_t)blockIdx.x * (kEncThreads / 64) + wave) * L::kBlocksPerWave;
 
   BlockOps<C> ops[NT];
   float nwn[NT], best[NT];
@@ -290,33 +295,24 @@ __global__ void __launch_bounds__(kEncThreads, 2) encode_kernel(const EncArgs a)
     brec[T] = 0u;
   }
 
-  // Stage s of the table: bytes s*kStageBytes .. (s+1)*kStageBytes, copied by
-  // the workgroup in 16-byte pieces (piece c by thread c % 256).
-  uint4 pre[L::kChunksPerThread];
-  auto fetch = [&](int s) {
-    const uint4* src = reinterpret_cast<const uint4*>(a.table + (size_t)s * L::kStageBytes);
+  // Stage st of the table (bytes st*kStageBytes ..) is copied straight into LDS
+  // (global_load_lds, 16 bytes per lane: wave w's lanes fill 1 KiB pieces
+  // r*kEncThreads + 64w .. +63), one stage ahead of its use; the barrier after
+  // each stage waits for the copy.
+  auto fetch = [&](int st, uint8_t* dst) {
+    const uint8_t* src = a.table + (size_t)st * L::kStageBytes;
 #pragma unroll
     for (int r = 0; r < L::kChunksPerThread; ++r) {
-      const int c = tid + r * kEncThreads;
-      if (c < L::kChunks) pre[r] = src[c];
+      const int c0 = r * kEncThreads + 64 * wave;  // wave-uniform
+      if (c0 < L::kChunks)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(src + (size_t)(c0 + lane) * 16),
+            (__attribute__((address_space(3))) void*)(dst + c0 * 16), 16, 0, 0);
     }
   };
-  auto put = [&](int buf) {
-    uint4* dst = reinterpret_cast<uint4*>(stage[buf]);
-#pragma unroll
-    for (int r = 0; r < L::kChunksPerThread; ++r) {
-      const int c = tid + r * kEncThreads;
-      if (c < L::kChunks) dst[c] = pre[r];
-    }
-  };
-  fetch(0);
-  put(0);
-  __syncthreads();
 
   const int alane = lane % 48;  // lanes 48..63 re-read lanes 0..15 (their B is zero)
-  for (int st = 0; st < L::kStages; ++st) {
-    if (st + 1 < L::kStages) fetch(st + 1);
-    const uint8_t* sb = stage[st & 1];
+  auto run_stage = [&](const uint8_t* sb, int st) {
     for (int s = 0; s < G; ++s) {
       const uint8_t* tb = sb + s * L::kTileBytes;
       bf16x8 A1[P];
@@ -328,9 +324,8 @@ __global__ void __launch_bounds__(kEncThreads, 2) encode_kernel(const EncArgs a)
           A2[j] = *reinterpret_cast<const s16x4*>(tb + j * F::kQBytes + 768 + alane * 8);
       }
       const int seed_base = (st * G + s) * 16 + 1 + 4 * qg;  // seed of this lane's row v = 0
-#pragma unroll
-      for (int T = 0; T < NT; ++T) {
-        f32x4 acc[P];
+      // c = Q^T w for this seed tile against block tile T.
+      auto tile_acc = [&](int T, f32x4 (&acc)[P]) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
           const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -344,23 +339,40 @@ __global__ void __launch_bounds__(kEncThreads, 2) encode_kernel(const EncArgs a)
             acc[j] += lo;
           }
         }
-        // -(least-squares residual) = ||c||^2 - ||w||^2; a seed is a candidate
-        // when its residual is below the best score.
-        float Lv[4];
-        bool any = false;
+      };
+      // -(least-squares residual) = ||c||^2 - ||w||^2, as one fixed FMA chain.
+      auto neg_residual = [&](int T, const f32x4 (&acc)[P], int v) {
+        float s2 = fmaf(acc[0][v], acc[0][v], nwn[T]);
+#pragma unroll
+        for (int j = 1; j < P; ++j) s2 = fmaf(acc[j][v], acc[j][v], s2);
+        return s2;
+      };
+      // Pass 1, the hot loop: one flag bit per block tile, set when some seed's
+      // residual is below the block's best score.  No branch between tiles, so
+      // one tile's MFMAs overlap the previous tile's arithmetic.
+      uint32_t flags = 0;  // wave-uniform: bit T set when any lane of tile T has a candidate
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        f32x4 acc[P];
+        tile_acc(T, acc);
+        float m = neg_residual(T, acc, 0);
+#pragma unroll
+        for (int v = 1; v < 4; ++v) m = fmaxf(m, neg_residual(T, acc, v));
+        if (__builtin_amdgcn_ballot_w64(m > -best[T])) flags |= 1u << T;
+      }
+      if (flags == 0) continue;
+      // Pass 2 (rare): the flagged tiles again (same MFMAs, same values), each
+      // candidate seed quantised and scored.
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        if (!((flags >> T) & 1u)) continue;
+        f32x4 acc[P];
+        tile_acc(T, acc);
+        bool improved = false;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float s2 = fmaf(acc[0][v], acc[0][v], nwn[T]);
-#pragma unroll
-          for (int j = 1; j < P; ++j) s2 = fmaf(acc[j][v], acc[j][v], s2);
-          Lv[v] = s2;
-          any |= s2 > -best[T];
-        }
-        if (!__builtin_amdgcn_ballot_w64(any)) continue;
-        // Candidate path (rare): quantise and score, lane by lane.
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const bool cand = Lv[v] > -best[T];
+          const float Lv = neg_residual(T, acc, v);
+          const bool cand = Lv > -best[T];
           if (!__builtin_amdgcn_ballot_w64(cand)) continue;
           const int seed = seed_base + v;
           const float* rd =
@@ -379,11 +391,11 @@ __global__ void __launch_bounds__(kEncThreads, 2) encode_kernel(const EncArgs a)
             int o = 0;
 #pragma unroll
             for (int i = 0; i < P; ++i) {
-              float s = Ri[o] * c[i];
+              float sum = Ri[o] * c[i];
               ++o;
 #pragma unroll
-              for (int k = i + 1; k < P; ++k, ++o) s = fmaf(Ri[o], c[k], s);
-              ts[i] = s;
+              for (int k = i + 1; k < P; ++k, ++o) sum = fmaf(Ri[o], c[k], sum);
+              ts[i] = sum;
             }
           }
           float hi = ts[0], lo = ts[0];
@@ -426,14 +438,17 @@ __global__ void __launch_bounds__(kEncThreads, 2) encode_kernel(const EncArgs a)
               q2 = fmaf(d, d, q2);
             }
           }
-          const float score = fmaxf(q2 - Lv[v], 0.f);
+          const float score = fmaxf(q2 - Lv, 0.f);
           if (cand && seed <= kLastSeed && score < best[T]) {
             best[T] = score;
             bseed[T] = seed;
             brec[T] = pack_record<P>(t, e);
+            improved = true;
           }
         }
-        // Merge the four lanes that share the block (lane groups qg = 0..3).
+        // Merge the four lanes that share the block (lane groups qg = 0..3),
+        // needed only when one of them found a better seed.
+        if (!__builtin_amdgcn_ballot_w64(improved)) continue;
 #pragma unroll
         for (int off = 16; off <= 32; off *= 2) {
           const float ob = __shfl_xor(best[T], off);
@@ -447,7 +462,17 @@ __global__ void __launch_bounds__(kEncThreads, 2) encode_kernel(const EncArgs a)
         }
       }
     }
-    if (st + 1 < L::kStages) put((st + 1) & 1);
+  };
+
+  static_assert(L::kStages % 2 == 0, "stages alternate between two buffers");
+  fetch(0, stage0);
+  __syncthreads();
+  for (int st = 0; st < L::kStages; st += 2) {
+    fetch(st + 1, stage1);
+    run_stage(stage0, st);
+    __syncthreads();
+    if (st + 2 < L::kStages) fetch(st + 2, stage0);
+    run_stage(stage1, st + 1);
     __syncthreads();
   }
 
