@@ -14,6 +14,13 @@ Prints one JSON line: effective weights/s (value), compressed HBM GB/s and its
 fraction of 8 TB/s, the roofline of the fused kernel (HIP events on the launch
 stream), the same-chip fp16 GEMV baseline and its speed-up, and the CPU oracle
 timed on a bounded sample of the same workload.
+
+    python bench.py --encode [--encode-bits 4|3] [--steps K] [--warmup W]
+
+times the seed-search encoder instead: one step = one 8192x8192 bf16 matrix
+(Llama-3-70B q_proj shape) encoded by exhaustive search over all 65535 seeds,
+with its own JSON line (encoded weights/s, the search kernel's roofline, and
+the oracle's exhaustive encoder timed on sampled blocks).
 """
 from __future__ import annotations
 
@@ -73,6 +80,12 @@ def parse_args():
                    help="also time seedlm_decode (dense fp32 W) on the largest matrix")
     p.add_argument("--graph", type=int, default=0,
                    help="1: replay each step as a captured HIP graph (one per rotated copy)")
+    p.add_argument("--encode", action="store_true",
+                   help="time the seed-search encoder instead (one step = one matrix encoded)")
+    p.add_argument("--encode-bits", type=int, default=4, choices=(3, 4))
+    p.add_argument("--encode-shape", type=str, default="",
+                   help="rows,cols of the encoded matrix (default: the Llama-3-70B q_proj "
+                        "shape, columns rounded up to a multiple of C)")
     return p.parse_args()
 
 
@@ -122,12 +135,129 @@ def cpu_baseline(cfg, budget_s):
     }
 
 
+ENC_METRIC = "encoded weights/s (bf16 -> SeedLM, exhaustive search over all 65535 seeds)"
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def cpu_encode_baseline(bits, C, P, budget_s):
+    """Time the oracle's exhaustive encoder on whole blocks sampled from the matrix."""
+    from oracle import seedlm_oracle as O
+    from workloads import bf16_to_float64
+
+    Wb = bf16_to_float64(bits).reshape(-1, C)
+    rng = np.random.default_rng(4321)
+    n, blocks, t = 8, 0, 0.0
+    while t < budget_s:
+        pick = rng.choice(Wb.shape[0], size=n, replace=False)
+        t0 = time.perf_counter()
+        O.encode_exhaustive(Wb[pick], C, P)
+        t += time.perf_counter() - t0
+        blocks += n
+        n = min(2 * n, 256)
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {
+        "value": blocks * C / t,
+        "unit": "weights/s",
+        "cores": int(max(1, blas)),
+        "kind": "oracle",
+        "sample": (f"{blocks} blocks ({blocks * C} weights) sampled from the matrix, each "
+                   f"searched over all 65535 seeds by encode_exhaustive (NumPy float64) in "
+                   f"{t:.2f} s; host cores available {len(os.sched_getaffinity(0))}"),
+    }
+
+
+def encode_main(args):
+    import torch
+
+    import prng_seeded_decode_amd as S
+    from workloads import gen_bf16_weights
+
+    C, P = (8, 3) if args.encode_bits == 4 else (12, 4)
+    if args.encode_shape:
+        rows, cols = (int(v) for v in args.encode_shape.split(","))
+    else:
+        rows, cols = 8192, -(-8192 // C) * C
+    bits = gen_bf16_weights(40, C, rows, cols, scale=0.02)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    W = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    enc = S.SeedLMEncoder(C, P, 16)
+    outs = S.seedlm_encode(enc, W, stream=stream)
+    for _ in range(args.warmup):
+        S.seedlm_encode(enc, W, *outs, stream=stream)
+    torch.cuda.synchronize()
+    evs = []
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        S.seedlm_encode(enc, W, *outs, stream=stream)
+        b.record(stream)
+        evs.append((a, b))
+    ev1.record(stream)
+    ev1.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    nblk = rows * cols // C
+    pairs = nblk * 65535
+    # Roofline of the search kernel: the algorithmic contraction is the pages'
+    # t* = pinv(U(s)) w for every block and seed, 2*C*P flops per (block, seed)
+    # pair, priced at the bf16 matrix-core peak (the kernel's operand type).
+    alg_flops = 2.0 * C * P * pairs
+    achieved = alg_flops / kern_s / 1e12
+    out = {
+        "metric": ENC_METRIC,
+        "value": rows * cols / (ms_per_step * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"seed search: {rows}x{cols} bf16 N(0, 0.02^2) weights (Llama-3-70B "
+                         f"q_proj shape) -> SeedLM C={C} P={P} K=16, all 65535 seeds per block"),
+            "blocks": nblk,
+            "block_seed_pairs": pairs,
+        },
+        "pairs_per_s": pairs / kern_s,
+        "kernel_ms_per_launch": round(kern_s * 1e3, 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_encode_baseline(bits, C, P, args.cpu_seconds)
+    enc.destroy()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.encode:
+        encode_main(args)
+        return
 
     import torch
 
