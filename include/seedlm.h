@@ -223,6 +223,25 @@ SEEDLM_API int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t r
                                 int64_t cols, int batch, void* stream);
 
 /*
+ * seedlm_gemm -- Y = X W^T for any number of activation rows (prefill), with W
+ * rebuilt from the handle's records inside the kernel and never stored in HBM
+ * (paperhub.cn rebuttal text before Eq. (1): weights are reconstructed on the
+ * fly from s and t and used to compute the activations).  Each 128 x 64 tile of
+ * W is decoded exactly once per 256 activation rows and contracted on the
+ * matrix cores (fp16 operands, fp32 accumulation).
+ *   X  device fp16 [ntok][cols], 16-byte aligned (row-major)
+ *   Y  device fp16 [ntok][rows] (round to nearest even); both caller-owned
+ *   ntok >= 1.  4-bit format (C = 8) with cols a multiple of 8, fp16 X and Y
+ *   only; other formats and dtypes return SEEDLM_E_UNSUPPORTED (for up to 16
+ *   rows seedlm_gemv covers them).
+ * Asynchronous on `stream`; no workspace, so calls may overlap.
+ * Errors: SEEDLM_E_INVALID (null, ntok < 1), SEEDLM_E_UNSUPPORTED (format,
+ * dtype, alignment), SEEDLM_E_DEVICE (launch failure).
+ */
+SEEDLM_API int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok,
+                           int x_dtype, int y_dtype, void* stream);
+
+/*
  * Seed search (compression).  SeedLM picks, for every block w of C weights, the
  * seed s, coefficients t and shared exponent e that make 2^e U(s) t closest to
  * w, searching all seeds (atlas.scime.ai "Approach"), with the pseudo-inverses

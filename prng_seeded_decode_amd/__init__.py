@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     seedlm_encode,
     seedlm_export,
     seedlm_fp16_gemv,
+    seedlm_gemm,
     seedlm_gemv,
     seedlm_gemv_many,
     seedlm_pack,

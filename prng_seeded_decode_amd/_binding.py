@@ -41,6 +41,7 @@ EXPORTED = (
     "seedlm_export",
     "seedlm_status_string",
     "seedlm_fp16_gemv",
+    "seedlm_gemm",
     "seedlm_encoder_create",
     "seedlm_encoder_destroy",
     "seedlm_encode",
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
     L.seedlm_status_string.argtypes = [i32]
     L.seedlm_status_string.restype = ctypes.c_char_p
     L.seedlm_fp16_gemv.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    L.seedlm_gemm.argtypes = [vp, vp, vp, i64, i32, i32, vp]
     L.seedlm_encoder_create.argtypes = [i32, i32, i32, ctypes.POINTER(vp)]
     L.seedlm_encoder_destroy.argtypes = [vp]
     L.seedlm_encode.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp]
@@ -264,6 +266,18 @@ def seedlm_decode(m: SeedLMMatrix, W_out, stream=None):
     _check(lib().seedlm_decode(m.handle, ctypes.c_void_p(W_out.data_ptr()), _stream_ptr(stream)),
            "seedlm_decode")
     return W_out
+
+
+def seedlm_gemm(m: SeedLMMatrix, X, Y, stream=None):
+    """Y[ntok][rows] = X[ntok][cols] W^T (fp16 device tensors), any ntok >= 1."""
+    if X.dim() != 2 or X.shape[1] != m.cols or Y.numel() != X.shape[0] * m.rows:
+        raise ValueError("X must be [ntok][cols] and Y hold ntok*rows elements")
+    if not (X.is_cuda and Y.is_cuda and X.is_contiguous() and Y.is_contiguous()):
+        raise ValueError("X and Y must be contiguous device tensors")
+    _check(lib().seedlm_gemm(m.handle, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(Y.data_ptr()),
+                             X.shape[0], _dtype_code(X), _dtype_code(Y), _stream_ptr(stream)),
+           "seedlm_gemm")
+    return Y
 
 
 def seedlm_export(m: SeedLMMatrix) -> bytes:

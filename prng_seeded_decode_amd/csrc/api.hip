@@ -162,6 +162,12 @@ int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_
   return launch_fp16_gemv(W, x, y, rows, cols, batch, static_cast<hipStream_t>(stream));
 }
 
+int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok, int x_dtype, int y_dtype,
+                void* stream) {
+  if (!h || !X || !Y || ntok < 1) return SEEDLM_E_INVALID;
+  return launch_gemm(h, X, Y, ntok, x_dtype, y_dtype, static_cast<hipStream_t>(stream));
+}
+
 int seedlm_encoder_create(int C, int P, int K, seedlm_encoder_handle* out) {
   if (!out) return SEEDLM_E_INVALID;
   *out = nullptr;

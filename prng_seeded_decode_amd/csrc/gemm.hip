@@ -1,0 +1,274 @@
+// Prefill-size decode-GEMM on the matrix cores: Y[t][r] = sum_c W[r][c] X[t][c]
+// for any number of token rows t, 4-bit format, fp16 X and Y, fp32 accumulation.
+//
+// SeedLM rebuilds the weights from each block's seed and coefficients where they
+// are used (paperhub.cn rebuttal text before Eq. (1); atlas.scime.ai
+// "Approach").  With many activation rows the rebuild is amortised over all of
+// them: a workgroup decodes a 128-row x 32-column tile of W exactly (the integer
+// block sum, entering as fp16(w * 2^10)) into LDS once, and its four waves
+// contract it against a 512-token slice of X with v_mfma_f32_32x32x16_f16.
+//
+// Tiles (one workgroup = 256 threads = 4 waves):
+//   rows    r0 .. r0+127 of W (output features), tokens t0 .. t0+T-1 of X,
+//           T = 512 (or 256 when 512-token tiles would leave over half the CUs
+//           idle);
+//   K step  32 columns = 4 blocks = one 16-byte group of a packed row;
+//   waves   2 x 2: wave (wr, wt) owns rows r0 + 64 wr .. +63 and tokens
+//           t0 + (T/2) wt .. +T/2-1, i.e. 2 x T/64 MFMA tiles of 32 x 32 (up to
+//           256 fp32 accumulators per lane), up to 32 MFMAs per K step.
+// Per K step each thread loads one 16-byte group (4 blocks) of one row into
+// registers and copies 8 x 16 bytes of X straight into LDS, two steps ahead;
+// the decode of step k+1 and the MFMAs of step k use different LDS buffers, so
+// the matrix cores run while the VALU decodes.
+//
+// MFMA operand layout (v_mfma_f32_32x32x16_f16, wave64): lane l supplies the 8
+// K values 8*(l/32) .. 8*(l/32)+7 of A row l%32 and of B column l%32; the
+// 32 x 32 fp32 result gives lane l column l%32, rows 8g + 4(l/32) + v in
+// register 4g + v (g, v = 0..3).  A = W rows, B = X tokens, so the result is
+// Y^T: lane l holds token l%32 and runs of four consecutive rows.
+#include <hip/hip_fp16.h>
+
+#include "lfsr_device.h"
+#include "mfma_decode.h"
+#include "seedlm_internal.h"
+
+namespace seedlm {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmThreads = 256;
+constexpr int kTileRows = 128;
+constexpr int kStepCols = 32;                       // 4 blocks of 8 columns, one 16-byte group
+constexpr int kSlices = kStepCols / 16;             // MFMAs of K = 16 per step
+constexpr int kXRow = kStepCols * 2;                // bytes per token row of an X tile
+constexpr int kXChunks = kXRow / 16;                // 16-byte chunks per token row
+constexpr int kLdsStride = kStepCols * 2 + 16;      // bytes per W row in LDS (padded)
+constexpr int kWBytes = kTileRows * kLdsStride;     // 10 KiB
+static_assert(kXChunks == 4, "X tile layout");
+
+// Token tile: 512 (256 per wave, 256 accumulator registers) for long inputs,
+// 256 when 512-token tiles would leave more than half the compute units idle.
+template <int TOKS>
+struct TokTile {
+  static constexpr int kTileToks = TOKS;
+  static constexpr int kNTiles = TOKS / 2 / 32;     // 32-token MFMA tiles per wave
+  static constexpr int kXBytes = TOKS * kXRow;      // swizzled, no padding
+  static constexpr int kXCopies = kXBytes / 1024 / 4;  // 1 KiB LDS copies per wave per step
+};
+
+struct GemmArgs {
+  const uint32_t* words;
+  const __half* x;
+  __half* y;
+  int rows, cols, Mp, nb, ntok;
+  uint32_t words_bytes, x_bytes;  // buffer sizes (< 2^31)
+};
+
+template <int TOKS>
+__global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs a) {
+  constexpr int kTileToks = TokTile<TOKS>::kTileToks, kNTiles = TokTile<TOKS>::kNTiles;
+  constexpr int kXBytes = TokTile<TOKS>::kXBytes, kXCopies = TokTile<TOKS>::kXCopies;
+  // Three buffers of each kind, as separate objects indexed at compile time, so
+  // that the compiler can tell that reads of one never wait for copies into
+  // another.
+  __shared__ uint32_t T0[256], T1[256];
+  __shared__ __attribute__((aligned(16))) uint8_t w0[kWBytes], w1[kWBytes], w2[kWBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t x0[kXBytes], x1[kXBytes], x2[kXBytes];
+  uint8_t* const wbuf[3] = {w0, w1, w2};
+  uint8_t* const xbuf[3] = {x0, x1, x2};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wt = wave & 1;
+  const int r0 = blockIdx.x * kTileRows, t0 = blockIdx.y * kTileToks;
+
+  for (int e = tid; e < 512; e += kGemmThreads) {
+    const uint32_t u = (uint32_t)e & 255u;
+    if (e < 256) T0[u] = ext_bits<uint32_t>(u);
+    else T1[u] = ext_bits<uint32_t>(u << 8);
+  }
+
+  // This thread's share of a K step: row dr = tid / 2 of the tile, whose step
+  // is one 16-byte group (4 blocks) of the packed row; the two threads of a
+  // row decode its words 2h and 2h+1 (h = tid & 1).  Buffer loads: an
+  // out-of-range offset reads zeros, so no load is conditional and steps past
+  // the end simply load zeros.
+  const int dr = tid >> 1, h = tid & 1;
+  const int row = r0 + dr;
+  const int nsteps = (a.nb + 3) / 4;
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.words, 0, (int)a.words_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, (int)a.x_bytes, 0x00020000);
+  auto load_w = [&](int ks) -> uint4 {
+    const int b0 = ks * 4;  // first block of the group
+    const int p = b0 / kPanelBlocks;
+    const int Wps = (int)panel_stored_width(p, a.nb);
+    const int q0 = b0 - p * kPanelBlocks;
+    // zero words decode to t = 0
+    const uint32_t off = (row < a.Mp && q0 < Wps)
+                             ? (uint32_t)((p * a.Mp * kPanelBlocks + row * Wps + q0) * 4)
+                             : 0x80000000u;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
+  // X of a step goes straight into LDS (buffer_load ... lds, 16 bytes per
+  // lane): the tile is 512 tokens x 64 bytes, and 16-byte chunk c of token t
+  // sits at t*64 + ((c ^ ((t >> 1) & 3)) * 16), so that the operand reads of
+  // eight consecutive tokens spread over all 32 banks twice.  Wave w, copy i
+  // fills LDS pieces P = (8w + i) * 64 + lane.
+  auto copy_x = [&](int ks, uint8_t* dst) {
+#pragma unroll
+    for (int i = 0; i < kXCopies; ++i) {
+      const int P = (kXCopies * wave + i) * 64 + lane;
+      const int tok = P >> 2, c = (P & 3) ^ ((tok >> 1) & 3);
+      const int col = ks * kStepCols + 8 * c;
+      const uint32_t off = (t0 + tok < a.ntok && col < a.cols)
+                               ? (uint32_t)((t0 + tok) * a.cols + col) * 2u
+                               : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, (__attribute__((address_space(3))) void*)(dst + (kXCopies * wave + i) * 1024), 16,
+          off, 0, 0, 0);
+    }
+  };
+  // Decode word p of a step's group into a W buffer: it holds block
+  // (p + row) & 3 of the step (the packed rows rotate their groups).
+  auto put_w1 = [&](uint8_t* dst, uint32_t w, uint32_t ext, int p) {
+    const int slot = (p + row) & 3;
+    *reinterpret_cast<half8*>(dst + dr * kLdsStride + slot * 16) = decode_c8_ext(w, ext);
+  };
+  auto mine = [&](uint4 wq, int j) -> uint32_t {  // word 2h + j of the group
+    return h ? (j ? wq.w : wq.z) : (j ? wq.y : wq.x);
+  };
+  auto put_w = [&](uint8_t* dst, uint4 wq) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) put_w1(dst, mine(wq, j), ext_c8(mine(wq, j), T0, T1), 2 * h + j);
+  };
+
+  f32x16 acc[2][kNTiles];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int n = 0; n < kNTiles; ++n)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[g][n][v] = 0.f;
+
+  const int arow = lane & 31, kq = lane >> 5, swz = (arow >> 1) & 3;
+  // MFMAs of one step: operands of slice s (16 columns) read one slice ahead;
+  // after slice s's MFMAs, this thread's word s of the next step's group is
+  // decoded, and the scheduler is told to alternate one MFMA with a few VALU
+  // instructions, so that the decode issues while the matrix cores work.
+  auto mma = [&](const uint8_t* wb, const uint8_t* xb, uint8_t* wnext, uint4 wq) {
+    uint32_t ext2[2];  // table lookups of both words, issued with slice 0's reads
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ext2[j] = ext_c8(mine(wq, j), T0, T1);
+    const uint8_t* wl = wb + (64 * wr + arow) * kLdsStride + kq * 16;
+    const uint8_t* xl = xb + (kTileToks / 2 * wt + arow) * kXRow;
+    half8 A[2][2], B[2][kNTiles];
+    auto rd = [&](int s) {
+      const int xo = ((2 * s + kq) ^ swz) * 16;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        A[s & 1][g] = *reinterpret_cast<const half8*>(wl + g * 32 * kLdsStride + s * 32);
+#pragma unroll
+      for (int n = 0; n < kNTiles; ++n)
+        B[s & 1][n] = *reinterpret_cast<const half8*>(xl + n * 32 * kXRow + xo);
+    };
+    rd(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) {
+      if (s + 1 < kSlices) rd(s + 1);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int n = 0; n < kNTiles; ++n)
+          acc[g][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s & 1][g], B[s & 1][n], acc[g][n],
+                                                             0, 0, 0);
+      put_w1(wnext, mine(wq, s), ext2[s], 2 * h + s);
+      // LDS reads first (the next slice's operands), then MFMAs alternating
+      // with VALU, then the decode's store.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 + kNTiles, 0);
+#pragma unroll
+      for (int m = 0; m < 2 * kNTiles; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then up to six VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);  // slices stay in order
+    }
+  };
+
+  // Prologue: steps 0 and 1 in flight, step 0 decoded.
+  uint4 wr3[3];
+  copy_x(0, xbuf[0]);
+  wr3[0] = load_w(0);
+  copy_x(1, xbuf[1]);
+  wr3[1] = load_w(1);
+  __syncthreads();  // T0/T1 ready (waits for all loads too)
+  put_w(wbuf[0], wr3[0]);
+  __syncthreads();
+
+  // Step k (buffers k % 3): start the copies of step k + 2, run the MFMAs of
+  // step k, decode step k + 1, then wait until only step k + 2's nine loads are
+  // in flight (vmcnt counts in issue order) and meet at the barrier.
+  auto step = [&](int k, int b) {
+    const int b1 = b == 2 ? 0 : b + 1, b2 = b == 0 ? 2 : b - 1;
+    copy_x(k + 2, xbuf[b2]);
+    wr3[b2] = load_w(k + 2);
+    mma(wbuf[b], xbuf[b], wbuf[b1], wr3[b1]);
+    __builtin_amdgcn_s_waitcnt(0x0079);  // vmcnt(9) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+  };
+  // Whole rounds of three steps (one loop exit, so the accumulators keep their
+  // registers); the at most two steps past the end multiply zeros.
+  for (int ks = 0; ks < nsteps; ks += 3) {
+    step(ks, 0);
+    step(ks + 1, 1);
+    step(ks + 2, 2);
+  }
+
+  // Y[t][r]: lane holds token 32n + l%32 and rows 32g + 8j + 4(l/32) + v.
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int n = 0; n < kNTiles; ++n) {
+      const int tok = t0 + kTileToks / 2 * wt + 32 * n + arow;
+      if (tok >= a.ntok) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rb = r0 + 64 * wr + 32 * g + 8 * j + 4 * kq;
+        __half* dst = a.y + (int64_t)tok * a.rows + rb;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (rb + v < a.rows) dst[v] = __float2half_rn(acc[g][n][4 * j + v] * 0x1p-10f);
+      }
+    }
+}
+
+}  // namespace
+
+int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
+                hipStream_t s) {
+  if (h->C != 8 || xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
+  if (h->cols % 8 != 0 || (uintptr_t)x % 16 != 0) return SEEDLM_E_UNSUPPORTED;
+  // 32-bit buffer offsets: the packed words and X must each stay below 2 GiB.
+  if (h->nwords * 4 >= (1LL << 31) || ntok * h->cols * 2 >= (1LL << 31))
+    return SEEDLM_E_UNSUPPORTED;
+  GemmArgs a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
+             static_cast<__half*>(y), (int)h->rows, (int)h->cols, (int)h->Mp, (int)h->nb,
+             (int)ntok, (uint32_t)(h->nwords * 4), (uint32_t)(ntok * h->cols * 2)};
+  const int64_t row_tiles = (h->rows + kTileRows - 1) / kTileRows;
+  // 512-token tiles once they fill at least half of the compute units (each
+  // does twice the MFMA work per decoded weight); 256-token tiles below that.
+  if (2 * row_tiles * ((ntok + 511) / 512) >= device_cu_count()) {
+    const dim3 grid((unsigned)row_tiles, (unsigned)((ntok + 511) / 512));
+    hipLaunchKernelGGL(gemm_c8_kernel<512>, grid, dim3(kGemmThreads), 0, s, a);
+  } else {
+    const dim3 grid((unsigned)row_tiles, (unsigned)((ntok + 255) / 256));
+    hipLaunchKernelGGL(gemm_c8_kernel<256>, grid, dim3(kGemmThreads), 0, s, a);
+  }
+  SEEDLM_HIP_CHECK(hipGetLastError());
+  return SEEDLM_OK;
+}
+
+}  // namespace seedlm

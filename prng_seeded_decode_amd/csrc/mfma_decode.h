@@ -1,0 +1,82 @@
+// Exact decode of packed blocks into fp16 operands for the matrix cores, shared
+// by the skinny decode-GEMM (gemv_mfma.hip) and the prefill GEMM (gemm.hip).
+//
+// A block is rebuilt exactly as an integer sum, I_i = sum_j t_j (z_{jC+i} - 2^15)
+// (SeedLM: paperdance.org abstract; atlas.scime.ai "Approach"), and enters the
+// MFMA as fp16(I_i * 2^(e-15) * 2^10) = fp16(w_i * 2^10): |w * 2^10| <= 32767,
+// so nothing overflows, and the products are scaled back by 2^-10 afterwards.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace seedlm {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+__device__ inline uint32_t ubfe(uint32_t v, uint32_t off, uint32_t w) {
+  return __builtin_amdgcn_ubfe(v, off, w);
+}
+
+// 2^(g - 20) for g in [0, 15]: the block scale 2^(e - 15) = 2^(g - 30) times
+// the fp16 range factor 2^10.
+__device__ inline float block_scale(uint32_t g) { return __uint_as_float((g + 107u) << 23); }
+
+// Stream bits 16..47 of a 4-bit block's seed from the two GF(2) byte tables.
+__device__ inline uint32_t ext_c8(uint32_t w, const uint32_t* T0, const uint32_t* T1) {
+  return T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];
+}
+
+// Eight fp16 weights (x 2^10) of a 4-bit block, in column order, given its
+// stream bits 16..47.
+__device__ inline half8 decode_c8_ext(uint32_t w, uint32_t ext) {
+  const uint32_t lo = (w & 0xFFFFu) | (ext << 16);             // stream bits 0..31
+  const int t0 = ((int)(w << 12)) >> 28;
+  const int t1 = ((int)(w << 8)) >> 28;
+  const int t2 = ((int)(w << 4)) >> 28;
+  const int base = -32768 * (t0 + t1 + t2);
+  const float sc = block_scale(w >> 28);
+  half8 out;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int z0 = (int)ubfe(lo, i, 16);       // z_i
+    const int z1 = (int)ubfe(lo, 8 + i, 16);   // z_{8+i}
+    const int z2 = (int)ubfe(ext, i, 16);      // z_{16+i}
+    const int I = t0 * z0 + t1 * z1 + t2 * z2 + base;
+    out[i] = (_Float16)((float)I * sc);
+  }
+  return out;
+}
+
+// Eight fp16 weights (x 2^10) of a 4-bit block, in column order.
+__device__ inline half8 decode_c8(uint32_t w, const uint32_t* T0, const uint32_t* T1) {
+  return decode_c8_ext(w, ext_c8(w, T0, T1));
+}
+
+// Twelve fp16 weights (x 2^10) of a 3-bit block, written to o[0..11].
+__device__ inline void decode_c12(uint32_t w, uint32_t g, const uint64_t* T0, const uint64_t* T1,
+                                  _Float16* o) {
+  const uint64_t ext = T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];  // stream bits 16..79
+  const uint32_t s0 = (w & 0xFFFFu) | ((uint32_t)ext << 16);    // bits 0..31
+  const uint32_t s1 = (uint32_t)ext;                            // bits 16..47
+  const uint32_t s2 = (uint32_t)(ext >> 16);                    // bits 32..63
+  int t[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t[j] = ((int)(w << (12 - 4 * j))) >> 28;
+  const int base = -32768 * (t[0] + t[1] + t[2] + t[3]);
+  const float sc = block_scale(g);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    int I = base;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = 12 * j + i;  // state index, window b[n .. n+15]
+      const int z = n <= 16 ? (int)ubfe(s0, n, 16)
+                            : (n <= 32 ? (int)ubfe(s1, n - 16, 16) : (int)ubfe(s2, n - 32, 16));
+      I += t[j] * z;
+    }
+    o[i] = (_Float16)((float)I * sc);
+  }
+}
+
+}  // namespace seedlm

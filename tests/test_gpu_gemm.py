@@ -1,0 +1,103 @@
+"""GPU prefill GEMM (seedlm_gemm, through the C ABI) against the CPU oracle.
+
+Y = X W^T with W from the oracle's float64 decode of the same records and X the
+same fp16 values.  Every token row of Y is a GEMV with fp16 output, so the bar
+is that of the fp16-output GEMV: normwise max|y - y_ref| / max|y_ref| <= 2e-3
+per token row.  Small shapes are checked on every output (ragged row, panel,
+block-group and token tails included, for both token tilings: 256 tokens per
+workgroup on small grids, 512 on large ones); the full 8192x8192, 2048-token
+shape on sampled rows and tokens, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+from oracle import seedlm_oracle as O
+from workloads import gen_records, gen_x
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _S():
+    import prng_seeded_decode_amd as S
+
+    return S
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run(cfg_id, rows, cols, ntok):
+    dev = _dev()
+    S = _S()
+    s, c, e = gen_records(cfg_id, 0, rows, cols, 8, 3)
+    m = S.seedlm_pack(s, c, e, rows, cols, 8, 3, 16)
+    X = gen_x(cfg_id, 0, ntok, cols, "f16")
+    Xd = torch.from_numpy(X).to(dev)
+    Y = torch.empty((ntok, rows), dtype=torch.float16, device=dev)
+    S.seedlm_gemm(m, Xd, Y)
+    torch.cuda.synchronize()
+    return (s, c, e), X, Y.cpu().numpy().astype(np.float64), m, Xd, Y
+
+
+def _rowwise_err(Yg, Yr):
+    return max(O.normwise_error(Yg[t], Yr[t]) for t in range(Yr.shape[0]))
+
+
+@pytest.mark.parametrize("rows,cols,ntok", [
+    (200, 296, 300),   # 37 blocks: a full and a 5-block panel; two token tiles, ragged
+    (100, 64, 1),      # one K step, one token, rows not a multiple of 8
+    (130, 520, 17),    # row tile tail of 2 rows
+    (1000, 2048, 513),
+    (4000, 256, 4100),  # enough tiles for the 512-token tiling, ragged rows and tokens
+])
+def test_gemm_matches_oracle_everywhere(rows, cols, ntok):
+    _say(f"gemm {rows}x{cols} ntok={ntok}")
+    (s, c, e), X, Yg, *_ = _run(61, rows, cols, ntok)
+    W = O.decode_rows(s, c, e, cols, 8, 3)
+    Yr = X.astype(np.float64) @ W.T
+    err = _rowwise_err(Yg, Yr)
+    _say(f"  max per-token normwise error {err:.2e}")
+    assert err <= TOL
+
+
+def test_gemm_full_shape_sampled():
+    """The benchmark's shape: Llama-3-70B q_proj (8192x8192), 2048 tokens."""
+    rows, cols, ntok = 8192, 8192, 2048
+    _say(f"gemm sampled {rows}x{cols} ntok={ntok}")
+    (s, c, e), X, Yg, *_ = _run(4, rows, cols, ntok)
+    rng = np.random.default_rng(3)
+    rs = np.concatenate([[0, rows - 1], rng.choice(rows, 30, replace=False)])
+    ts = np.concatenate([[0, ntok - 1], rng.choice(ntok, 14, replace=False)])
+    W = O.decode_rows(s[rs], c[rs], e[rs], cols, 8, 3)
+    Yr = X[ts].astype(np.float64) @ W.T  # (tokens, sampled rows)
+    err = _rowwise_err(Yg[np.ix_(ts, rs)], Yr)
+    _say(f"  sampled max per-token normwise error {err:.2e}")
+    assert err <= TOL
+
+
+def test_gemm_deterministic_and_rejects_unsupported():
+    dev = _dev()
+    S = _S()
+    _, _, Y1, m, Xd, Y = _run(62, 256, 512, 260)
+    S.seedlm_gemm(m, Xd, Y)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.cpu().numpy().astype(np.float64), Y1)
+    # fp32 activations, 3-bit format: not supported by this entry point
+    with pytest.raises(S.SeedLMError):
+        S.seedlm_gemm(m, Xd.float(), Y)
+    s, c, e = gen_records(62, 1, 64, 96, 12, 4)
+    m3 = S.seedlm_pack(s, c, e, 64, 96, 12, 4, 16)
+    X3 = torch.zeros((8, 96), dtype=torch.float16, device=dev)
+    Y3 = torch.empty((8, 64), dtype=torch.float16, device=dev)
+    with pytest.raises(S.SeedLMError):
+        S.seedlm_gemm(m3, X3, Y3)
