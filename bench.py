@@ -17,10 +17,16 @@ timed on a bounded sample of the same workload.
 
     python bench.py --encode [--encode-bits 4|3] [--steps K] [--warmup W]
 
-times the seed-search encoder instead: one step = one 8192x8192 bf16 matrix
-(Llama-3-70B q_proj shape) encoded by exhaustive search over all 65535 seeds,
-with its own JSON line (encoded weights/s, the search kernel's roofline, and
-the oracle's exhaustive encoder timed on sampled blocks).
+times the seed-search encoder instead, and
+
+    python bench.py --gemm [--tokens 2048]
+
+the prefill decode-GEMM (one step = the layer's 7 matrices at that many
+tokens, with torch's dense fp16 GEMM on the same shapes beside it).  In the
+encoder mode one step = one 8192x8192 bf16 matrix (Llama-3-70B q_proj shape)
+encoded by exhaustive search over all 65535 seeds.  Each mode prints its own
+JSON line with its dominant kernel's roofline and the oracle timed on a
+bounded sample.
 """
 from __future__ import annotations
 
@@ -80,6 +86,9 @@ def parse_args():
                    help="also time seedlm_decode (dense fp32 W) on the largest matrix")
     p.add_argument("--graph", type=int, default=0,
                    help="1: replay each step as a captured HIP graph (one per rotated copy)")
+    p.add_argument("--gemm", action="store_true",
+                   help="time the prefill decode-GEMM instead (one step = a layer at --tokens)")
+    p.add_argument("--tokens", type=int, default=2048)
     p.add_argument("--encode", action="store_true",
                    help="time the seed-search encoder instead (one step = one matrix encoded)")
     p.add_argument("--encode-bits", type=int, default=4, choices=(3, 4))
@@ -249,6 +258,153 @@ def encode_main(args):
     print(json.dumps(out), flush=True)
 
 
+GEMM_METRIC = "prefill tokens/s through one decoder layer (decode-GEMM on the matrix cores)"
+F16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def cpu_gemm_baseline(cfg, ntok, budget_s):
+    """Time the oracle (decode + float64 product) on sampled rows x sampled tokens."""
+    from oracle import seedlm_oracle as O
+    from workloads import gen_records, gen_x
+
+    rng = np.random.default_rng(777)
+    flops, t, rounds = 0.0, 0.0, 0
+    nr, nt = 4, 16
+    while t < budget_s:
+        for mid, mat in enumerate(cfg.matrices):
+            s, c, e = gen_records(cfg.config_id, mid, mat.rows, mat.cols, cfg.C, cfg.P)
+            pick = rng.choice(mat.rows, size=nr, replace=False)
+            X = gen_x(cfg.config_id, mid, nt, mat.cols, "f16").astype(np.float64)
+            t0 = time.perf_counter()
+            W = O.decode_rows(s[pick], c[pick], e[pick], mat.cols, cfg.C, cfg.P)
+            X @ W.T
+            t += time.perf_counter() - t0
+            flops += 2.0 * nr * nt * mat.cols
+        rounds += 1
+        nr = min(2 * nr, 64)
+    layer_flops_per_token = 2.0 * sum(m.rows * m.cols for m in cfg.matrices)
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {
+        "value": flops / t / layer_flops_per_token,
+        "unit": "tokens/s",
+        "cores": int(max(1, blas)),
+        "kind": "oracle",
+        "sample": (f"sampled rows x 16 tokens of the 7 layer matrices ({rounds} rounds, "
+                   f"{flops / 1e9:.1f} GFLOP) in {t:.2f} s: oracle decode (NumPy) + float64 "
+                   f"product, scaled to whole-layer tokens/s; host cores available "
+                   f"{len(os.sched_getaffinity(0))}"),
+    }
+
+
+def gemm_main(args):
+    import torch
+
+    import prng_seeded_decode_amd as S
+    from workloads import CONFIGS, gen_records
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    ntok = args.tokens
+    mats, xs, ys = [], [], []
+    for mid, mat in enumerate(cfg.matrices):
+        s, c, e = gen_records(cfg.config_id, mid, mat.rows, mat.cols, cfg.C, cfg.P)
+        mats.append(S.seedlm_pack(s, c, e, mat.rows, mat.cols, cfg.C, cfg.P, cfg.K))
+        g = torch.Generator(device=dev).manual_seed(1000 + mid)
+        xs.append(torch.randn((ntok, mat.cols), generator=g, device=dev).half())
+        ys.append(torch.empty((ntok, mat.rows), dtype=torch.float16, device=dev))
+
+    def step():
+        for m, x, y in zip(mats, xs, ys):
+            S.seedlm_gemm(m, x, y, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    ev1.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    # the dominant kernel: the 28672x8192 / 8192x28672 launches, timed alone
+    big = max(range(len(mats)), key=lambda i: cfg.matrices[i].rows * cfg.matrices[i].cols)
+    evs = []
+    for _ in range(args.steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        S.seedlm_gemm(mats[big], xs[big], ys[big], stream=stream)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    bm = cfg.matrices[big]
+    alg_flops = 2.0 * bm.rows * bm.cols * ntok
+    achieved = alg_flops / kern_s / 1e12
+    layer_weights = sum(m.rows * m.cols for m in cfg.matrices)
+    # same-chip dense fp16 baseline (torch.matmul -> hipBLASLt) on the same shapes
+    dense = None
+    if not args.no_fp16:
+        Ws = [torch.randn((m.rows, m.cols), device=dev).half() for m in cfg.matrices]
+        for _ in range(args.warmup):
+            for W, x, y in zip(Ws, xs, ys):
+                torch.matmul(x, W.t(), out=y)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            for W, x, y in zip(Ws, xs, ys):
+                torch.matmul(x, W.t(), out=y)
+        ev1.record(stream)
+        ev1.synchronize()
+        dms = ev0.elapsed_time(ev1) / args.steps
+        dense = {"ms_per_step": round(dms, 4),
+                 "TFLOPs": round(2.0 * layer_weights * ntok / (dms * 1e-3) / 1e12, 1),
+                 "seedlm_over_dense_time": round(ms / dms, 3)}
+        del Ws
+    out = {
+        "metric": GEMM_METRIC,
+        "value": ntok / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: q,k,v,o,gate,up,down decode-GEMM, {ntok} tokens, "
+                         f"SeedLM C={cfg.C} P={cfg.P} K={cfg.K}, fp16 X/Y"),
+            "tokens": ntok,
+        },
+        "TFLOPs": round(2.0 * layer_weights * ntok / (ms * 1e-3) / 1e12, 1),
+        "kernel_ms_per_launch": round(kern_s * 1e3, 3),
+        "kernel_shape": [bm.rows, bm.cols, ntok],
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": F16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / F16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+        "dense_fp16_baseline": dense,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_gemm_baseline(cfg, ntok, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -257,6 +413,9 @@ def main():
         sys.exit(2)
     if args.encode:
         encode_main(args)
+        return
+    if args.gemm:
+        gemm_main(args)
         return
 
     import torch

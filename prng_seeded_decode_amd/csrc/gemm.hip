@@ -65,6 +65,9 @@ struct GemmArgs {
   uint32_t words_bytes, x_bytes;  // buffer sizes (< 2^31)
 };
 
+// Chunk swizzle of the X tiles (see copy_x); depends on token bits 1..3 only.
+__device__ inline int xswz(int t) { return (((t >> 1) ^ (t >> 3)) & 1) | (((t >> 2) & 1) << 1); }
+
 template <int TOKS>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs a) {
   constexpr int kTileToks = TokTile<TOKS>::kTileToks, kNTiles = TokTile<TOKS>::kNTiles;
@@ -112,15 +115,18 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
     return make_uint4(v[0], v[1], v[2], v[3]);
   };
   // X of a step goes straight into LDS (buffer_load ... lds, 16 bytes per
-  // lane): the tile is 512 tokens x 64 bytes, and 16-byte chunk c of token t
-  // sits at t*64 + ((c ^ ((t >> 1) & 3)) * 16), so that the operand reads of
-  // eight consecutive tokens spread over all 32 banks twice.  Wave w, copy i
-  // fills LDS pieces P = (8w + i) * 64 + lane.
+  // lane): the tile is T tokens x 64 bytes, and 16-byte chunk c of token t sits
+  // at t*64 + ((c ^ f(t)) * 16) with f(t) = ((t>>1 ^ t>>3) & 1) | (t>>2 & 1) << 1.
+  // Tokens with equal t mod 4 (equal bank offset t*64 within 256 bytes) get
+  // distinct chunk positions over any 16 consecutive tokens, and tokens with
+  // equal t mod 2 over any 8, so operand reads are free of bank conflicts
+  // whether 16 lanes share 64 banks or 8 lanes share 32.  Wave w, copy i fills
+  // LDS pieces P = (kXCopies w + i) * 64 + lane.
   auto copy_x = [&](int ks, uint8_t* dst) {
 #pragma unroll
     for (int i = 0; i < kXCopies; ++i) {
       const int P = (kXCopies * wave + i) * 64 + lane;
-      const int tok = P >> 2, c = (P & 3) ^ ((tok >> 1) & 3);
+      const int tok = P >> 2, c = (P & 3) ^ xswz(tok);
       const int col = ks * kStepCols + 8 * c;
       const uint32_t off = (t0 + tok < a.ntok && col < a.cols)
                                ? (uint32_t)((t0 + tok) * a.cols + col) * 2u
@@ -152,7 +158,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[g][n][v] = 0.f;
 
-  const int arow = lane & 31, kq = lane >> 5, swz = (arow >> 1) & 3;
+  const int arow = lane & 31, kq = lane >> 5, swz = xswz(arow);
   // MFMAs of one step: operands of slice s (16 columns) read one slice ahead;
   // after slice s's MFMAs, this thread's word s of the next step's group is
   // decoded, and the scheduler is told to alternate one MFMA with a few VALU
