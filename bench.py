@@ -21,7 +21,8 @@ times the seed-search encoder instead, and
 
     python bench.py --gemm [--tokens 2048]
 
-the prefill decode-GEMM (one step = the layer's 7 matrices at that many
+(--sweep: the design-space sweep of the encoder over (C, P) on Gaussian
+weights) or the prefill decode-GEMM (one step = the layer's 7 matrices at that many
 tokens, with torch's dense fp16 GEMM on the same shapes beside it).  In the
 encoder mode one step = one 8192x8192 bf16 matrix (Llama-3-70B q_proj shape)
 encoded by exhaustive search over all 65535 seeds.  Each mode prints its own
@@ -89,6 +90,8 @@ def parse_args():
     p.add_argument("--gemm", action="store_true",
                    help="time the prefill decode-GEMM instead (one step = a layer at --tokens)")
     p.add_argument("--tokens", type=int, default=2048)
+    p.add_argument("--sweep", action="store_true",
+                   help="design-space sweep: reconstruction error of Gaussian blocks per (C, P)")
     p.add_argument("--encode", action="store_true",
                    help="time the seed-search encoder instead (one step = one matrix encoded)")
     p.add_argument("--encode-bits", type=int, default=4, choices=(3, 4))
@@ -405,6 +408,91 @@ def gemm_main(args):
     print(json.dumps(out), flush=True)
 
 
+SWEEP_FORMATS = [(6, 1), (7, 2), (8, 3), (9, 4), (10, 5), (11, 6), (12, 7),   # 4 bits/weight
+                 (8, 1), (9, 1), (10, 2), (11, 3), (12, 4),                    # <= 3 bits/weight
+                 (8, 2), (8, 4)]                                               # C = 8 curve
+
+
+def sweep_main(args):
+    """Relative reconstruction MSE of N(0,1) blocks (bf16) for each supported
+    (C, P) at K = 16, with every block searched over all 65535 seeds on the GPU
+    and sampled blocks re-scored and re-searched by the oracle."""
+    import torch
+
+    import prng_seeded_decode_amd as S
+    from oracle import seedlm_oracle as O
+    from workloads import bf16_to_float64, gen_bf16_weights
+
+    dev = torch.device("cuda:0")
+    rows, nb = 2048, 256
+    table, total_pairs, total_s = [], 0, 0.0
+    rng = np.random.default_rng(99)
+    t_oracle = 0.0
+    for C, P in SWEEP_FORMATS:
+        bits = gen_bf16_weights(50, 100 * C + P, rows, nb * C)
+        W = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        enc = S.SeedLMEncoder(C, P, 16)
+        outs = S.seedlm_encode(enc, W)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        S.seedlm_encode(enc, W, *outs)
+        b.record()
+        b.synchronize()
+        t = a.elapsed_time(b) * 1e-3
+        sd, cf, ex, err = (o.cpu().numpy() for o in outs)
+        Wb = bf16_to_float64(bits).reshape(-1, C)
+        wn = np.sum(Wb ** 2, axis=1)
+        err = err.reshape(-1).astype(np.float64)
+        rel = float(err.sum() / wn.sum())
+        # oracle: re-score the GPU's records in float64 and re-search sampled blocks
+        pick = rng.choice(Wb.shape[0], size=4, replace=False)
+        t0 = time.perf_counter()
+        dec = O.decode_rows(sd.view(np.uint16).reshape(-1, 1)[pick], cf.reshape(-1, 1, P)[pick],
+                            ex.reshape(-1, 1)[pick], C, C, P)
+        e64 = np.sum((Wb[pick] - dec) ** 2, axis=1)
+        _, _, _, _, eo = O.encode_exhaustive(Wb[pick], C, P)
+        t_oracle += time.perf_counter() - t0
+        nblk = Wb.shape[0]
+        table.append({
+            "C": C, "P": P, "K": 16,
+            "bits_per_weight": round((16 + 4 * P + 4) / C, 4),
+            "rel_mse": round(rel, 6),
+            "snr_db": round(-10 * np.log10(rel), 3),
+            "gpu_ms": round(t * 1e3, 3),
+            "pairs_per_s": nblk * 65535 / t,
+            "oracle_max_score_gap_over_wn": float(np.max(np.abs(e64 - eo.reshape(-1)) / wn[pick])),
+        })
+        total_pairs += nblk * 65535
+        total_s += t
+        enc.destroy()
+        del W, outs
+    best4 = min((r for r in table if r["bits_per_weight"] <= 4.0), key=lambda r: r["rel_mse"])
+    best3 = min((r for r in table if r["bits_per_weight"] <= 3.0), key=lambda r: r["rel_mse"])
+    out = {
+        "metric": "seed-search design-space sweep: block-seed pairs/s over all formats",
+        "value": total_pairs / total_s,
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": 1,
+        "warmup": 1,
+        "ms_per_step": round(total_s * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"{len(table)} (C, P) formats at K = 16, each on {rows}x{nb}C "
+                                f"N(0,1) bf16 weights, every block against all 65535 seeds")},
+        "best_4bit": {"C": best4["C"], "P": best4["P"], "rel_mse": best4["rel_mse"]},
+        "best_3bit": {"C": best3["C"], "P": best3["P"], "rel_mse": best3["rel_mse"]},
+        "sweep": table,
+        "oracle_seconds": round(t_oracle, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -416,6 +504,9 @@ def main():
         return
     if args.gemm:
         gemm_main(args)
+        return
+    if args.sweep:
+        sweep_main(args)
         return
 
     import torch

@@ -262,6 +262,10 @@ typedef struct seedlm_encoder* seedlm_encoder_handle;
  * format (C, P, K) the search reads: the thin QR factors of U(s) for all 65535
  * seeds (12 MiB for (8,3,16), 23 MiB for (12,4,16)).  Synchronous.  The
  * handle owns the table.
+ * Formats: K = 16 with (C, P) one of the packed formats (8,3) and (12,4), or,
+ * for studying the design space (records only; seedlm_pack takes the packed
+ * formats alone), (6,1) (7,2) (9,4) (10,5) (11,6) (12,7) (8,1) (9,1) (10,2)
+ * (11,3) (8,2) (8,4).
  * Errors: SEEDLM_E_INVALID (null out), SEEDLM_E_UNSUPPORTED ((C,P,K) not
  * supported), SEEDLM_E_NOMEM, SEEDLM_E_DEVICE.
  */
@@ -273,7 +277,7 @@ SEEDLM_API int seedlm_encoder_destroy(seedlm_encoder_handle e);
 /*
  * seedlm_encode -- exhaustive seed search for every block of a dense matrix.
  *   W      device bf16 [rows][cols] (raw bf16 bit patterns, row-major), cols a
- *          multiple of C; 16-byte aligned for C = 8, 8-byte aligned for C = 12;
+ *          multiple of C; 16-byte aligned for C = 8, 2-byte aligned otherwise;
  *          finite values
  *   seeds  device uint16 [rows][nb], nb = cols / C     (out)
  *   coeffs device int8   [rows][nb][P]                 (out)

@@ -63,40 +63,42 @@ constexpr int kSeedTiles = 4096;  // 16-seed tiles: seeds 1 .. 65536 (65536 is p
 constexpr int kEncThreads = 512;  // 8 waves
 constexpr int kLastSeed = 65535;
 
-template <int C>
-struct EncFmt;
-template <>
-struct EncFmt<8> {
-  static constexpr int P = 3;
-  static constexpr int kQBytes = 768;   // one column j of a tile: 48 lanes x 16 B
-  static constexpr int kTiles = 8;      // block tiles per wave
-  static constexpr int kStage = 8;      // seed tiles per LDS stage
-};
-template <>
-struct EncFmt<12> {
-  static constexpr int P = 4;
-  static constexpr int kQBytes = 1152;  // 48 lanes x 16 B (hi, mid) + 48 x 8 B (lo)
-  static constexpr int kTiles = 4;
-  static constexpr int kStage = 4;
+// A format (C weights per block, P coefficients per block, K = 16).  The two
+// packed formats, (8,3) and (12,4), keep their tuned work split; the others
+// serve the design-space study (records only).
+template <int C, int P>
+struct EncFmt {
+  static_assert(C >= 2 && C <= 12 && P >= 1 && P <= 7 && P < C, "supported formats");
+  // Q's three bf16 parts along K: all in one 16x16x32 MFMA when 3C <= 32, else
+  // hi and mid there and lo in a 16x16x16 MFMA.
+  static constexpr bool kSplit = 3 * C > 32;
+  static constexpr int kSlots = kSplit ? 2 * C : 3 * C;  // used K slots of the 32-wide operand
+  static constexpr int kGroups = (kSlots + 7) / 8;       // lane groups (8 slots each) holding them
+  // Table columns store 48 lanes when lane group 3 is unused (lanes 48..63
+  // then re-read lanes 0..15: finite values against zero weights), else 64.
+  static constexpr int kALanes = kGroups == 4 ? 64 : 48;
+  static constexpr int kQBytes = kALanes * 16 + (kSplit ? 48 * 8 : 0);  // one column j of a tile
+  static constexpr bool kPacked83 = C == 8 && P == 3;
+  static constexpr int kTiles = kPacked83 ? 8 : (P >= 6 ? 2 : 4);  // block tiles per wave
+  static constexpr int kStage = kPacked83 ? 8 : 4;   // seed tiles per LDS stage
 };
 
-template <int C>
+template <int C, int P>
 struct EncLayout {
-  static constexpr int P = EncFmt<C>::P;
+  using F = EncFmt<C, P>;
   static constexpr int NR = P * (P + 1) / 2;           // entries of an upper triangle
   static constexpr int kRBytes = 2 * NR * 4;           // R^-1 then R, fp32, per seed
-  static constexpr int kTileBytes = P * EncFmt<C>::kQBytes + 16 * kRBytes;
-  static constexpr int kStageBytes = EncFmt<C>::kStage * kTileBytes;
-  static constexpr int kStages = kSeedTiles / EncFmt<C>::kStage;
+  static constexpr int kROff = P * F::kQBytes;         // R data of the 16 seeds of a tile
+  static constexpr int kTileBytes = (kROff + 16 * kRBytes + 255) / 256 * 256;
+  static constexpr int kStageBytes = F::kStage * kTileBytes;
+  static constexpr int kStages = kSeedTiles / F::kStage;
   static constexpr int kChunks = kStageBytes / 16;     // 16-byte pieces per stage
   static constexpr int kChunksPerThread = (kChunks + kEncThreads - 1) / kEncThreads;
-  static constexpr int kBlocksPerWave = 16 * EncFmt<C>::kTiles;
+  static constexpr int kBlocksPerWave = 16 * F::kTiles;
   static constexpr int kBlocksPerGroup = (kEncThreads / 64) * kBlocksPerWave;
+  static_assert(kChunks % 64 == 0, "a stage splits into whole 1 KiB wave pieces");
+  static_assert(kSeedTiles % F::kStage == 0 && kStages % 2 == 0, "stages alternate");
 };
-static_assert(EncLayout<8>::kStageBytes % 16 == 0 && EncLayout<12>::kStageBytes % 16 == 0, "");
-static_assert(kSeedTiles % EncFmt<8>::kStage == 0 && kSeedTiles % EncFmt<12>::kStage == 0, "");
-static_assert(EncLayout<8>::kChunks % 64 == 0 && EncLayout<12>::kChunks % 64 == 0,
-              "a stage splits into whole 1 KiB wave pieces");
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ inline uint16_t bf16_bits(float f) {
@@ -112,10 +114,11 @@ __device__ inline double bf16_value(uint16_t h) {
 // out as three bf16 parts each in the MFMA operand layout, R^-1 and R as fp32
 // upper triangles (row-major).  Seed 65536 (padding of the last tile) gets
 // zeros; the search never accepts it.
-template <int C>
+template <int C, int P>
 __global__ void __launch_bounds__(256) seed_table_kernel(uint8_t* __restrict__ table) {
-  using L = EncLayout<C>;
-  constexpr int P = L::P, NR = L::NR;
+  using L = EncLayout<C, P>;
+  using F = EncFmt<C, P>;
+  constexpr int NR = L::NR;
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
   if (m >= 16 * kSeedTiles) return;
   const int seed = m + 1, tile = m >> 4, n = m & 15;
@@ -165,24 +168,27 @@ __global__ void __launch_bounds__(256) seed_table_kernel(uint8_t* __restrict__ t
       const double r2 = r1 - bf16_value(part[1][i]);
       part[2][i] = bf16_bits((float)r2);
     }
-    uint8_t* col = tb + j * EncFmt<C>::kQBytes;
-    // K slot k (0..23) of the 32-wide operand holds part k / C, entry k % C:
-    // hi, mid, lo for C = 8; hi, mid for C = 12 (lo goes to the 16-wide one).
-    for (int qg = 0; qg < 3; ++qg) {
+    uint8_t* col = tb + j * F::kQBytes;
+    // K slot k (< kSlots) of the 32-wide operand holds part k / C, entry k % C
+    // (hi, mid and, unless split, lo); the rest is zero.
+    for (int qg = 0; qg < F::kALanes / 16; ++qg) {
       uint16_t* dst = reinterpret_cast<uint16_t*>(col + (16 * qg + n) * 16);
       for (int u = 0; u < 8; ++u) {
         const int k = 8 * qg + u;
-        dst[u] = part[k / C][k % C];
+        dst[u] = k < F::kSlots ? part[k / C][k % C] : (uint16_t)0;
       }
     }
-    if (C == 12) {  // lo part: K slots 0..11 of the 16-wide operand
+    if (F::kSplit) {  // lo part: K slots 0..C-1 of the 16-wide operand
       for (int qg = 0; qg < 3; ++qg) {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(col + 768 + (16 * qg + n) * 8);
-        for (int u = 0; u < 4; ++u) dst[u] = part[2][4 * qg + u];
+        uint16_t* dst = reinterpret_cast<uint16_t*>(col + F::kALanes * 16 + (16 * qg + n) * 8);
+        for (int u = 0; u < 4; ++u) {
+          const int k = 4 * qg + u;
+          dst[u] = k < C ? part[2][k] : (uint16_t)0;
+        }
       }
     }
   }
-  float* rd = reinterpret_cast<float*>(tb + P * EncFmt<C>::kQBytes + n * L::kRBytes);
+  float* rd = reinterpret_cast<float*>(tb + L::kROff + n * L::kRBytes);
   int o = 0;
   for (int i = 0; i < P; ++i)
     for (int j = i; j < P; ++j, ++o) {
@@ -202,76 +208,74 @@ struct EncArgs {
 };
 
 // The block's weights as the B operand(s) of the MFMAs, and its squared norm.
-template <int C>
-struct BlockOps;
-template <>
-struct BlockOps<8> {
-  bf16x8 b1;
-  __device__ void load(const uint16_t* W, int64_t b, bool valid, int qg, float& wn) {
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (valid) v = *reinterpret_cast<const uint4*>(W + b * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = __uint_as_float(((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
-      s = fmaf(x, x, s);
-    }
-    wn = s;
-    if (qg == 3) v = make_uint4(0u, 0u, 0u, 0u);  // K slots 24..31 are unused
-    b1 = __builtin_bit_cast(bf16x8, v);
-  }
-};
-template <>
-struct BlockOps<12> {
+// 32-wide operand: K slot k < kSlots holds w[k % C] (against Q's parts), lane
+// group qg holding slots 8qg .. 8qg+7; 16-wide operand (split formats): slot
+// k < C holds w[k] (against lo), lane group qg holding slots 4qg .. 4qg+3.
+template <int C, int P>
+struct BlockOps {
+  using F = EncFmt<C, P>;
   bf16x8 b1;
   s16x4 b2;
   __device__ void load(const uint16_t* W, int64_t b, bool valid, int qg, float& wn) {
-    uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
-    if (valid) {
-      const uint2* p = reinterpret_cast<const uint2*>(W + b * 12);
+    uint16_t x[C];
+    if constexpr (C == 8) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (valid) v = *reinterpret_cast<const uint4*>(W + b * 8);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int h = 0; h < 3; ++h) {
-        const uint2 v = p[h];
-        w[2 * h] = v.x;
-        w[2 * h + 1] = v.y;
-      }
+      for (int i = 0; i < 8; ++i) x[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < C; ++i) x[i] = valid ? W[b * C + i] : (uint16_t)0;
     }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      const float x = __uint_as_float(((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
-      s = fmaf(x, x, s);
+    for (int i = 0; i < C; ++i) {
+      const float xf = __uint_as_float((uint32_t)x[i] << 16);
+      s = fmaf(xf, xf, s);
     }
     wn = s;
-    // 32-wide operand: slots 0..11 and 12..23 both hold w0..w11 (against hi
-    // and mid); lane group qg holds slots 8qg .. 8qg+7, i.e. words
-    // (4qg .. 4qg+3) mod 6.  16-wide operand: slots 0..11 hold w0..w11 (lo).
-    uint4 v1 = make_uint4(0u, 0u, 0u, 0u);
-    uint2 v2 = make_uint2(0u, 0u);
-    if (qg < 3) {
-      v1 = make_uint4(w[(4 * qg) % 6], w[(4 * qg + 1) % 6], w[(4 * qg + 2) % 6],
-                      w[(4 * qg + 3) % 6]);
-      v2 = make_uint2(w[2 * qg], w[2 * qg + 1]);
+    auto pick = [&](int k, int nslots, int per, int u) -> uint32_t {
+      // slot per*qg + u of this lane, the lane group known only at run time
+      uint32_t val = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kk = per * q + u;
+        const uint32_t c = kk < nslots ? (uint32_t)x[kk % C] : 0u;
+        if (qg == q) val = c;
+      }
+      (void)k;
+      return val;
+    };
+    uint32_t w1[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      w1[h] = pick(0, F::kSlots, 8, 2 * h) | (pick(0, F::kSlots, 8, 2 * h + 1) << 16);
+    b1 = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+    if constexpr (F::kSplit) {
+      const uint32_t lo0 = pick(0, C, 4, 0) | (pick(0, C, 4, 1) << 16);
+      const uint32_t lo1 = pick(0, C, 4, 2) | (pick(0, C, 4, 3) << 16);
+      b2 = __builtin_bit_cast(s16x4, make_uint2(lo0, lo1));
+    } else {
+      b2 = s16x4{0, 0, 0, 0};
     }
-    b1 = __builtin_bit_cast(bf16x8, v1);
-    b2 = __builtin_bit_cast(s16x4, v2);
   }
 };
 
+// t_j as nibbles at bits 4j (P <= 7), e + 15 at bits 28..31.
 template <int P>
 __device__ inline uint32_t pack_record(const float (&t)[P], int e) {
-  uint32_t r = (uint32_t)(e + 15) << 16;
+  uint32_t r = (uint32_t)(e + 15) << 28;
 #pragma unroll
   for (int j = 0; j < P; ++j) r |= ((uint32_t)(int)t[j] & 15u) << (4 * j);
   return r;
 }
 
-template <int C>
+template <int C, int P>
 __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a) {
-  using L = EncLayout<C>;
-  using F = EncFmt<C>;
-  constexpr int P = L::P, NR = L::NR, NT = F::kTiles, G = F::kStage;
+  using L = EncLayout<C, P>;
+  using F = EncFmt<C, P>;
+  constexpr int NR = L::NR, NT = F::kTiles, G = F::kStage;
   // Two stage buffers as separate objects, so that the compiler can tell that
   // reads of one never wait for the copy into the other.
   __shared__ __attribute__((aligned(16))) uint8_t stage0[L::kStageBytes];
@@ -280,7 +284,7 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
   const int n = lane & 15, qg = lane >> 4;
   const int64_t block0 = ((int64_t)blockIdx.x * (kEncThreads / 64) + wave) * L::kBlocksPerWave;
 
-  BlockOps<C> ops[NT];
+  BlockOps<C, P> ops[NT];
   float nwn[NT], best[NT];
   int bseed[NT];
   uint32_t brec[NT];
@@ -311,7 +315,8 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
     }
   };
 
-  const int alane = lane % 48;  // lanes 48..63 re-read lanes 0..15 (their B is zero)
+  // lanes 48..63 re-read lanes 0..15 when lane group 3 is unused (their B is zero)
+  const int alane = F::kALanes == 64 ? lane : lane % 48;
   auto run_stage = [&](const uint8_t* sb, int st) {
     for (int s = 0; s < G; ++s) {
       const uint8_t* tb = sb + s * L::kTileBytes;
@@ -320,8 +325,9 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
 #pragma unroll
       for (int j = 0; j < P; ++j) {
         A1[j] = *reinterpret_cast<const bf16x8*>(tb + j * F::kQBytes + alane * 16);
-        if constexpr (C == 12)
-          A2[j] = *reinterpret_cast<const s16x4*>(tb + j * F::kQBytes + 768 + alane * 8);
+        if constexpr (F::kSplit)
+          A2[j] = *reinterpret_cast<const s16x4*>(tb + j * F::kQBytes + F::kALanes * 16 +
+                                                  (lane % 48) * 8);
       }
       const int seed_base = (st * G + s) * 16 + 1 + 4 * qg;  // seed of this lane's row v = 0
       // c = Q^T w for this seed tile against block tile T.
@@ -330,7 +336,7 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
         for (int j = 0; j < P; ++j) {
           const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[j], ops[T].b1, zero, 0, 0, 0);
-          if constexpr (C == 12) {
+          if constexpr (F::kSplit) {
             // The lo part gets an accumulator of its own: chaining this MFMA onto
             // the 16x16x32 result (a different opcode) read a stale accumulator
             // when the two were issued back to back, and the compiler does not
@@ -482,7 +488,7 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
       const int64_t b = block0 + 16 * T + n;
       if (b >= a.nblk) continue;
       a.seeds[b] = (uint16_t)bseed[T];
-      a.exps[b] = (int8_t)((int)(brec[T] >> 16) - 15);
+      a.exps[b] = (int8_t)((int)(brec[T] >> 28) - 15);
 #pragma unroll
       for (int j = 0; j < P; ++j) {
         const int nib = (int)((brec[T] >> (4 * j)) & 15u);
@@ -495,33 +501,58 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
 
 }  // namespace
 
-size_t encoder_table_bytes(int C) {
-  return (size_t)kSeedTiles * (C == 8 ? EncLayout<8>::kTileBytes : EncLayout<12>::kTileBytes);
+// Formats the encoder is built for: the two packed ones, then the rest of the
+// 4-bit frontier ((20 + 4P) / C = 4 bits: (6,1) .. (12,7)), the 3-bit frontier
+// (largest P with (20 + 4P) / C <= 3) and two more points at C = 8.
+#define SEEDLM_ENC_FORMATS(X) \
+  X(8, 3) X(12, 4)            \
+  X(6, 1) X(7, 2) X(9, 4) X(10, 5) X(11, 6) X(12, 7) \
+  X(8, 1) X(9, 1) X(10, 2) X(11, 3) \
+  X(8, 2) X(8, 4)
+
+bool encoder_format_supported(int C, int P) {
+#define X(c, p) if (C == c && P == p) return true;
+  SEEDLM_ENC_FORMATS(X)
+#undef X
+  return false;
 }
 
-int launch_seed_table(int C, void* table, hipStream_t s) {
+size_t encoder_table_bytes(int C, int P) {
+#define X(c, p) if (C == c && P == p) return (size_t)kSeedTiles * EncLayout<c, p>::kTileBytes;
+  SEEDLM_ENC_FORMATS(X)
+#undef X
+  return 0;
+}
+
+int launch_seed_table(int C, int P, void* table, hipStream_t s) {
   const dim3 grid(16 * kSeedTiles / 256), block(256);
-  if (C == 8)
-    hipLaunchKernelGGL(seed_table_kernel<8>, grid, block, 0, s, static_cast<uint8_t*>(table));
-  else
-    hipLaunchKernelGGL(seed_table_kernel<12>, grid, block, 0, s, static_cast<uint8_t*>(table));
-  SEEDLM_HIP_CHECK(hipGetLastError());
-  return SEEDLM_OK;
+#define X(c, p)                                                                              \
+  if (C == c && P == p) {                                                                    \
+    hipLaunchKernelGGL((seed_table_kernel<c, p>), grid, block, 0, s, static_cast<uint8_t*>(table)); \
+    SEEDLM_HIP_CHECK(hipGetLastError());                                                     \
+    return SEEDLM_OK;                                                                        \
+  }
+  SEEDLM_ENC_FORMATS(X)
+#undef X
+  return SEEDLM_E_UNSUPPORTED;
 }
 
-int launch_encode(int C, const void* table, const void* W, int64_t nblk, uint16_t* seeds,
+int launch_encode(int C, int P, const void* table, const void* W, int64_t nblk, uint16_t* seeds,
                   int8_t* coeffs, int8_t* exps, float* err, hipStream_t s) {
-  const int64_t per = C == 8 ? EncLayout<8>::kBlocksPerGroup : EncLayout<12>::kBlocksPerGroup;
-  const int64_t groups = (nblk + per - 1) / per;
-  if (groups > 0x7FFFFFFF) return SEEDLM_E_UNSUPPORTED;
   EncArgs a{static_cast<const uint8_t*>(table), static_cast<const uint16_t*>(W), nblk, seeds,
             coeffs, exps, err};
-  if (C == 8)
-    hipLaunchKernelGGL(encode_kernel<8>, dim3((unsigned)groups), dim3(kEncThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(encode_kernel<12>, dim3((unsigned)groups), dim3(kEncThreads), 0, s, a);
-  SEEDLM_HIP_CHECK(hipGetLastError());
-  return SEEDLM_OK;
+#define X(c, p)                                                                              \
+  if (C == c && P == p) {                                                                    \
+    const int64_t per = EncLayout<c, p>::kBlocksPerGroup;                                    \
+    const int64_t groups = (nblk + per - 1) / per;                                           \
+    if (groups > 0x7FFFFFFF) return SEEDLM_E_UNSUPPORTED;                                    \
+    hipLaunchKernelGGL((encode_kernel<c, p>), dim3((unsigned)groups), dim3(kEncThreads), 0, s, a); \
+    SEEDLM_HIP_CHECK(hipGetLastError());                                                     \
+    return SEEDLM_OK;                                                                        \
+  }
+  SEEDLM_ENC_FORMATS(X)
+#undef X
+  return SEEDLM_E_UNSUPPORTED;
 }
 
 }  // namespace seedlm

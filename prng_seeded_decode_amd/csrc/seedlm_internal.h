@@ -99,9 +99,10 @@ int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_
                      int batch, hipStream_t s);
 int build_ext_table(seedlm_matrix* h);
 // Seed search: per-seed QR table (bytes for format C) and the search itself.
-size_t encoder_table_bytes(int C);
-int launch_seed_table(int C, void* table, hipStream_t s);
-int launch_encode(int C, const void* table, const void* W, int64_t nblk, uint16_t* seeds,
+bool encoder_format_supported(int C, int P);
+size_t encoder_table_bytes(int C, int P);
+int launch_seed_table(int C, int P, void* table, hipStream_t s);
+int launch_encode(int C, int P, const void* table, const void* W, int64_t nblk, uint16_t* seeds,
                   int8_t* coeffs, int8_t* exps, float* err, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).

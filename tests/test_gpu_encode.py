@@ -191,3 +191,17 @@ def test_encode_is_deterministic_and_rejects_bad_arguments():
                            None) == S.E_INVALID
     assert L.seedlm_encode(enc.handle, ctypes.c_void_p(W.data_ptr()), 0, 64, p, p, p, p,
                            None) == S.E_INVALID
+
+
+# The other formats the encoder is built for (records only: the design-space
+# study).  Each is checked on every block of a small Gaussian matrix.
+DESIGN_FORMATS = [(6, 1), (7, 2), (9, 4), (10, 5), (11, 6), (12, 7), (8, 1), (9, 1), (10, 2),
+                  (11, 3), (8, 2), (8, 4)]
+
+
+@pytest.mark.parametrize("C,P", DESIGN_FORMATS)
+def test_encode_design_space_formats_match_oracle(C, P):
+    _say(f"encode format C={C} P={P}")
+    bits = gen_bf16_weights(9, 10 * C + P, 2, 12 * C)  # 24 blocks
+    s, c, e, err = _run(bits, C, P)
+    _check_blocks(_blocks(bf16_to_float64(bits), C), s, c, e, err, C, P, min_seed_match=0.8)
