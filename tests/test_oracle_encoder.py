@@ -76,3 +76,45 @@ def test_planted_blocks_reencode_exactly():
     assert np.array_equal(rec, W)
     assert np.array_equal(O.decode_rows(s2, c2, e2, 8 * nblk, 8, 3), W)
     assert np.array_equal(s2, seeds)
+
+
+@pytest.mark.parametrize("Q", [3, 4])
+def test_quantize_exponent_rule_by_thresholds(Q):
+    """Q-bit integers in [-2^(Q-1), 2^(Q-1)-1]; round-half-even keeps t*/2^e in
+    range exactly when t*/2^e < 2^(Q-1) - 1/2 and t*/2^e >= -(2^(Q-1) + 1/2), so
+    the chosen e is the smallest one in [-15, 0] meeting both (else 0)."""
+    rng = np.random.default_rng(Q)
+    ts = rng.standard_normal((2000, 3)) * np.exp2(rng.uniform(-16, 4, (2000, 1)))
+    t, e = O.quantize(ts, Q)
+    half = 1 << (Q - 1)
+    for v, tv, ev in zip(ts, t, e):
+        want = 0
+        for cand in range(-15, 1):
+            y = v / 2.0 ** cand
+            if y.max() < half - 0.5 and y.min() >= -(half + 0.5):
+                want = cand
+                break
+        assert ev == want
+        assert tv.min() >= -half and tv.max() <= half - 1
+    # boundary cases, Q = 3: 3.5 rounds to 4 (does not fit at e = 0: clamp to 3);
+    # -4.5 rounds to -4 (fits at e = 0)
+    if Q == 3:
+        t1, e1 = O.quantize(np.array([[3.5, 0.0, 0.0]]), 3)
+        assert e1[0] == 0 and t1[0, 0] == 3
+        t2, e2 = O.quantize(np.array([[-4.5, 0.0, 0.0]]), 3)
+        assert e2[0] == 0 and t2[0, 0] == -4
+
+
+def test_planted_blocks_reencode_exactly_12bit_seeds():
+    """The K = 12 search (4095 seeds) returns planted records exactly."""
+    rng = np.random.default_rng(12)
+    n, C, P, K = 6, 7, 3, 12
+    seeds = rng.integers(1, 1 << K, (1, n))
+    coeffs = rng.integers(-8, 8, (1, n, P)).astype(np.int8)
+    coeffs[0, :, 0] = 7
+    exps = rng.integers(-12, -5, (1, n)).astype(np.int8)
+    W = O.decode_rows(seeds, coeffs, exps, n * C, C, P, K)
+    s2, c2, e2, rec, err = O.encode_exhaustive(W, C, P, K=K)
+    assert np.all(err == 0)
+    assert np.array_equal(s2.reshape(-1), seeds.reshape(-1))
+    assert np.array_equal(O.decode_rows(s2, c2, e2, n * C, C, P, K), W)

@@ -1,6 +1,7 @@
 """Pins for the oracle's LFSR: invariants that a primitive degree-16 polynomial
 fixes, and states worked out by hand (tests/golden/block_seed1.txt)."""
 import numpy as np
+import pytest
 
 from oracle import seedlm_oracle as O
 
@@ -71,3 +72,30 @@ def test_gf2_linearity_of_the_state_sequence():
         b = O.lfsr_states(s2, 48)
         c = O.lfsr_states(s1 ^ s2, 48)
         assert [x ^ y for x, y in zip(a, b)] == c
+
+
+# Other seed widths of the design-space study: each LFSR must be maximal-length.
+@pytest.mark.parametrize("K", [12, 20])
+def test_other_seed_widths_have_full_period(K):
+    n = (1 << K) - 1
+    seen = np.zeros(1 << K, dtype=bool)
+    z, total = 1, 0
+    for _ in range(n):
+        assert not seen[z]
+        seen[z] = True
+        total += z - (1 << (K - 1))
+        z = O.lfsr_step(z, K)
+    assert z == 1                      # back at the seed after exactly 2^K - 1 steps
+    assert seen[1:].all() and not seen[0]
+    assert total == 0                  # the values (z - 2^(K-1)) sum to zero over a period
+
+
+def test_other_seed_widths_first_states_by_hand():
+    # K = 12, feedback bits 0,1,4,6 of z enter at bit 11.  From z = 1: bit 0 is
+    # set, so f = 1 and z1 = 0 | 1 << 11 = 2048; then 2048 has none of bits
+    # 0,1,4,6 set: z2 = 1024, z3 = 512, z4 = 256, z5 = 128.
+    assert O.lfsr_states(1, 6, 12) == [1, 2048, 1024, 512, 256, 128]
+    # K = 20, feedback bits 0,3 enter at bit 19: z1 = 2^19, then halving.
+    assert O.lfsr_states(1, 6, 20) == [1, 524288, 262144, 131072, 65536, 32768]
+    with pytest.raises(ValueError):
+        O.lfsr_states(4096, 2, 12)
