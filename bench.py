@@ -408,14 +408,19 @@ def gemm_main(args):
     print(json.dumps(out), flush=True)
 
 
-SWEEP_FORMATS = [(6, 1), (7, 2), (8, 3), (9, 4), (10, 5), (11, 6), (12, 7),   # 4 bits/weight
-                 (8, 1), (9, 1), (10, 2), (11, 3), (12, 4),                    # <= 3 bits/weight
-                 (8, 2), (8, 4)]                                               # C = 8 curve
+# (C, P, K, Q): block length, latent dimension, seed width, coefficient width
+SWEEP_FORMATS = [(c, p, 16, 4) for c, p in
+                 [(6, 1), (7, 2), (8, 3), (9, 4), (10, 5), (11, 6), (12, 7),   # 4 bits/weight
+                  (8, 1), (9, 1), (10, 2), (11, 3), (12, 4),                    # <= 3 bits/weight
+                  (8, 2), (8, 4)]]                                              # C = 8 curve
+SWEEP_FORMATS += [(7, 3, 12, 4), (9, 3, 20, 4),      # 4 bits/weight, other seed widths
+                  (8, 2, 12, 4), (12, 3, 20, 4),     # 3 bits/weight, other seed widths
+                  (8, 4, 16, 3), (10, 3, 16, 3)]     # 3-bit coefficients
 
 
 def sweep_main(args):
     """Relative reconstruction MSE of N(0,1) blocks (bf16) for each supported
-    (C, P) at K = 16, with every block searched over all 65535 seeds on the GPU
+    (C, P, K, Q), with every block searched over all 2^K - 1 seeds on the GPU
     and sampled blocks re-scored and re-searched by the oracle."""
     import torch
 
@@ -428,10 +433,12 @@ def sweep_main(args):
     table, total_pairs, total_s = [], 0, 0.0
     rng = np.random.default_rng(99)
     t_oracle = 0.0
-    for C, P in SWEEP_FORMATS:
+    for C, P, K, Q in SWEEP_FORMATS:
+        print(f"# sweep C={C} P={P} K={K} Q={Q}", file=sys.stderr, flush=True)
+        nseed = (1 << K) - 1
         bits = gen_bf16_weights(50, 100 * C + P, rows, nb * C)
         W = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
-        enc = S.SeedLMEncoder(C, P, 16)
+        enc = S.SeedLMEncoder(C, P, K, Q)
         outs = S.seedlm_encode(enc, W)
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
@@ -449,22 +456,23 @@ def sweep_main(args):
         # oracle: re-score the GPU's records in float64 and re-search sampled blocks
         pick = rng.choice(Wb.shape[0], size=4, replace=False)
         t0 = time.perf_counter()
-        dec = O.decode_rows(sd.view(np.uint16).reshape(-1, 1)[pick], cf.reshape(-1, 1, P)[pick],
-                            ex.reshape(-1, 1)[pick], C, C, P)
+        sd = sd.view(np.uint16 if K <= 16 else np.uint32)
+        dec = O.decode_rows(sd.reshape(-1, 1)[pick], cf.reshape(-1, 1, P)[pick],
+                            ex.reshape(-1, 1)[pick], C, C, P, K=K)
         e64 = np.sum((Wb[pick] - dec) ** 2, axis=1)
-        _, _, _, _, eo = O.encode_exhaustive(Wb[pick], C, P)
+        _, _, _, _, eo = O.encode_exhaustive(Wb[pick], C, P, K=K, Q=Q)
         t_oracle += time.perf_counter() - t0
         nblk = Wb.shape[0]
         table.append({
-            "C": C, "P": P, "K": 16,
-            "bits_per_weight": round((16 + 4 * P + 4) / C, 4),
+            "C": C, "P": P, "K": K, "Q": Q,
+            "bits_per_weight": round((K + Q * P + 4) / C, 4),
             "rel_mse": round(rel, 6),
             "snr_db": round(-10 * np.log10(rel), 3),
             "gpu_ms": round(t * 1e3, 3),
-            "pairs_per_s": nblk * 65535 / t,
+            "pairs_per_s": nblk * nseed / t,
             "oracle_max_score_gap_over_wn": float(np.max(np.abs(e64 - eo.reshape(-1)) / wn[pick])),
         })
-        total_pairs += nblk * 65535
+        total_pairs += nblk * nseed
         total_s += t
         enc.destroy()
         del W, outs
@@ -483,10 +491,10 @@ def sweep_main(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": (f"{len(table)} (C, P) formats at K = 16, each on {rows}x{nb}C "
-                                f"N(0,1) bf16 weights, every block against all 65535 seeds")},
-        "best_4bit": {"C": best4["C"], "P": best4["P"], "rel_mse": best4["rel_mse"]},
-        "best_3bit": {"C": best3["C"], "P": best3["P"], "rel_mse": best3["rel_mse"]},
+        "config": {"workload": (f"{len(table)} (C, P, K, Q) formats, each on {rows}x{nb}C "
+                                f"N(0,1) bf16 weights, every block against all 2^K - 1 seeds")},
+        "best_4bit": {k: best4[k] for k in ("C", "P", "K", "Q", "rel_mse")},
+        "best_3bit": {k: best3[k] for k in ("C", "P", "K", "Q", "rel_mse")},
         "sweep": table,
         "oracle_seconds": round(t_oracle, 2),
     }

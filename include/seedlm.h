@@ -259,17 +259,22 @@ typedef struct seedlm_encoder* seedlm_encoder_handle;
 
 /*
  * seedlm_encoder_create -- build, on the current device, the per-seed table of
- * format (C, P, K) the search reads: the thin QR factors of U(s) for all 65535
- * seeds (12 MiB for (8,3,16), 23 MiB for (12,4,16)).  Synchronous.  The
- * handle owns the table.
- * Formats: K = 16 with (C, P) one of the packed formats (8,3) and (12,4), or,
- * for studying the design space (records only; seedlm_pack takes the packed
- * formats alone), (6,1) (7,2) (9,4) (10,5) (11,6) (12,7) (8,1) (9,1) (10,2)
- * (11,3) (8,2) (8,4).
- * Errors: SEEDLM_E_INVALID (null out), SEEDLM_E_UNSUPPORTED ((C,P,K) not
+ * format (C, P, K, Q) the search reads: the thin QR factors of U(s) for all
+ * 2^K - 1 seeds (12 MiB for (8,3,16,4), 23 MiB for (12,4,16,4)).  Q is the
+ * coefficient width (t in [-2^(Q-1), 2^(Q-1) - 1]).  Synchronous.  The handle
+ * owns the table.
+ * Formats: the packed formats (8,3,16,4) and (12,4,16,4), and for studying
+ * the design space (records only; seedlm_pack takes the packed formats alone,
+ * and the seed width and coefficient width are the pages' knobs below 3 bits:
+ * paperhub.cn, answer on 1.5-2.5 bits per weight): with K = 16, Q = 4 the
+ * (C, P) pairs (6,1) (7,2) (9,4) (10,5) (11,6) (12,7) (8,1) (9,1) (10,2) (11,3)
+ * (8,2) (8,4); with other seed widths (7,3,12,4) (8,2,12,4) (9,3,20,4)
+ * (12,3,20,4); with 3-bit coefficients (8,4,16,3) (10,3,16,3).  The K-bit
+ * LFSRs: x^12+x^6+x^4+x+1, x^16+x^5+x^3+x^2+1 (the format's), x^20+x^3+1.
+ * Errors: SEEDLM_E_INVALID (null out), SEEDLM_E_UNSUPPORTED (format not
  * supported), SEEDLM_E_NOMEM, SEEDLM_E_DEVICE.
  */
-SEEDLM_API int seedlm_encoder_create(int C, int P, int K, seedlm_encoder_handle* out);
+SEEDLM_API int seedlm_encoder_create(int C, int P, int K, int Q, seedlm_encoder_handle* out);
 
 /* seedlm_encoder_destroy -- free the encoder's table; NULL is a no-op. */
 SEEDLM_API int seedlm_encoder_destroy(seedlm_encoder_handle e);
@@ -279,7 +284,7 @@ SEEDLM_API int seedlm_encoder_destroy(seedlm_encoder_handle e);
  *   W      device bf16 [rows][cols] (raw bf16 bit patterns, row-major), cols a
  *          multiple of C; 16-byte aligned for C = 8, 2-byte aligned otherwise;
  *          finite values
- *   seeds  device uint16 [rows][nb], nb = cols / C     (out)
+ *   seeds  device uint16 [rows][nb] (uint32 for K > 16), nb = cols / C (out)
  *   coeffs device int8   [rows][nb][P]                 (out)
  *   exps   device int8   [rows][nb]                    (out)
  *   err    device float  [rows][nb], the fp32 score of the chosen record, or
@@ -291,7 +296,7 @@ SEEDLM_API int seedlm_encoder_destroy(seedlm_encoder_handle e);
  * SEEDLM_E_UNSUPPORTED (grid too large), SEEDLM_E_DEVICE (launch failure).
  */
 SEEDLM_API int seedlm_encode(seedlm_encoder_handle e, const void* W, int64_t rows,
-                             int64_t cols, uint16_t* seeds, int8_t* coeffs, int8_t* exps,
+                             int64_t cols, void* seeds, int8_t* coeffs, int8_t* exps,
                              float* err, void* stream);
 
 #ifdef __cplusplus

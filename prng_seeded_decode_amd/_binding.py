@@ -96,7 +96,7 @@ def lib() -> ctypes.CDLL:
     L.seedlm_status_string.restype = ctypes.c_char_p
     L.seedlm_fp16_gemv.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     L.seedlm_gemm.argtypes = [vp, vp, vp, i64, i32, i32, vp]
-    L.seedlm_encoder_create.argtypes = [i32, i32, i32, ctypes.POINTER(vp)]
+    L.seedlm_encoder_create.argtypes = [i32, i32, i32, i32, ctypes.POINTER(vp)]
     L.seedlm_encoder_destroy.argtypes = [vp]
     L.seedlm_encode.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp]
     for name in EXPORTED:
@@ -303,11 +303,11 @@ def seedlm_fp16_gemv(W, x, y, batch=None, stream=None):
 class SeedLMEncoder:
     """A seed-search encoder for one format on the current device (owns its table)."""
 
-    def __init__(self, C=8, P=3, K=16):
+    def __init__(self, C=8, P=3, K=16, Q=4):
         h = ctypes.c_void_p()
-        _check(lib().seedlm_encoder_create(C, P, K, ctypes.byref(h)), "seedlm_encoder_create")
+        _check(lib().seedlm_encoder_create(C, P, K, Q, ctypes.byref(h)), "seedlm_encoder_create")
         self._h = h
-        self.C, self.P, self.K = C, P, K
+        self.C, self.P, self.K, self.Q = C, P, K, Q
 
     @property
     def handle(self):
@@ -332,7 +332,7 @@ def seedlm_encode(enc: SeedLMEncoder, W, seeds=None, coeffs=None, exps=None, err
     """Seed search for every block of W (bf16 device tensor [rows][cols]).
 
     Returns device tensors seeds [rows][nb] (torch.int16 holding the uint16 bit
-    patterns), coeffs [rows][nb][P] int8, exps [rows][nb] int8 and err [rows][nb]
+    patterns; int32 for K > 16), coeffs [rows][nb][P] int8, exps [rows][nb] int8 and err [rows][nb]
     float32 (the fp32 score of each chosen record).  Preallocated outputs may be
     passed in."""
     import torch
@@ -345,7 +345,8 @@ def seedlm_encode(enc: SeedLMEncoder, W, seeds=None, coeffs=None, exps=None, err
     nb = cols // enc.C
     dev = W.device
     if seeds is None:
-        seeds = torch.empty((rows, nb), dtype=torch.int16, device=dev)
+        seeds = torch.empty((rows, nb), dtype=torch.int16 if enc.K <= 16 else torch.int32,
+                            device=dev)
     if coeffs is None:
         coeffs = torch.empty((rows, nb, enc.P), dtype=torch.int8, device=dev)
     if exps is None:

@@ -168,23 +168,24 @@ int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok, int x_dty
   return launch_gemm(h, X, Y, ntok, x_dtype, y_dtype, static_cast<hipStream_t>(stream));
 }
 
-int seedlm_encoder_create(int C, int P, int K, seedlm_encoder_handle* out) {
+int seedlm_encoder_create(int C, int P, int K, int Q, seedlm_encoder_handle* out) {
   if (!out) return SEEDLM_E_INVALID;
   *out = nullptr;
-  if (K != 16 || !encoder_format_supported(C, P)) return SEEDLM_E_UNSUPPORTED;
+  if (!encoder_format_supported(C, P, K, Q)) return SEEDLM_E_UNSUPPORTED;
   seedlm_encoder* e = new (std::nothrow) seedlm_encoder;
   if (!e) return SEEDLM_E_NOMEM;
   e->C = C;
   e->P = P;
   e->K = K;
-  e->table_bytes = encoder_table_bytes(C, P);
+  e->Q = Q;
+  e->table_bytes = encoder_table_bytes(C, P, K, Q);
   int rc = SEEDLM_OK;
   if (hipGetDevice(&e->device) != hipSuccess) rc = SEEDLM_E_DEVICE;
   if (rc == SEEDLM_OK && hipMalloc(&e->d_table, e->table_bytes) != hipSuccess) {
     e->d_table = nullptr;
     rc = SEEDLM_E_NOMEM;
   }
-  if (rc == SEEDLM_OK) rc = launch_seed_table(C, P, e->d_table, nullptr);
+  if (rc == SEEDLM_OK) rc = launch_seed_table(C, P, K, Q, e->d_table, nullptr);
   if (rc == SEEDLM_OK && hipStreamSynchronize(nullptr) != hipSuccess) rc = SEEDLM_E_DEVICE;
   if (rc != SEEDLM_OK) {
     if (e->d_table) (void)hipFree(e->d_table);
@@ -203,8 +204,8 @@ int seedlm_encoder_destroy(seedlm_encoder_handle e) {
   return rc;
 }
 
-int seedlm_encode(seedlm_encoder_handle e, const void* W, int64_t rows, int64_t cols,
-                  uint16_t* seeds, int8_t* coeffs, int8_t* exps, float* err, void* stream) {
+int seedlm_encode(seedlm_encoder_handle e, const void* W, int64_t rows, int64_t cols, void* seeds,
+                  int8_t* coeffs, int8_t* exps, float* err, void* stream) {
   if (!e || !W || !seeds || !coeffs || !exps) return SEEDLM_E_INVALID;
   if (rows <= 0 || cols <= 0 || cols % e->C != 0) return SEEDLM_E_INVALID;
   const uintptr_t align = e->C == 8 ? 16 : 2;
@@ -213,8 +214,8 @@ int seedlm_encode(seedlm_encoder_handle e, const void* W, int64_t rows, int64_t 
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return SEEDLM_E_DEVICE;
   if (dev != e->device) return SEEDLM_E_INVALID;
-  return launch_encode(e->C, e->P, e->d_table, W, rows * (cols / e->C), seeds, coeffs, exps, err,
-                       static_cast<hipStream_t>(stream));
+  return launch_encode(e->C, e->P, e->K, e->Q, e->d_table, W, rows * (cols / e->C), seeds, coeffs,
+                       exps, err, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -59,16 +59,31 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSeedTiles = 4096;  // 16-seed tiles: seeds 1 .. 65536 (65536 is padding)
 constexpr int kEncThreads = 512;  // 8 waves
-constexpr int kLastSeed = 65535;
 
-// A format (C weights per block, P coefficients per block, K = 16).  The two
-// packed formats, (8,3) and (12,4), keep their tuned work split; the others
-// serve the design-space study (records only).
-template <int C, int P>
+// The K-bit LFSR: z' = (z >> 1) | (f << (K - 1)), f the XOR of a few bits of z
+// (characteristic polynomials x^12 + x^6 + x^4 + x + 1, x^16 + x^5 + x^3 +
+// x^2 + 1 -- the format's -- and x^20 + x^3 + 1, all primitive).
+template <int K>
+__device__ inline uint32_t lfsr_next(uint32_t z) {
+  static_assert(K == 12 || K == 16 || K == 20, "seed widths");
+  uint32_t f;
+  if constexpr (K == 12) f = z ^ (z >> 1) ^ (z >> 4) ^ (z >> 6);
+  else if constexpr (K == 16) f = z ^ (z >> 2) ^ (z >> 3) ^ (z >> 5);
+  else f = z ^ (z >> 3);
+  return (z >> 1) | ((f & 1u) << (K - 1));
+}
+
+// A format: C weights per block, P coefficients per block, K-bit seeds, Q-bit
+// coefficients.  The two packed formats, (8,3) and (12,4) with K = 16 and
+// Q = 4, keep their tuned work split; the others serve the design-space study
+// (records only).
+template <int C, int P, int K, int Q>
 struct EncFmt {
   static_assert(C >= 2 && C <= 12 && P >= 1 && P <= 7 && P < C, "supported formats");
+  static_assert(Q == 3 || Q == 4, "coefficients fit a nibble");
+  static constexpr int kSeedTiles = (1 << K) / 16;  // seeds 1 .. 2^K (2^K is padding)
+  static constexpr int kLastSeed = (1 << K) - 1;
   // Q's three bf16 parts along K: all in one 16x16x32 MFMA when 3C <= 32, else
   // hi and mid there and lo in a 16x16x16 MFMA.
   static constexpr bool kSplit = 3 * C > 32;
@@ -78,26 +93,26 @@ struct EncFmt {
   // then re-read lanes 0..15: finite values against zero weights), else 64.
   static constexpr int kALanes = kGroups == 4 ? 64 : 48;
   static constexpr int kQBytes = kALanes * 16 + (kSplit ? 48 * 8 : 0);  // one column j of a tile
-  static constexpr bool kPacked83 = C == 8 && P == 3;
+  static constexpr bool kPacked83 = C == 8 && P == 3 && K == 16 && Q == 4;
   static constexpr int kTiles = kPacked83 ? 8 : (P >= 6 ? 2 : 4);  // block tiles per wave
   static constexpr int kStage = kPacked83 ? 8 : 4;   // seed tiles per LDS stage
 };
 
-template <int C, int P>
+template <int C, int P, int K, int Q>
 struct EncLayout {
-  using F = EncFmt<C, P>;
+  using F = EncFmt<C, P, K, Q>;
   static constexpr int NR = P * (P + 1) / 2;           // entries of an upper triangle
   static constexpr int kRBytes = 2 * NR * 4;           // R^-1 then R, fp32, per seed
   static constexpr int kROff = P * F::kQBytes;         // R data of the 16 seeds of a tile
   static constexpr int kTileBytes = (kROff + 16 * kRBytes + 255) / 256 * 256;
   static constexpr int kStageBytes = F::kStage * kTileBytes;
-  static constexpr int kStages = kSeedTiles / F::kStage;
+  static constexpr int kStages = F::kSeedTiles / F::kStage;
   static constexpr int kChunks = kStageBytes / 16;     // 16-byte pieces per stage
   static constexpr int kChunksPerThread = (kChunks + kEncThreads - 1) / kEncThreads;
   static constexpr int kBlocksPerWave = 16 * F::kTiles;
   static constexpr int kBlocksPerGroup = (kEncThreads / 64) * kBlocksPerWave;
   static_assert(kChunks % 64 == 0, "a stage splits into whole 1 KiB wave pieces");
-  static_assert(kSeedTiles % F::kStage == 0 && kStages % 2 == 0, "stages alternate");
+  static_assert(F::kSeedTiles % F::kStage == 0 && kStages % 2 == 0, "stages alternate");
 };
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
@@ -112,38 +127,37 @@ __device__ inline double bf16_value(uint16_t h) {
 // One thread per seed: U(s) from the LFSR, thin QR by Gram-Schmidt with one
 // re-orthogonalisation pass (fp64), R^-1 by back substitution; Q's columns go
 // out as three bf16 parts each in the MFMA operand layout, R^-1 and R as fp32
-// upper triangles (row-major).  Seed 65536 (padding of the last tile) gets
+// upper triangles (row-major).  Seed 2^K (padding of the last tile) gets
 // zeros; the search never accepts it.
-template <int C, int P>
+template <int C, int P, int K, int Q>
 __global__ void __launch_bounds__(256) seed_table_kernel(uint8_t* __restrict__ table) {
-  using L = EncLayout<C, P>;
-  using F = EncFmt<C, P>;
+  using L = EncLayout<C, P, K, Q>;
+  using F = EncFmt<C, P, K, Q>;
   constexpr int NR = L::NR;
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  if (m >= 16 * kSeedTiles) return;
+  if (m >= 16 * F::kSeedTiles) return;
   const int seed = m + 1, tile = m >> 4, n = m & 15;
-  double Q[C][P], R[P][P], Ri[P][P];
+  double Qm[C][P], R[P][P], Ri[P][P];
   for (int i = 0; i < P; ++i)
     for (int j = 0; j < P; ++j) R[i][j] = Ri[i][j] = 0.0;
-  if (seed <= kLastSeed) {
+  if (seed <= F::kLastSeed) {
     uint32_t z = (uint32_t)seed;
     for (int k = 0; k < C * P; ++k) {  // column-major fill: U[i][j] = v_{jC+i}
-      Q[k % C][k / C] = ((double)z - 32768.0) / 32768.0;
-      const uint32_t f = (z ^ (z >> 2) ^ (z >> 3) ^ (z >> 5)) & 1u;
-      z = (z >> 1) | (f << 15);
+      Qm[k % C][k / C] = ((double)z - (double)(1 << (K - 1))) / (double)(1 << (K - 1));
+      z = lfsr_next<K>(z);
     }
     for (int j = 0; j < P; ++j) {
       for (int pass = 0; pass < 2; ++pass)
         for (int k = 0; k < j; ++k) {
           double r = 0.0;
-          for (int i = 0; i < C; ++i) r += Q[i][k] * Q[i][j];
-          for (int i = 0; i < C; ++i) Q[i][j] -= r * Q[i][k];
+          for (int i = 0; i < C; ++i) r += Qm[i][k] * Qm[i][j];
+          for (int i = 0; i < C; ++i) Qm[i][j] -= r * Qm[i][k];
           R[k][j] += r;
         }
       double nn = 0.0;
-      for (int i = 0; i < C; ++i) nn += Q[i][j] * Q[i][j];
+      for (int i = 0; i < C; ++i) nn += Qm[i][j] * Qm[i][j];
       R[j][j] = sqrt(nn);
-      for (int i = 0; i < C; ++i) Q[i][j] /= R[j][j];
+      for (int i = 0; i < C; ++i) Qm[i][j] /= R[j][j];
     }
     for (int i = P - 1; i >= 0; --i) {
       Ri[i][i] = 1.0 / R[i][i];
@@ -155,13 +169,13 @@ __global__ void __launch_bounds__(256) seed_table_kernel(uint8_t* __restrict__ t
     }
   } else {
     for (int i = 0; i < C; ++i)
-      for (int j = 0; j < P; ++j) Q[i][j] = 0.0;
+      for (int j = 0; j < P; ++j) Qm[i][j] = 0.0;
   }
   uint8_t* tb = table + (size_t)tile * L::kTileBytes;
   for (int j = 0; j < P; ++j) {
     uint16_t part[3][C];
     for (int i = 0; i < C; ++i) {
-      const double q = Q[i][j];
+      const double q = Qm[i][j];
       part[0][i] = bf16_bits((float)q);
       const double r1 = q - bf16_value(part[0][i]);
       part[1][i] = bf16_bits((float)r1);
@@ -201,7 +215,7 @@ struct EncArgs {
   const uint8_t* table;
   const uint16_t* W;  // bf16 bits, nblk blocks of C
   int64_t nblk;
-  uint16_t* seeds;
+  void* seeds;  // uint16 for K <= 16, uint32 above
   int8_t* coeffs;
   int8_t* exps;
   float* err;  // may be null
@@ -211,9 +225,9 @@ struct EncArgs {
 // 32-wide operand: K slot k < kSlots holds w[k % C] (against Q's parts), lane
 // group qg holding slots 8qg .. 8qg+7; 16-wide operand (split formats): slot
 // k < C holds w[k] (against lo), lane group qg holding slots 4qg .. 4qg+3.
-template <int C, int P>
+template <int C, int P, int K, int Q>
 struct BlockOps {
-  using F = EncFmt<C, P>;
+  using F = EncFmt<C, P, K, Q>;
   bf16x8 b1;
   s16x4 b2;
   __device__ void load(const uint16_t* W, int64_t b, bool valid, int qg, float& wn) {
@@ -271,10 +285,10 @@ __device__ inline uint32_t pack_record(const float (&t)[P], int e) {
   return r;
 }
 
-template <int C, int P>
+template <int C, int P, int K, int Q>
 __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a) {
-  using L = EncLayout<C, P>;
-  using F = EncFmt<C, P>;
+  using L = EncLayout<C, P, K, Q>;
+  using F = EncFmt<C, P, K, Q>;
   constexpr int NR = L::NR, NT = F::kTiles, G = F::kStage;
   // Two stage buffers as separate objects, so that the compiler can tell that
   // reads of one never wait for the copy into the other.
@@ -284,7 +298,7 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
   const int n = lane & 15, qg = lane >> 4;
   const int64_t block0 = ((int64_t)blockIdx.x * (kEncThreads / 64) + wave) * L::kBlocksPerWave;
 
-  BlockOps<C, P> ops[NT];
+  BlockOps<C, P, K, Q> ops[NT];
   float nwn[NT], best[NT];
   int bseed[NT];
   uint32_t brec[NT];
@@ -410,26 +424,28 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
             hi = fmaxf(hi, ts[j]);
             lo = fminf(lo, ts[j]);
           }
-          // Smallest e with hi * 2^-e < 7.5 and lo * 2^-e >= -8.5 (the range that
-          // rounds half-to-even into [-8, 7]): with hi = f 2^k, f in [0.5, 1),
-          // e = k - 3 when f < 15/16, else k - 2; with -lo = g 2^k, e = k - 4 when
-          // g <= 17/32, else k - 3.
+          // Smallest e with hi * 2^-e < H - 1/2 and lo * 2^-e >= -(H + 1/2),
+          // H = 2^(Q-1) (the range that rounds half-to-even into [-H, H-1]):
+          // with hi = f 2^k, f in [0.5, 1), e = k - (Q-1) when f < 1 - 2^-Q,
+          // else k - Q + 2; with -lo = g 2^k, e = k - Q when g <= 1/2 + 2^-(Q+1),
+          // else k - Q + 1.  (Q = 4: 15/16 and 17/32.)
+          constexpr float kH = (float)(1 << (Q - 1));
           int e_hi = -64, e_lo = -64;
           if (hi > 0.f) {
             int k;
             const float f = frexpf(hi, &k);
-            e_hi = k - 3 + (f >= 0.9375f ? 1 : 0);
+            e_hi = k - (Q - 1) + (f >= 1.f - 0.5f / kH ? 1 : 0);
           }
           if (lo < 0.f) {
             int k;
             const float g = frexpf(-lo, &k);
-            e_lo = k - 4 + (g > 0.53125f ? 1 : 0);
+            e_lo = k - Q + (g > 0.5f + 0.25f / kH ? 1 : 0);
           }
           const int e = min(max(max(e_hi, e_lo), -15), 0);
           float t[P], tau[P];
 #pragma unroll
           for (int j = 0; j < P; ++j) {
-            t[j] = fminf(fmaxf(rintf(ldexpf(ts[j], -e)), -8.f), 7.f);
+            t[j] = fminf(fmaxf(rintf(ldexpf(ts[j], -e)), -kH), kH - 1.f);
             tau[j] = ldexpf(t[j], e);
           }
           // score = residual + ||c - R tau||^2
@@ -445,7 +461,7 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
             }
           }
           const float score = fmaxf(q2 - Lv, 0.f);
-          if (cand && seed <= kLastSeed && score < best[T]) {
+          if (cand && seed <= F::kLastSeed && score < best[T]) {
             best[T] = score;
             bseed[T] = seed;
             brec[T] = pack_record<P>(t, e);
@@ -487,7 +503,8 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
     for (int T = 0; T < NT; ++T) {
       const int64_t b = block0 + 16 * T + n;
       if (b >= a.nblk) continue;
-      a.seeds[b] = (uint16_t)bseed[T];
+      if constexpr (K <= 16) static_cast<uint16_t*>(a.seeds)[b] = (uint16_t)bseed[T];
+      else static_cast<uint32_t*>(a.seeds)[b] = (uint32_t)bseed[T];
       a.exps[b] = (int8_t)((int)(brec[T] >> 28) - 15);
 #pragma unroll
       for (int j = 0; j < P; ++j) {
@@ -501,54 +518,62 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
 
 }  // namespace
 
-// Formats the encoder is built for: the two packed ones, then the rest of the
-// 4-bit frontier ((20 + 4P) / C = 4 bits: (6,1) .. (12,7)), the 3-bit frontier
-// (largest P with (20 + 4P) / C <= 3) and two more points at C = 8.
-#define SEEDLM_ENC_FORMATS(X) \
-  X(8, 3) X(12, 4)            \
-  X(6, 1) X(7, 2) X(9, 4) X(10, 5) X(11, 6) X(12, 7) \
-  X(8, 1) X(9, 1) X(10, 2) X(11, 3) \
-  X(8, 2) X(8, 4)
+// Formats the encoder is built for (C, P, K, Q): the two packed ones, then the
+// rest of the 4-bit frontier ((K + QP + 4) / C = 4 at K = 16, Q = 4: (6,1) ..
+// (12,7)), the 3-bit frontier (largest P within 3 bits), two more points at
+// C = 8, and the frontiers at other seed widths (K = 12, 20) and with 3-bit
+// coefficients.
+#define SEEDLM_ENC_FORMATS(X)                                                     \
+  X(8, 3, 16, 4) X(12, 4, 16, 4)                                                  \
+  X(6, 1, 16, 4) X(7, 2, 16, 4) X(9, 4, 16, 4) X(10, 5, 16, 4) X(11, 6, 16, 4)    \
+  X(12, 7, 16, 4) X(8, 1, 16, 4) X(9, 1, 16, 4) X(10, 2, 16, 4) X(11, 3, 16, 4)   \
+  X(8, 2, 16, 4) X(8, 4, 16, 4)                                                   \
+  X(7, 3, 12, 4) X(9, 3, 20, 4) X(8, 2, 12, 4) X(12, 3, 20, 4)                    \
+  X(8, 4, 16, 3) X(10, 3, 16, 3)
 
-bool encoder_format_supported(int C, int P) {
-#define X(c, p) if (C == c && P == p) return true;
+bool encoder_format_supported(int C, int P, int K, int Q) {
+#define X(c, p, k, q) if (C == c && P == p && K == k && Q == q) return true;
   SEEDLM_ENC_FORMATS(X)
 #undef X
   return false;
 }
 
-size_t encoder_table_bytes(int C, int P) {
-#define X(c, p) if (C == c && P == p) return (size_t)kSeedTiles * EncLayout<c, p>::kTileBytes;
+size_t encoder_table_bytes(int C, int P, int K, int Q) {
+#define X(c, p, k, q)                                                                  \
+  if (C == c && P == p && K == k && Q == q)                                            \
+    return (size_t)EncFmt<c, p, k, q>::kSeedTiles * EncLayout<c, p, k, q>::kTileBytes;
   SEEDLM_ENC_FORMATS(X)
 #undef X
   return 0;
 }
 
-int launch_seed_table(int C, int P, void* table, hipStream_t s) {
-  const dim3 grid(16 * kSeedTiles / 256), block(256);
-#define X(c, p)                                                                              \
-  if (C == c && P == p) {                                                                    \
-    hipLaunchKernelGGL((seed_table_kernel<c, p>), grid, block, 0, s, static_cast<uint8_t*>(table)); \
-    SEEDLM_HIP_CHECK(hipGetLastError());                                                     \
-    return SEEDLM_OK;                                                                        \
+int launch_seed_table(int C, int P, int K, int Q, void* table, hipStream_t s) {
+#define X(c, p, k, q)                                                                   \
+  if (C == c && P == p && K == k && Q == q) {                                           \
+    const dim3 grid(16 * EncFmt<c, p, k, q>::kSeedTiles / 256), block(256);             \
+    hipLaunchKernelGGL((seed_table_kernel<c, p, k, q>), grid, block, 0, s,              \
+                       static_cast<uint8_t*>(table));                                   \
+    SEEDLM_HIP_CHECK(hipGetLastError());                                                \
+    return SEEDLM_OK;                                                                   \
   }
   SEEDLM_ENC_FORMATS(X)
 #undef X
   return SEEDLM_E_UNSUPPORTED;
 }
 
-int launch_encode(int C, int P, const void* table, const void* W, int64_t nblk, uint16_t* seeds,
-                  int8_t* coeffs, int8_t* exps, float* err, hipStream_t s) {
+int launch_encode(int C, int P, int K, int Q, const void* table, const void* W, int64_t nblk,
+                  void* seeds, int8_t* coeffs, int8_t* exps, float* err, hipStream_t s) {
   EncArgs a{static_cast<const uint8_t*>(table), static_cast<const uint16_t*>(W), nblk, seeds,
             coeffs, exps, err};
-#define X(c, p)                                                                              \
-  if (C == c && P == p) {                                                                    \
-    const int64_t per = EncLayout<c, p>::kBlocksPerGroup;                                    \
-    const int64_t groups = (nblk + per - 1) / per;                                           \
-    if (groups > 0x7FFFFFFF) return SEEDLM_E_UNSUPPORTED;                                    \
-    hipLaunchKernelGGL((encode_kernel<c, p>), dim3((unsigned)groups), dim3(kEncThreads), 0, s, a); \
-    SEEDLM_HIP_CHECK(hipGetLastError());                                                     \
-    return SEEDLM_OK;                                                                        \
+#define X(c, p, k, q)                                                                   \
+  if (C == c && P == p && K == k && Q == q) {                                           \
+    const int64_t per = EncLayout<c, p, k, q>::kBlocksPerGroup;                         \
+    const int64_t groups = (nblk + per - 1) / per;                                      \
+    if (groups > 0x7FFFFFFF) return SEEDLM_E_UNSUPPORTED;                               \
+    hipLaunchKernelGGL((encode_kernel<c, p, k, q>), dim3((unsigned)groups),             \
+                       dim3(kEncThreads), 0, s, a);                                     \
+    SEEDLM_HIP_CHECK(hipGetLastError());                                                \
+    return SEEDLM_OK;                                                                   \
   }
   SEEDLM_ENC_FORMATS(X)
 #undef X

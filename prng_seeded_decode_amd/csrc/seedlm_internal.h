@@ -39,7 +39,7 @@ struct seedlm_matrix {
 
 // An encoder: the per-seed table of one format on one device.
 struct seedlm_encoder {
-  int C = 0, P = 0, K = 0;
+  int C = 0, P = 0, K = 0, Q = 0;
   int device = 0;
   void* d_table = nullptr;
   size_t table_bytes = 0;
@@ -99,11 +99,11 @@ int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_
                      int batch, hipStream_t s);
 int build_ext_table(seedlm_matrix* h);
 // Seed search: per-seed QR table (bytes for format C) and the search itself.
-bool encoder_format_supported(int C, int P);
-size_t encoder_table_bytes(int C, int P);
-int launch_seed_table(int C, int P, void* table, hipStream_t s);
-int launch_encode(int C, int P, const void* table, const void* W, int64_t nblk, uint16_t* seeds,
-                  int8_t* coeffs, int8_t* exps, float* err, hipStream_t s);
+bool encoder_format_supported(int C, int P, int K, int Q);
+size_t encoder_table_bytes(int C, int P, int K, int Q);
+int launch_seed_table(int C, int P, int K, int Q, void* table, hipStream_t s);
+int launch_encode(int C, int P, int K, int Q, const void* table, const void* W, int64_t nblk,
+                  void* seeds, int8_t* coeffs, int8_t* exps, float* err, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -10,7 +10,8 @@ wn = ||w||^2:
     few dozen operations on terms of size <= wn stays near 1e-6 * wn;
   * that float64 score is within 1e-5 * wn of the oracle's minimum (a seed the
     kernel prefers by less than its rounding error is as good a choice);
-  * records are valid (seed in [1, 65535], t in [-8, 7], e in [-15, 0]), and
+  * records are valid (seed in [1, 2^K - 1], t in [-2^(Q-1), 2^(Q-1) - 1],
+    e in [-15, 0]), and
     where the seed agrees with the oracle's, t and e agree too.
 Seeds themselves are compared as a rate (they differ only at near-ties).
 Small matrices run the oracle on every block; large ones on sampled blocks.
@@ -46,41 +47,45 @@ def _say(*a):
 _ENCODERS = {}
 
 
-def _encoder(C, P):
-    if (C, P) not in _ENCODERS:
-        _ENCODERS[(C, P)] = _S().SeedLMEncoder(C, P, 16)
-    return _ENCODERS[(C, P)]
+def _encoder(C, P, K=16, Q=4):
+    key = (C, P, K, Q)
+    if key not in _ENCODERS:
+        _ENCODERS.clear()  # one seed table resident at a time
+        _ENCODERS[key] = _S().SeedLMEncoder(C, P, K, Q)
+    return _ENCODERS[key]
 
 
-def _run(bits, C, P):
+def _run(bits, C, P, K=16, Q=4):
     """Encode bf16 bit patterns on the GPU; returns host numpy records + scores."""
     dev = _dev()
     W = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    s, c, e, err = _S().seedlm_encode(_encoder(C, P), W)
+    s, c, e, err = _S().seedlm_encode(_encoder(C, P, K, Q), W)
     torch.cuda.synchronize()
-    return (s.cpu().numpy().view(np.uint16), c.cpu().numpy(), e.cpu().numpy(),
-            err.cpu().numpy().astype(np.float64))
+    s = s.cpu().numpy().view(np.uint16 if K <= 16 else np.uint32)
+    return s, c.cpu().numpy(), e.cpu().numpy(), err.cpu().numpy().astype(np.float64)
 
 
 def _blocks(W64, C):
     return W64.reshape(-1, C)
 
 
-def _check_blocks(Wb, s_g, c_g, e_g, err_g, C, P, min_seed_match=0.9):
+def _check_blocks(Wb, s_g, c_g, e_g, err_g, C, P, min_seed_match=0.9, K=16, Q=4):
     """Wb: (k, C) float64 blocks; GPU records for exactly those blocks."""
     k = Wb.shape[0]
     s_g = s_g.reshape(k, 1)
     c_g = c_g.reshape(k, 1, P)
     e_g = e_g.reshape(k, 1)
     err_g = err_g.reshape(k)
-    assert s_g.min() >= 1 and c_g.min() >= -8 and c_g.max() <= 7
+    h = 1 << (Q - 1)
+    assert s_g.min() >= 1 and int(s_g.max()) <= (1 << K) - 1
+    assert c_g.min() >= -h and c_g.max() <= h - 1
     assert e_g.min() >= -15 and e_g.max() <= 0
     wn = np.sum(Wb ** 2, axis=1)
-    dec = O.decode_rows(s_g, c_g, e_g, C, C, P)
+    dec = O.decode_rows(s_g, c_g, e_g, C, C, P, K=K)
     err64 = np.sum((Wb - dec) ** 2, axis=1)
     assert np.all(np.abs(err_g - err64) <= SCORE_TOL * wn + 1e-30), \
         np.max(np.abs(err_g - err64) / np.maximum(wn, 1e-30))
-    s_o, c_o, e_o, rec_o, err_o = O.encode_exhaustive(Wb, C, P)
+    s_o, c_o, e_o, rec_o, err_o = O.encode_exhaustive(Wb, C, P, K=K, Q=Q)
     err_o = err_o.reshape(k)
     assert np.all(err64 <= err_o + SCORE_TOL * wn + 1e-30), \
         np.max((err64 - err_o) / np.maximum(wn, 1e-30))
@@ -205,3 +210,48 @@ def test_encode_design_space_formats_match_oracle(C, P):
     bits = gen_bf16_weights(9, 10 * C + P, 2, 12 * C)  # 24 blocks
     s, c, e, err = _run(bits, C, P)
     _check_blocks(_blocks(bf16_to_float64(bits), C), s, c, e, err, C, P, min_seed_match=0.8)
+
+
+# Other seed widths (the K-bit LFSRs x^12+x^6+x^4+x+1 and x^20+x^3+1) and 3-bit
+# coefficients.  K = 20 walks 2^20 - 1 seeds: the oracle's exhaustive search
+# takes about half a minute per format there.
+SEED_WIDTH_FORMATS = [(7, 3, 12, 4), (8, 2, 12, 4), (9, 3, 20, 4), (12, 3, 20, 4),
+                      (8, 4, 16, 3), (10, 3, 16, 3)]
+
+
+@pytest.mark.parametrize("C,P,K,Q", SEED_WIDTH_FORMATS)
+def test_encode_seed_and_coefficient_widths_match_oracle(C, P, K, Q):
+    _say(f"encode format C={C} P={P} K={K} Q={Q}")
+    bits = gen_bf16_weights(9, 100 * K + 10 * C + P + Q, 2, 12 * C)  # 24 blocks
+    s, c, e, err = _run(bits, C, P, K, Q)
+    _check_blocks(_blocks(bf16_to_float64(bits), C), s, c, e, err, C, P, min_seed_match=0.8,
+                  K=K, Q=Q)
+
+
+def test_encode_seed_width_planted_records():
+    """Blocks made from K = 12 and K = 20 records (seeds past 2^16 for the
+    latter, so the wider seed output is exercised), rounded to bf16."""
+    for C, P, K in [(7, 3, 12), (9, 3, 20)]:
+        _say(f"encode planted C={C} P={P} K={K}")
+        rng = np.random.default_rng(77 + K)
+        n = 16
+        seeds = rng.integers(1, 1 << K, (1, n)).astype(np.uint32)
+        if K == 20:
+            seeds[0, :8] |= 1 << 16
+        coeffs = rng.integers(-8, 8, (1, n, P)).astype(np.int8)
+        coeffs[0, :, 0] = 7
+        exps = rng.integers(-12, -5, (1, n)).astype(np.int8)
+        W = O.decode_rows(seeds, coeffs, exps, n * C, C, P, K=K)
+        bits = to_bf16_bits(W).reshape(1, n * C)
+        s, c, e, err = _run(bits, C, P, K, 4)
+        planted = s.reshape(-1).astype(np.int64) == seeds.reshape(-1).astype(np.int64)
+        _say(f"  planted seed recovered for {planted.sum()} of {n} blocks")
+        assert planted.mean() >= 0.8
+        assert np.array_equal(c.reshape(-1, P)[planted], coeffs.reshape(-1, P)[planted])
+        assert np.array_equal(e.reshape(-1)[planted], exps.reshape(-1)[planted])
+        Wb = _blocks(bf16_to_float64(bits), C)
+        wn = np.sum(Wb ** 2, axis=1)
+        dec = O.decode_rows(s.reshape(n, 1), c.reshape(n, 1, P), e.reshape(n, 1), C, C, P, K=K)
+        assert np.all(np.abs(err - np.sum((Wb - dec) ** 2, axis=1)) <= SCORE_TOL * wn)
+        # no worse than the planted record itself
+        assert np.all(err <= np.sum((Wb - W.reshape(n, C)) ** 2, axis=1) + SCORE_TOL * wn)

@@ -103,10 +103,11 @@ def test_device_entry_points_reject_null_handles_without_touching_the_gpu():
     assert L.seedlm_fp16_gemv(x, x, x, 4, 12, 1, None) == S.E_INVALID
     assert L.seedlm_gemm(None, x, x, 4, S.F16, S.F16, None) == S.E_INVALID
     h = ctypes.c_void_p()
-    assert L.seedlm_encoder_create(8, 5, 16, ctypes.byref(h)) == S.E_UNSUPPORTED
-    assert L.seedlm_encoder_create(12, 3, 16, ctypes.byref(h)) == S.E_UNSUPPORTED
-    assert L.seedlm_encoder_create(8, 3, 12, ctypes.byref(h)) == S.E_UNSUPPORTED
-    assert L.seedlm_encoder_create(13, 4, 16, ctypes.byref(h)) == S.E_UNSUPPORTED
-    assert L.seedlm_encoder_create(8, 3, 16, None) == S.E_INVALID
+    assert L.seedlm_encoder_create(8, 5, 16, 4, ctypes.byref(h)) == S.E_UNSUPPORTED
+    assert L.seedlm_encoder_create(12, 3, 16, 4, ctypes.byref(h)) == S.E_UNSUPPORTED
+    assert L.seedlm_encoder_create(8, 3, 12, 4, ctypes.byref(h)) == S.E_UNSUPPORTED
+    assert L.seedlm_encoder_create(8, 3, 16, 5, ctypes.byref(h)) == S.E_UNSUPPORTED
+    assert L.seedlm_encoder_create(13, 4, 16, 4, ctypes.byref(h)) == S.E_UNSUPPORTED
+    assert L.seedlm_encoder_create(8, 3, 16, 4, None) == S.E_INVALID
     assert L.seedlm_encoder_destroy(None) == S.OK
     assert L.seedlm_encode(None, x, 4, 64, x, x, x, x, None) == S.E_INVALID
