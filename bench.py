@@ -44,7 +44,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-LUT_SOURCE = os.path.join(ROOT, "prng_seeded_decode_amd", "csrc", "gemv_lut.hip")
+LUT_SOURCES = [os.path.join(ROOT, "prng_seeded_decode_amd", "csrc", f)
+               for f in ("gemv_lut.hip", "lut_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lut_kernel_llama3_70b_layer_4bit_traffic.txt")
 
 
@@ -57,8 +58,11 @@ def measured_traffic():
         with open(TRAFFIC_FILE) as f:
             kv = dict(line.split(None, 1) for line in f
                       if line.strip() and not line.startswith("#"))
-        with open(LUT_SOURCE, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for path in LUT_SOURCES:
+            with open(path, "rb") as f:
+                h.update(f.read())
+        digest = h.hexdigest()
     except (OSError, ValueError):
         return None
     if kv.get("source_sha256", "").strip() != digest:

@@ -136,8 +136,8 @@ SEEDLM_API int seedlm_gemv(seedlm_handle h, const void* x, void* y, int batch,
 
 /*
  * seedlm_gemv_many -- y[i] = W_i x[i] for n matrices, same result as n calls
- * of seedlm_gemv on `stream`.  Consecutive batch-1 4-bit matrices are run
- * together (up to 8 per launch) so that small matrices share the GPU and the
+ * of seedlm_gemv on `stream`.  Consecutive batch-1 matrices of one format are
+ * run together (up to 8 per launch) so that small matrices share the GPU and the
  * per-launch cost is paid once; a decoder layer's q/k/v/o/gate/up/down is the
  * intended use (the pages' inference step, applied to every weight matrix:
  * paperhub.cn rebuttal text before Eq. (1)).
@@ -190,12 +190,13 @@ SEEDLM_API const char* seedlm_status_string(int status);
 
 /*
  * Kernel variants, for A/B measurement.  The default (SEEDLM_VARIANT_AUTO) is
- * what seedlm_gemv runs: LUT for batch 1 of the 4-bit format, MFMA for every
- * other fp16-x/fp16-y call, SIMPLE otherwise (fp32 x or fp32 y, where the
- * 1e-5 bar needs fp32 weights).
- *   SEEDLM_VARIANT_LUT     batch 1, 4-bit: basis bits from GF(2) byte tables in
- *                          LDS, dot with x through per-panel activation byte
- *                          tables in LDS
+ * what seedlm_gemv runs: LUT for batch 1 (both formats), MFMA for every other
+ * fp16-x/fp16-y call, SIMPLE otherwise (fp32 x or fp32 y, where the 1e-5 bar
+ * needs fp32 weights).
+ *   SEEDLM_VARIANT_LUT     batch 1, both formats: basis bits from GF(2) byte
+ *                          tables in LDS, dot with x through activation byte
+ *                          tables in LDS (per panel of 32 blocks for 4-bit,
+ *                          per half panel for 3-bit)
  *   SEEDLM_VARIANT_TABLE   as LUT, basis bits from a 2^16-entry table in L2
  *   SEEDLM_VARIANT_SIMPLE  any shape: one wave per row, per-lane LFSR stepping,
  *                          fp32 weights

@@ -66,11 +66,14 @@ int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch, int 
   switch (variant) {
     case SEEDLM_VARIANT_AUTO:
       if (batch == 1 && h->C == 8) return launch_gemv_lut(h, x, y, x_dtype, y_dtype, false, s);
+      if (batch == 1 && h->C == 12)
+        return launch_gemv_lut12_group(&h, &x, &y, 1, x_dtype, y_dtype, s, 3);
       if (x_dtype == SEEDLM_F16 && y_dtype == SEEDLM_F16)
         return launch_gemv_mfma(h, x, y, batch, x_dtype, y_dtype, s);
       return launch_gemv_simple(h, x, y, batch, x_dtype, y_dtype, s);
     case SEEDLM_VARIANT_LUT:
       if (batch != 1) return SEEDLM_E_UNSUPPORTED;
+      if (h->C == 12) return launch_gemv_lut12_group(&h, &x, &y, 1, x_dtype, y_dtype, s, 3);
       return launch_gemv_lut(h, x, y, x_dtype, y_dtype, false, s);
     case SEEDLM_VARIANT_TABLE: {
       if (batch != 1 || h->C != 8) return SEEDLM_E_UNSUPPORTED;
@@ -96,7 +99,7 @@ namespace {
 
 // Shared body of seedlm_gemv_many{,_begin,_end}: phases & 1 runs the main
 // kernels, phases & 2 the panel reductions.  Matrices outside the grouped
-// batch-1 4-bit path run their whole seedlm_gemv in phase 1.
+// batch-1 paths run their whole seedlm_gemv in phase 1.
 int gemv_many_phases(const seedlm_handle* handles, const void* const* x, void* const* y, int n,
                      int batch, int x_dtype, int y_dtype, void* stream, int phases) {
   if (!handles || !x || !y || n < 0) return SEEDLM_E_INVALID;
@@ -109,16 +112,19 @@ int gemv_many_phases(const seedlm_handle* handles, const void* const* x, void* c
   hipStream_t s = static_cast<hipStream_t>(stream);
   int i = 0;
   while (i < n) {
-    // Group consecutive batch-1 4-bit matrices (up to 8) into one launch pair.
+    // Group consecutive batch-1 matrices of one format (up to 8) into one
+    // launch pair.
+    const int C = handles[i]->C;
     int k = 0;
-    while (batch == 1 && i + k < n && k < 8 && handles[i + k]->C == 8 &&
+    while (batch == 1 && i + k < n && k < 8 && handles[i + k]->C == C &&
            handles[i + k]->bytes < 0x80000000ull)
       ++k;
     if (k >= 1) {
       const seedlm_matrix* hs[8];
       for (int j = 0; j < k; ++j) hs[j] = handles[i + j];
       const int st =
-          launch_gemv_lut_group(hs, x + i, y + i, k, x_dtype, y_dtype, false, s, phases);
+          C == 8 ? launch_gemv_lut_group(hs, x + i, y + i, k, x_dtype, y_dtype, false, s, phases)
+                 : launch_gemv_lut12_group(hs, x + i, y + i, k, x_dtype, y_dtype, s, phases);
       if (st != SEEDLM_OK) return st;
       i += k;
     } else {

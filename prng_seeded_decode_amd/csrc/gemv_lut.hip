@@ -49,12 +49,8 @@
 // words of a lane, so the LDS latency of one block hides behind the others.  A
 // row's partial sum is reduced over its 8 lanes with DPP and written per panel;
 // reduce_panels_kernel adds the panels in a fixed order (deterministic).
-#include <hip/hip_fp16.h>
-
-#include <algorithm>
-
 #include "lfsr_device.h"
-#include "seedlm_internal.h"
+#include "lut_common.h"
 
 namespace seedlm {
 namespace {
@@ -77,58 +73,10 @@ struct Smem {
 constexpr int kColT0 = 0, kColTC = 16, kColL2 = 32;  // column bases in region B
 constexpr uint32_t kRegionB = 65536;  // byte offset of B inside Smem
 
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-// Up to kMaxGroup matrices share one launch; their work items are numbered one
-// after another (matrix-major, then panel, then 8-row slab).
-constexpr int kMaxGroup = 8;
-struct LutMatrix {
-  const uint32_t* words;
-  const void* x;
-  float* partial;
-  void* y;
-  uint32_t words_bytes;
-  int Mp, rows, cols, nb, np;
-  int64_t item_begin;  // first global work item of this matrix
-  int red_begin;       // first reduce workgroup of this matrix (64 rows each)
-};
-constexpr int kMaxWorkgroups = 512;
-struct LutGroup {
-  LutMatrix m[kMaxGroup];
-  int n;
-  int red_blocks;  // reduce workgroups over all matrices
-  int grid;
-  // Workgroup w processes global work items [bounds[w], bounds[w+1]).
-  int32_t bounds[kMaxWorkgroups + 1];
-};
-
 // Cost model of the work split: a panel's table build costs about as much as
 // kBuildCost slabs of 8 rows.
 constexpr int64_t kBuildCost = 51;
 
-template <typename XT>
-__device__ inline float ldx(const XT* p);
-template <>
-__device__ inline float ldx<float>(const float* p) { return *p; }
-template <>
-__device__ inline float ldx<__half>(const __half* p) { return __half2float(*p); }
-
-// LDS byte address [lanec.b0, src.byte K, lanec.b2, 0]: row = stream byte,
-// column = this lane's slot (lanec.b0 = 4*slot), region = lanec.b2.
-template <int K>
-__device__ inline uint32_t lut_addr(uint32_t src, uint32_t lanec) {
-  return __builtin_amdgcn_perm(src, lanec, 0x0C020000u | ((4u + K) << 8));
-}
-
-template <typename T>
-__device__ inline T lds_at(const uint8_t* base, uint32_t byte_off) {
-  return *reinterpret_cast<const T*>(base + byte_off);
-}
-
-template <int CTRL>
-__device__ inline float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
 
 __device__ void build_panel_lut(Smem& sm, float xval) {
   // xval: this thread's x value of the panel (threads 0..255), loaded ahead.
@@ -419,56 +367,11 @@ __global__ void __launch_bounds__(kThreads, 1)
   }
 }
 
-template <typename YT>
-__device__ inline void store_y(YT* p, float v);
-template <>
-__device__ inline void store_y<float>(float* p, float v) { *p = v; }
-template <>
-__device__ inline void store_y<__half>(__half* p, float v) { *p = __float2half_rn(v); }
-
-// Panel reduction: y[r] = sum over panels p of partial[p][r].  A workgroup owns
-// 64 consecutive rows of one matrix (lane = row, so every load reads 256
-// contiguous bytes); wave w adds panels w, w+4, w+8, ... with up to 32 loads in
-// flight, and the four wave sums combine through LDS as (w0+w1)+(w2+w3).  The
-// order is fixed for a given panel count, so repeated calls give identical
-// results.
-template <typename YT>
-__global__ void __launch_bounds__(256) reduce_panels_kernel(const LutGroup grp) {
-  __shared__ float wsum[4][64];
-  int mi = 0;
-  while (mi + 1 < grp.n && (int)blockIdx.x >= grp.m[mi + 1].red_begin) ++mi;
-  const LutMatrix& M = grp.m[mi];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int r = ((int)blockIdx.x - M.red_begin) * 64 + lane;
-  const int rr = r < M.rows ? r : M.rows - 1;  // in-bounds load; no store below
-  const float* __restrict__ partial = M.partial + rr;
-  const int np = M.np;
-  const int64_t Mp = M.Mp;
-  float s = 0.f;
-  for (int p0 = wv; p0 < np; p0 += 4 * 32) {
-    float v[32];
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const int p = p0 + 4 * k;
-      v[k] = p < np ? partial[p * Mp] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < 32; ++k) s += v[k];
-  }
-  wsum[wv][lane] = s;
-  __syncthreads();
-  if (wv == 0 && r < M.rows)
-    store_y(static_cast<YT*>(M.y) + r, (wsum[0][lane] + wsum[1][lane]) + (wsum[2][lane] + wsum[3][lane]));
-}
-
 bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys, int n,
                 LutGroup& grp) {
   if (n < 1 || n > kMaxGroup) return false;
   grp = LutGroup{};
   grp.n = n;
-  int64_t items = 0;
-  int64_t red = 0;
   for (int i = 0; i < n; ++i) {
     const seedlm_matrix* h = hs[i];
     if (h->C != 8 || h->P != 3 || h->bytes >= 0x80000000ull) return false;
@@ -484,41 +387,9 @@ bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* con
     M.cols = (int)h->cols;
     M.nb = (int)h->nb;
     M.np = (int)h->np;
-    M.item_begin = items;
-    M.red_begin = (int)red;
-    items += h->np * (h->Mp / 8);
-    red += (h->rows + 63) / 64;
+    M.slabs = (int)(h->Mp / 8);
   }
-  if (red >= (1LL << 30) || items >= (1LL << 31)) return false;
-  grp.red_blocks = (int)red;
-  // Split the items into G ranges of equal cost: one unit per 8-row slab plus
-  // kBuildCost per panel a range starts or enters (its table build).
-  int64_t G = device_cu_count();
-  if (G > kMaxWorkgroups) G = kMaxWorkgroups;
-  if (G > items) G = items;
-  // Costs accumulate panel by panel: a range that enters a panel pays the
-  // build once, then one unit per slab.  One sweep places every boundary.
-  int64_t total_cost = 0;
-  for (int i = 0; i < n; ++i) total_cost += (int64_t)grp.m[i].np * (grp.m[i].Mp / 8 + kBuildCost);
-  grp.bounds[0] = 0;
-  int64_t w = 1, acc = 0;
-  for (int i = 0; i < n && w < G; ++i) {
-    const int64_t slabs = grp.m[i].Mp / 8;
-    for (int64_t p = 0; p < grp.m[i].np && w < G; ++p) {
-      const int64_t start = grp.m[i].item_begin + p * slabs;
-      const int64_t next = acc + kBuildCost + slabs;  // cost before the next panel
-      for (; w < G && w * total_cost / G <= next; ++w) {
-        const int64_t t = w * total_cost / G;
-        const int64_t j = t <= acc ? 0 : std::max<int64_t>(1, t - acc - kBuildCost);
-        grp.bounds[w] = (int32_t)(start + j);
-      }
-      acc = next;
-    }
-  }
-  for (; w < G; ++w) grp.bounds[w] = (int32_t)items;
-  grp.bounds[G] = (int32_t)items;
-  grp.grid = (int)G;
-  return true;
+  return split_group(grp, kBuildCost);
 }
 
 template <typename XT, bool kGT>
@@ -548,14 +419,7 @@ int launch_gemv_lut_group(const seedlm_matrix* const* hs, const void* const* xs,
     }
     SEEDLM_HIP_CHECK(hipGetLastError());
   }
-  if (phases & 2) {
-    const int64_t grid = grp.red_blocks;
-    if (ydt == SEEDLM_F32)
-      hipLaunchKernelGGL((reduce_panels_kernel<float>), dim3((unsigned)grid), dim3(256), 0, s, grp);
-    else
-      hipLaunchKernelGGL((reduce_panels_kernel<__half>), dim3((unsigned)grid), dim3(256), 0, s, grp);
-    SEEDLM_HIP_CHECK(hipGetLastError());
-  }
+  if (phases & 2) return launch_reduce(grp, ydt, s);
   return SEEDLM_OK;
 }
 

@@ -90,6 +90,8 @@ int launch_gemv_lut(const seedlm_matrix* h, const void* x, void* y, int xdt, int
 int launch_gemv_lut_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys,
                           int n, int xdt, int ydt, bool global_table, hipStream_t s, int phases);
 // Matrix-core path (fp16 x and y only; E_UNSUPPORTED otherwise).
+int launch_gemv_lut12_group(const seedlm_matrix* const* hs, const void* const* xs,
+                            void* const* ys, int n, int xdt, int ydt, hipStream_t s, int phases);
 int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
                      hipStream_t s);
 // Prefill GEMM (4-bit, fp16 X and Y; E_UNSUPPORTED otherwise).
