@@ -142,19 +142,26 @@ __global__ void __launch_bounds__(kThreads, 1)
   // host split them so that every range has about the same cost.
   const int64_t begin = grp.bounds[blockIdx.x];
   const int64_t end = grp.bounds[blockIdx.x + 1];
+  // Where `begin` lies: matrix mi, panel pp, first slab sa.  This is the only
+  // division of the loop; each later segment starts at the next panel.
+  int mi = 0;
+  while (mi + 1 < grp.n && begin >= grp.m[mi + 1].item_begin) ++mi;
+  int pp = 0, sa = 0;
+  if (begin < end) {
+    const uint32_t local = (uint32_t)(begin - grp.m[mi].item_begin);
+    const uint32_t slabs = (uint32_t)grp.m[mi].slabs;
+    pp = (int)(local / slabs);
+    sa = (int)(local - (uint32_t)pp * slabs);
+  }
   // The x of a segment's panel is loaded one segment ahead (threads 0..255
   // hold one raw value each) with a buffer load whose out-of-range offset
   // reads zero, so no branch or select follows the load and nothing waits on
   // it until the table build that uses it.
-  auto fetch_x = [&](int64_t item) -> uint32_t {
-    int m2 = 0;
-    while (m2 + 1 < grp.n && item >= grp.m[m2 + 1].item_begin) ++m2;
+  auto fetch_x = [&](int m2, int p2, bool valid) -> uint32_t {
     const LutMatrix& N = grp.m[m2];
-    const int64_t c = (item - N.item_begin) / (N.Mp / 8) * 256 + tid;
-    const uint32_t off = (item < end && tid < 256 && c < N.cols) ? (uint32_t)c * sizeof(XT)
-                                                                  : 0x80000000u;
-    // The matrix is the same for the whole workgroup: say so, so that the
-    // descriptor lives in scalar registers.
+    const int64_t c = (int64_t)p2 * 256 + tid;
+    const uint32_t off = (valid && tid < 256 && c < N.cols) ? (uint32_t)c * sizeof(XT)
+                                                           : 0x80000000u;
     const uint64_t xp = (uint64_t)N.x;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)xp);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(xp >> 32));
@@ -172,7 +179,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     else
       return __uint_as_float(raw);
   };
-  uint32_t x_next = fetch_x(begin);
+  uint32_t x_next = fetch_x(mi, pp, begin < end);
 
   // Copies of the GF(2) tables and of TC (built once per launch): values
   // staged, then replicated with 16-byte writes where consecutive lanes write
@@ -225,17 +232,18 @@ __global__ void __launch_bounds__(kThreads, 1)
 
 
   for (int64_t it = begin; it < end;) {
-    int mi = 0;
-    while (mi + 1 < grp.n && it >= grp.m[mi + 1].item_begin) ++mi;
     const LutMatrix& M = grp.m[mi];
     const int64_t Mp = M.Mp, np = M.np;
-    const int slabs = M.Mp / 8;
-    const int64_t local = it - M.item_begin;
-    const int64_t p = local / slabs;
-    const int sa = (int)(local - p * slabs);
-    const int64_t seg_stop = M.item_begin + (p + 1) * slabs;
-    const int64_t seg_end = seg_stop < end ? seg_stop : end;
-    const int sb = (int)(seg_end - M.item_begin - p * slabs);
+    const int slabs = M.slabs;
+    const int64_t p = pp;
+    const int64_t pstart = M.item_begin + p * slabs;
+    const int64_t seg_end = pstart + slabs < end ? pstart + slabs : end;
+    const int sb = (int)(seg_end - pstart);
+    int mn = mi, pn = pp + 1;  // the next segment's panel
+    if (pn == M.np) {
+      pn = 0;
+      ++mn;
+    }
     const int Wp = (int)panel_stored_width(p, M.nb);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)M.words, 0, (int)M.words_bytes, 0x00020000);
@@ -253,7 +261,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     const int s_first = sa + wave;
     v4u A[2] = {load(s_first), load(s_first + kWaves)};
     const uint32_t x_this = x_next;
-    x_next = fetch_x(seg_end);
+    x_next = fetch_x(mn < grp.n ? mn : mi, pn, seg_end < end);
     __syncthreads();  // previous panel's tables no longer in use
     build_panel_lut(sm, x_value(x_this));
     __syncthreads();
@@ -364,6 +372,9 @@ __global__ void __launch_bounds__(kThreads, 1)
       }
     }
     it = seg_end;
+    mi = mn;
+    pp = pn;
+    sa = 0;
   }
 }
 

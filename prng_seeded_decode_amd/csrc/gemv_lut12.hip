@@ -56,6 +56,7 @@ struct Smem {
   uint32_t R1[256][64];  // [T0lo | T1lo | T0hi | T1hi]
   float xs[kUnitCols];
   uint32_t gf2lo[512], gf2hi[512];  // T0 then T1, staged before replication
+  int next_slab;                    // slab counter of the current segment
 };
 constexpr int kH0 = 0, kH1 = 16, kH2 = 32, kH3 = 48;      // region 0 columns
 constexpr int kT0lo = 0, kT1lo = 16, kT0hi = 32, kT1hi = 48;  // region 1 columns
@@ -73,15 +74,45 @@ __host__ __device__ constexpr uint32_t byte_sel(int K) { return 0x0C020000u | ((
 // kBuildCost slabs of 16 rows.
 constexpr int64_t kBuildCost = 40;
 
+// Rows 8*vg .. 8*vg+7 of one table pair of a slot: the first table prices bits
+// MA .. MA+7 of a byte (c_MA ..), the second bits MB .. MB+NB-1; the first also
+// carries `base` (-2^15 sum x for H0).  Indices are compile-time, so c stays in
+// registers.
+template <int MA, int MB, int NB>
+__device__ inline void build_pair(const float (&c)[27], float base, int vg, uint32_t* ta,
+                                  uint32_t* tb) {
+  float Ba = base, Bb = 0.f;
+#pragma unroll
+  for (int k = 3; k < 8; ++k) {
+    if ((vg >> (k - 3)) & 1) {
+      Ba += c[MA + k];
+      if (k < NB) Bb += c[MB + k];
+    }
+  }
+  float La[8], Lb[8];
+  La[0] = Lb[0] = 0.f;
+#pragma unroll
+  for (int n = 1; n < 8; ++n) {
+    const int low = __builtin_ctz(n), rest = n & (n - 1);
+    La[n] = La[rest] + c[MA + low];
+    Lb[n] = low < NB ? Lb[rest] + c[MB + low] : Lb[rest];
+  }
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int v = 8 * vg + n;
+    ta[v * 64] = __float_as_uint(La[n] + Ba);
+    tb[v * 64] = __float_as_uint(Lb[n] + Bb);
+  }
+}
+
 __device__ void build_unit_lut(Smem& sm, float xval) {
   // xval: this thread's x value of the unit (threads 0..191), loaded ahead.
   const int tid = threadIdx.x;
   if (tid < kUnitCols) sm.xs[tid] = xval;
   __syncthreads();
-  // Thread -> (slot, table pair, 8-row group): pair 0 writes H0 and H2, pair 1
-  // H1 and H3, rows 8*vg .. 8*vg+7.  A half-wave covers the 16 slots of both
-  // tables of a write for one vg, i.e. 32 different banks of one row.
-  const int slot = tid & 15, pair = (tid >> 4) & 1, vg = tid >> 5;
+  // Thread -> (table pair, slot, 8-row group): threads 0..511 write H0 and H2,
+  // 512..1023 H1 and H3 (a choice uniform over each wave), rows 8*vg .. 8*vg+7.
+  const int slot = tid & 15, vg = (tid >> 4) & 31, pair = tid >> 9;
   float xv[12];
 #pragma unroll
   for (int i = 0; i < 12; ++i) xv[i] = sm.xs[slot * 12 + i];
@@ -93,40 +124,13 @@ __device__ void build_unit_lut(Smem& sm, float xval) {
   c[26] = 32768.f * xv[11];
 #pragma unroll
   for (int m = 25; m >= 15; --m) c[m] = fmaf(0.5f, c[m + 1], 32768.f * xv[m - 15]);
-  float S = 0.f;
+  if (pair == 0) {
+    float S = 0.f;
 #pragma unroll
-  for (int i = 0; i < 12; ++i) S += xv[i];
-  // ca: coefficients of the first table (H0 or H1), cb: of the second (H2 or
-  // H3; H3 has three).
-  float ca[8], cb[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    ca[k] = pair ? c[8 + k] : c[k];
-    cb[k] = pair ? (k < 3 ? c[24 + k] : 0.f) : c[16 + k];
-  }
-  float Ba = pair ? 0.f : -32768.f * S, Bb = 0.f;
-#pragma unroll
-  for (int k = 3; k < 8; ++k) {
-    if ((vg >> (k - 3)) & 1) {
-      Ba += ca[k];
-      Bb += cb[k];
-    }
-  }
-  float La[8], Lb[8];
-  La[0] = Lb[0] = 0.f;
-#pragma unroll
-  for (int n = 1; n < 8; ++n) {
-    const int low = __builtin_ctz(n), rest = n & (n - 1);
-    La[n] = La[rest] + ca[low];
-    Lb[n] = Lb[rest] + cb[low];
-  }
-  uint32_t* ta = pair ? &sm.R0[0][kH1 + slot] : &sm.R0[0][kH0 + slot];
-  uint32_t* tb = pair ? &sm.R0[0][kH3 + slot] : &sm.R0[0][kH2 + slot];
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int v = 8 * vg + n;
-    ta[v * 64] = __float_as_uint(La[n] + Ba);
-    tb[v * 64] = __float_as_uint(Lb[n] + Bb);
+    for (int i = 0; i < 12; ++i) S += xv[i];
+    build_pair<0, 16, 8>(c, -32768.f * S, vg, &sm.R0[0][kH0 + slot], &sm.R0[0][kH2 + slot]);
+  } else {
+    build_pair<8, 24, 3>(c, 0.f, vg, &sm.R0[0][kH1 + slot], &sm.R0[0][kH3 + slot]);
   }
 }
 
@@ -139,15 +143,24 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
 
   const int64_t begin = grp.bounds[blockIdx.x];
   const int64_t end = grp.bounds[blockIdx.x + 1];
+  // Where `begin` lies: matrix mi, column unit u, first slab sa.  This is the
+  // only division of the loop; each later segment starts at the next unit.
+  int mi = 0;
+  while (mi + 1 < grp.n && begin >= grp.m[mi + 1].item_begin) ++mi;
+  int u = 0, sa = 0;
+  if (begin < end) {
+    const uint32_t local = (uint32_t)(begin - grp.m[mi].item_begin);
+    const uint32_t slabs = (uint32_t)grp.m[mi].slabs;
+    u = (int)(local / slabs);
+    sa = (int)(local - (uint32_t)u * slabs);
+  }
   // The x of a segment's unit is loaded one segment ahead (threads 0..191 hold
   // one raw value each) with a buffer load whose out-of-range offset reads
   // zero: columns past the matrix enter the tables as x = 0.
-  auto fetch_x = [&](int64_t item) -> uint32_t {
-    int m2 = 0;
-    while (m2 + 1 < grp.n && item >= grp.m[m2 + 1].item_begin) ++m2;
+  auto fetch_x = [&](int m2, int u2, bool valid) -> uint32_t {
     const LutMatrix& N = grp.m[m2];
-    const int64_t c = (item - N.item_begin) / N.slabs * kUnitCols + tid;
-    const uint32_t off = (item < end && tid < kUnitCols && c < N.cols)
+    const int64_t c = (int64_t)u2 * kUnitCols + tid;
+    const uint32_t off = (valid && tid < kUnitCols && c < N.cols)
                              ? (uint32_t)c * sizeof(XT) : 0x80000000u;
     const uint64_t xp = (uint64_t)N.x;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)xp);
@@ -166,7 +179,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
     else
       return __uint_as_float(raw);
   };
-  uint32_t x_next = fetch_x(begin);
+  uint32_t x_next = fetch_x(mi, u, begin < end);
 
   // GF(2) tables (built once per launch), 16 copies of each word: staged, then
   // replicated with 16-byte writes.
@@ -210,17 +223,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
   }
 
   for (int64_t it = begin; it < end;) {
-    int mi = 0;
-    while (mi + 1 < grp.n && it >= grp.m[mi + 1].item_begin) ++mi;
     const LutMatrix& M = grp.m[mi];
     const int64_t Mp = M.Mp;
     const int slabs = M.slabs;
-    const int64_t local = it - M.item_begin;
-    const int64_t u = local / slabs;  // column unit: half h of panel p
-    const int sa = (int)(local - u * slabs);
-    const int64_t seg_stop = M.item_begin + (u + 1) * slabs;
-    const int64_t seg_end = seg_stop < end ? seg_stop : end;
-    const int sb = (int)(seg_end - M.item_begin - u * slabs);
+    const int64_t ustart = M.item_begin + (int64_t)u * slabs;  // u: half (u & 1) of panel p
+    const int64_t seg_end = ustart + slabs < end ? ustart + slabs : end;
+    const int sb = (int)(seg_end - ustart);
+    int mn = mi, un = u + 1;  // the next segment's unit
+    if (un == M.np) {
+      un = 0;
+      ++mn;
+    }
     const int64_t p = u >> 1;
     const int grp4 = 4 * (int)(u & 1) + g;  // this lane's slot group in the panel
     const int Wp = (int)panel_stored_width(p, M.nb);
@@ -252,8 +265,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
     const int s_first = sa + wave;
     Slab A[2] = {load(s_first), load(s_first + kWaves)};
     const uint32_t x_this = x_next;
-    x_next = fetch_x(seg_end);
-    __syncthreads();  // previous unit's tables no longer in use
+    x_next = fetch_x(mn < grp.n ? mn : mi, un, seg_end < end);
+    __syncthreads();  // previous unit's tables and slab counter no longer in use
+    if (tid == 0) sm.next_slab = sa + 2 * kWaves;
     build_unit_lut(sm, x_value(x_this));
     __syncthreads();
 
@@ -358,18 +372,38 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc * 0x1p-30f), prsrc, poff, 0, 0);
     };
 
-    // Two register sets alternate, each load issued two slabs ahead of its use.
-    for (int s0 = s_first; s0 < sb; s0 += 4 * kWaves) {
-      Slab Bq[2] = {load(s0 + 2 * kWaves), load(s0 + 3 * kWaves)};
-      const int n0 = min(4, (sb - s0 + kWaves - 1) / kWaves);  // valid slabs of the group
-      run(A[0], s0);
-      A[0] = load(s0 + 4 * kWaves);
-      if (n0 > 1) run(A[1], s0 + kWaves);
-      A[1] = load(s0 + 5 * kWaves);
-      if (n0 > 2) run(Bq[0], s0 + 2 * kWaves);
-      if (n0 > 3) run(Bq[1], s0 + 3 * kWaves);
+    // A wave's first two slabs are fixed (their loads went out before the
+    // build); after that it takes the next slab of the segment from a counter
+    // in LDS.  The SIMDs favour their older waves, so with a fixed share the
+    // younger waves finished several microseconds later; taking slabs on demand
+    // lets every wave finish within about one slab of the others.  Indices a
+    // wave takes only grow, so once one is past the segment all later ones are.
+    // Two register sets alternate, each load issued two slabs ahead of its use;
+    // loads past the segment read harmless words (or zeros past the buffer).
+    auto grab = [&]() -> int {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(&sm.next_slab, 1);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    int i0 = s_first, i1 = s_first + kWaves;
+    while (i0 < sb) {
+      const int i2 = grab(), i3 = grab();
+      Slab Bq[2] = {load(i2), load(i3)};
+      run(A[0], i0);
+      const int i4 = grab();
+      A[0] = load(i4);
+      if (i1 < sb) run(A[1], i1);
+      const int i5 = grab();
+      A[1] = load(i5);
+      if (i2 < sb) run(Bq[0], i2);
+      if (i3 < sb) run(Bq[1], i3);
+      i0 = i4;
+      i1 = i5;
     }
     it = seg_end;
+    mi = mn;
+    u = un;
+    sa = 0;
   }
 }
 
