@@ -75,7 +75,9 @@ def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # The part needs tens of milliseconds of load to reach its steady clocks: after
+    # 10 warm-up steps the next 50 ran ~20% slower than the same steps later on.
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--config", type=int, default=4)
     p.add_argument("--batch", type=int, default=1)
     p.add_argument("--variant", type=int, default=0)
@@ -591,6 +593,11 @@ def main():
             eager_step(k, phase)
 
     # ---- whole-step timing ----
+    # The collector stays off while launches are timed: a collection pause in the
+    # host loop could otherwise leave the GPU idle inside a timed interval.
+    import gc
+
+    gc.disable()
     for k in range(args.warmup):
         run_step(k)
     torch.cuda.synchronize()
@@ -623,17 +630,16 @@ def main():
     # of each step (seedlm_gemv_many_begin), the panel reduction outside them ----
     kern_ms = []
     if args.variant == 0:
-        kev = []
-        for k in range(args.steps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for k, (a, b) in enumerate(kev):
             a.record(stream)
             run_step(k, "begin")
             b.record(stream)
             run_step(k, "end")
-            kev.append((a, b))
         torch.cuda.synchronize()
         kern_ms = [a.elapsed_time(b) for a, b in kev]
+    gc.enable()
 
     layer_weights = sum(d["mat"].rows * d["mat"].cols for d in mats)
     layer_bytes = sum(d["bytes"] for d in mats)
@@ -679,6 +685,7 @@ def main():
                     torch.nn.functional.linear(xs[i], W, out=ys[i])
 
         res = {}
+        gc.disable()
         for own, name in ((True, "own_fp16_gemv"), (False, "torch_linear_fp16")):
             for k in range(args.warmup):
                 fp16_step(k, own)
@@ -689,6 +696,7 @@ def main():
             ev1.record(stream)
             ev1.synchronize()
             res[name] = ev0.elapsed_time(ev1) / args.steps
+        gc.enable()
         best = min(res.values())
         fp16 = {"ms_per_step": {k: round(v, 4) for k, v in res.items()},
                 "fp16_GBps": round(sum(2 * r * c for r, c in ((d["mat"].rows, d["mat"].cols) for d in mats))
