@@ -76,8 +76,10 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     # The part needs tens of milliseconds of load to reach its steady clocks: after
-    # 10 warm-up steps the next 50 ran ~20% slower than the same steps later on.
-    p.add_argument("--warmup", type=int, default=200)
+    # 10 warm-up steps of the batch-1 layer the next 50 ran ~20% slower than the
+    # same steps later on.  Default: 200 steps of the decode-GEMV (~25 ms), 20 of
+    # the prefill GEMM (~100 ms), 3 seed searches (~300 ms).
+    p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--config", type=int, default=4)
     p.add_argument("--batch", type=int, default=1)
     p.add_argument("--variant", type=int, default=0)
@@ -509,6 +511,8 @@ def sweep_main(args):
 
 def main():
     args = parse_args()
+    if args.warmup is None:
+        args.warmup = 3 if args.encode else (20 if args.gemm else 200)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
