@@ -282,10 +282,12 @@ SEEDLM_API int seedlm_encoder_destroy(seedlm_encoder_handle e);
 
 /*
  * seedlm_encode -- exhaustive seed search for every block of a dense matrix.
- *   W      device bf16 [rows][cols] (raw bf16 bit patterns, row-major), cols a
- *          multiple of C; 16-byte aligned for C = 8, 2-byte aligned otherwise;
- *          finite values
- *   seeds  device uint16 [rows][nb] (uint32 for K > 16), nb = cols / C (out)
+ *   W      device bf16 [rows][cols] (raw bf16 bit patterns, row-major); 16-byte
+ *          aligned when C = 8 and cols is a multiple of 8, 2-byte aligned
+ *          otherwise; finite values.  When cols is not a multiple of C, a row's
+ *          last block holds its cols - (nb-1) C weights followed by zeros, and is
+ *          searched as a full block (seedlm_decode drops the padding columns)
+ *   seeds  device uint16 [rows][nb] (uint32 for K > 16), nb = ceil(cols / C) (out)
  *   coeffs device int8   [rows][nb][P]                 (out)
  *   exps   device int8   [rows][nb]                    (out)
  *   err    device float  [rows][nb], the fp32 score of the chosen record, or

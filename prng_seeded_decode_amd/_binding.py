@@ -340,9 +340,7 @@ def seedlm_encode(enc: SeedLMEncoder, W, seeds=None, coeffs=None, exps=None, err
     if W.dtype != torch.bfloat16 or W.dim() != 2 or not (W.is_cuda and W.is_contiguous()):
         raise ValueError("W must be a contiguous 2-D bfloat16 device tensor")
     rows, cols = W.shape
-    if cols % enc.C:
-        raise ValueError("cols must be a multiple of C")
-    nb = cols // enc.C
+    nb = -(-cols // enc.C)  # a short last block is searched with zeros in its missing slots
     dev = W.device
     if seeds is None:
         seeds = torch.empty((rows, nb), dtype=torch.int16 if enc.K <= 16 else torch.int32,

@@ -213,15 +213,15 @@ int seedlm_encoder_destroy(seedlm_encoder_handle e) {
 int seedlm_encode(seedlm_encoder_handle e, const void* W, int64_t rows, int64_t cols, void* seeds,
                   int8_t* coeffs, int8_t* exps, float* err, void* stream) {
   if (!e || !W || !seeds || !coeffs || !exps) return SEEDLM_E_INVALID;
-  if (rows <= 0 || cols <= 0 || cols % e->C != 0) return SEEDLM_E_INVALID;
-  const uintptr_t align = e->C == 8 ? 16 : 2;
+  if (rows <= 0 || cols <= 0) return SEEDLM_E_INVALID;
+  const uintptr_t align = e->C == 8 && cols % 8 == 0 ? 16 : 2;
   if ((uintptr_t)W % align != 0) return SEEDLM_E_INVALID;
-  if (rows > INT64_MAX / cols) return SEEDLM_E_INVALID;
+  if (rows > INT64_MAX / (cols + e->C)) return SEEDLM_E_INVALID;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return SEEDLM_E_DEVICE;
   if (dev != e->device) return SEEDLM_E_INVALID;
-  return launch_encode(e->C, e->P, e->K, e->Q, e->d_table, W, rows * (cols / e->C), seeds, coeffs,
-                       exps, err, static_cast<hipStream_t>(stream));
+  return launch_encode(e->C, e->P, e->K, e->Q, e->d_table, W, rows, cols, seeds, coeffs, exps, err,
+                       static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

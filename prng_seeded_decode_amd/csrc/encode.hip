@@ -213,8 +213,9 @@ __global__ void __launch_bounds__(256) seed_table_kernel(uint8_t* __restrict__ t
 
 struct EncArgs {
   const uint8_t* table;
-  const uint16_t* W;  // bf16 bits, nblk blocks of C
-  int64_t nblk;
+  const uint16_t* W;  // bf16 bits, [rows][cols]
+  int64_t nblk;       // rows * nbr
+  int64_t cols, nbr;  // columns, blocks per row (ceil(cols / C))
   void* seeds;  // uint16 for K <= 16, uint32 above
   int8_t* coeffs;
   int8_t* exps;
@@ -230,17 +231,29 @@ struct BlockOps {
   using F = EncFmt<C, P, K, Q>;
   bf16x8 b1;
   s16x4 b2;
-  __device__ void load(const uint16_t* W, int64_t b, bool valid, int qg, float& wn) {
+  // Block b of a [rows][cols] matrix: row b / nbr, columns (b % nbr) * C ..;
+  // a row's last block may be short (cols not a multiple of C), and its
+  // missing weights are read as zeros.
+  __device__ void load(const uint16_t* W, int64_t b, bool valid, int64_t cols, int64_t nbr,
+                       int qg, float& wn) {
     uint16_t x[C];
-    if constexpr (C == 8) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (valid) v = *reinterpret_cast<const uint4*>(W + b * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (cols % C == 0) {
+      if constexpr (C == 8) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (valid) v = *reinterpret_cast<const uint4*>(W + b * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+        for (int i = 0; i < 8; ++i) x[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+      } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) x[i] = valid ? W[b * C + i] : (uint16_t)0;
+      }
     } else {
+      const int64_t r = valid ? b / nbr : 0;
+      const int64_t c0 = (b - r * nbr) * C;
+      const int64_t n = valid ? cols - c0 : 0;  // weights present (may exceed C)
 #pragma unroll
-      for (int i = 0; i < C; ++i) x[i] = valid ? W[b * C + i] : (uint16_t)0;
+      for (int i = 0; i < C; ++i) x[i] = i < n ? W[r * cols + c0 + i] : (uint16_t)0;
     }
     float s = 0.f;
 #pragma unroll
@@ -306,7 +319,7 @@ __global__ void __launch_bounds__(kEncThreads, 4) encode_kernel(const EncArgs a)
   for (int T = 0; T < NT; ++T) {
     const int64_t b = block0 + 16 * T + n;
     float wn;
-    ops[T].load(a.W, b, b < a.nblk, qg, wn);
+    ops[T].load(a.W, b, b < a.nblk, a.cols, a.nbr, qg, wn);
     nwn[T] = -wn;
     best[T] = __builtin_inff();
     bseed[T] = 0;
@@ -561,10 +574,13 @@ int launch_seed_table(int C, int P, int K, int Q, void* table, hipStream_t s) {
   return SEEDLM_E_UNSUPPORTED;
 }
 
-int launch_encode(int C, int P, int K, int Q, const void* table, const void* W, int64_t nblk,
-                  void* seeds, int8_t* coeffs, int8_t* exps, float* err, hipStream_t s) {
-  EncArgs a{static_cast<const uint8_t*>(table), static_cast<const uint16_t*>(W), nblk, seeds,
-            coeffs, exps, err};
+int launch_encode(int C, int P, int K, int Q, const void* table, const void* W, int64_t rows,
+                  int64_t cols, void* seeds, int8_t* coeffs, int8_t* exps, float* err,
+                  hipStream_t s) {
+  const int64_t nbr = (cols + C - 1) / C;
+  const int64_t nblk = rows * nbr;
+  EncArgs a{static_cast<const uint8_t*>(table), static_cast<const uint16_t*>(W), nblk, cols, nbr,
+            seeds, coeffs, exps, err};
 #define X(c, p, k, q)                                                                   \
   if (C == c && P == p && K == k && Q == q) {                                           \
     const int64_t per = EncLayout<c, p, k, q>::kBlocksPerGroup;                         \

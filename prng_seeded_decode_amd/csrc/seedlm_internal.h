@@ -104,8 +104,9 @@ int build_ext_table(seedlm_matrix* h);
 bool encoder_format_supported(int C, int P, int K, int Q);
 size_t encoder_table_bytes(int C, int P, int K, int Q);
 int launch_seed_table(int C, int P, int K, int Q, void* table, hipStream_t s);
-int launch_encode(int C, int P, int K, int Q, const void* table, const void* W, int64_t nblk,
-                  void* seeds, int8_t* coeffs, int8_t* exps, float* err, hipStream_t s);
+int launch_encode(int C, int P, int K, int Q, const void* table, const void* W, int64_t rows,
+                  int64_t cols, void* seeds, int8_t* coeffs, int8_t* exps, float* err,
+                  hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

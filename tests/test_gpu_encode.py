@@ -183,19 +183,20 @@ def test_encode_is_deterministic_and_rejects_bad_arguments():
     enc = _encoder(8, 3)
     W = torch.zeros((4, 64), dtype=torch.bfloat16, device=dev)
     with pytest.raises(ValueError):
-        S.seedlm_encode(enc, torch.zeros((4, 60), dtype=torch.bfloat16, device=dev))
+        S.seedlm_encode(enc, torch.zeros((4, 64), dtype=torch.float16, device=dev))
     import ctypes
 
     L = S.lib()
     out = torch.empty(64, dtype=torch.int32, device=dev)
     p = ctypes.c_void_p(out.data_ptr())
-    # misaligned W (C = 8 needs 16-byte alignment)
+    # misaligned W (C = 8 with cols a multiple of 8 needs 16-byte alignment)
     assert L.seedlm_encode(enc.handle, ctypes.c_void_p(W.data_ptr() + 2), 2, 16, p, p, p, p,
-                           None) == S.E_INVALID
-    assert L.seedlm_encode(enc.handle, ctypes.c_void_p(W.data_ptr()), 4, 60, p, p, p, p,
                            None) == S.E_INVALID
     assert L.seedlm_encode(enc.handle, ctypes.c_void_p(W.data_ptr()), 0, 64, p, p, p, p,
                            None) == S.E_INVALID
+    assert L.seedlm_encode(enc.handle, ctypes.c_void_p(W.data_ptr()), 4, 0, p, p, p, p,
+                           None) == S.E_INVALID
+    assert L.seedlm_encode(enc.handle, None, 4, 64, p, p, p, p, None) == S.E_INVALID
 
 
 # The other formats the encoder is built for (records only: the design-space
@@ -255,3 +256,35 @@ def test_encode_seed_width_planted_records():
         assert np.all(np.abs(err - np.sum((Wb - dec) ** 2, axis=1)) <= SCORE_TOL * wn)
         # no worse than the planted record itself
         assert np.all(err <= np.sum((Wb - W.reshape(n, C)) ** 2, axis=1) + SCORE_TOL * wn)
+
+
+@pytest.mark.parametrize("C,P,rows,cols", [(8, 3, 6, 8 * 9 + 3), (12, 4, 5, 12 * 7 + 4),
+                                          (8, 3, 3, 5), (12, 4, 2, 12 * 341 + 4)])
+def test_encode_ragged_columns(C, P, rows, cols):
+    """cols not a multiple of C (4096 = 12*341 + 4 for the 3-bit Llama shapes): a row's
+    last block holds its real weights followed by zeros and is searched as a full
+    block, so the oracle's search runs on the same zero-padded block.  The records
+    pack and decode at the real shape."""
+    _say(f"encode ragged C={C} {rows}x{cols}")
+    nb = -(-cols // C)
+    bits = gen_bf16_weights(10, 1000 + cols, rows, cols)
+    s, c, e, err = _run(bits, C, P)
+    assert s.shape == (rows, nb) and c.shape == (rows, nb, P)
+    padded = np.zeros((rows, nb * C), dtype=np.float64)
+    padded[:, :cols] = bf16_to_float64(bits)
+    Wb = _blocks(padded, C)
+    k = Wb.shape[0]
+    if k > 64:  # check the row ends and a sample of the rest against the search
+        idx = np.unique(np.concatenate([np.arange(nb - 1, k, nb),
+                                        np.random.default_rng(3).choice(k, 24, replace=False)]))
+    else:
+        idx = np.arange(k)
+    _check_blocks(Wb[idx], s.reshape(k)[idx], c.reshape(k, P)[idx], e.reshape(k)[idx],
+                  err.reshape(k)[idx], C, P, min_seed_match=0.8)
+    S = _S()
+    m = S.seedlm_pack(s.astype(np.uint16), c, e, rows, cols, C, P, 16)
+    Wd = torch.empty((rows, cols), dtype=torch.float32, device=_dev())
+    S.seedlm_decode(m, Wd)
+    torch.cuda.synchronize()
+    ref = O.decode_rows(s, c, e, cols, C, P)
+    assert np.array_equal(Wd.cpu().numpy(), ref.astype(np.float32))
