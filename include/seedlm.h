@@ -227,14 +227,15 @@ SEEDLM_API int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t r
  * seedlm_gemm -- Y = X W^T for any number of activation rows (prefill), with W
  * rebuilt from the handle's records inside the kernel and never stored in HBM
  * (paperhub.cn rebuttal text before Eq. (1): weights are reconstructed on the
- * fly from s and t and used to compute the activations).  Each 128 x 64 tile of
- * W is decoded exactly once per 256 activation rows and contracted on the
- * matrix cores (fp16 operands, fp32 accumulation).
+ * fly from s and t and used to compute the activations).  Each 128-row tile of
+ * W is decoded exactly once per 256 or 512 activation rows and contracted on
+ * the matrix cores (fp16 operands, fp32 accumulation).
  *   X  device fp16 [ntok][cols], 16-byte aligned (row-major)
  *   Y  device fp16 [ntok][rows] (round to nearest even); both caller-owned
- *   ntok >= 1.  4-bit format (C = 8) with cols a multiple of 8, fp16 X and Y
- *   only; other formats and dtypes return SEEDLM_E_UNSUPPORTED (for up to 16
- *   rows seedlm_gemv covers them).
+ *   ntok >= 1.  Both packed formats (C = 8 and C = 12) with cols a multiple of
+ *   8, fp16 X and Y only; other dtypes return SEEDLM_E_UNSUPPORTED (for up to
+ *   16 rows seedlm_gemv covers them), as do X or the packed buffer of 2 GiB or
+ *   more.
  * Asynchronous on `stream`; no workspace, so calls may overlap.
  * Errors: SEEDLM_E_INVALID (null, ntok < 1), SEEDLM_E_UNSUPPORTED (format,
  * dtype, alignment), SEEDLM_E_DEVICE (launch failure).

@@ -1,5 +1,6 @@
 // Prefill-size decode-GEMM on the matrix cores: Y[t][r] = sum_c W[r][c] X[t][c]
-// for any number of token rows t, 4-bit format, fp16 X and Y, fp32 accumulation.
+// for any number of token rows t, fp16 X and Y, fp32 accumulation; 4-bit format
+// (gemm_c8_kernel) and 3-bit format (gemm_c12_kernel, at the end of the file).
 //
 // SeedLM rebuilds the weights from each block's seed and coefficients where they
 // are used (paperhub.cn rebuttal text before Eq. (1); atlas.scime.ai
@@ -251,11 +252,213 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
     }
 }
 
+// The 3-bit format (C = 12, P = 4): the same scheme with a K step of 48 columns
+// (one 16-byte group = 4 blocks of 12) and 256-token tiles.  X and W rows of a
+// step are 96 bytes; in LDS they are padded to 112 bytes (7 chunks of 16), and
+// 7t mod 16 takes 16 distinct values over 16 consecutive tokens (and 7t mod 8
+// over 8), so operand reads are free of bank conflicts without a swizzle.
+// Each block's exponent nibble comes from the format's separate nibble array
+// (one u16 per group of four blocks, in the order of the group's words).
+constexpr int kStep12 = 48;                  // columns per K step
+constexpr int kSlices12 = kStep12 / 16;      // MFMAs of K = 16 per step
+constexpr int kRow12 = 112;                  // LDS bytes per X token row / W row
+constexpr int kToks12 = 256;                 // tokens per tile
+constexpr int kNTiles12 = kToks12 / 2 / 32;  // 32-token MFMA tiles per wave
+constexpr int kX12Bytes = kToks12 * kRow12;  // 28 KiB
+constexpr int kW12Bytes = kTileRows * kRow12;  // 14 KiB
+constexpr int kX12Copies = kX12Bytes / 1024 / 4;  // 1 KiB LDS copies per wave per step
+static_assert(kX12Bytes % 4096 == 0 && kX12Copies == 7, "X tile layout");
+
+struct Gemm12Args {
+  const uint32_t* words;
+  const __half* x;
+  __half* y;
+  int rows, cols, Mp, nb, ntok;
+  uint32_t buf_bytes, exp_off, x_bytes;  // packed buffer size, exponent array offset, X size
+};
+
+__global__ void __launch_bounds__(kGemmThreads, 1) gemm_c12_kernel(const Gemm12Args a) {
+  __shared__ uint64_t T0[256], T1[256];
+  __shared__ __attribute__((aligned(16))) uint8_t w0[kW12Bytes], w1[kW12Bytes], w2[kW12Bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t x0[kX12Bytes], x1[kX12Bytes], x2[kX12Bytes];
+  uint8_t* const wbuf[3] = {w0, w1, w2};
+  uint8_t* const xbuf[3] = {x0, x1, x2};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wt = wave & 1;
+  const int r0 = blockIdx.x * kTileRows, t0 = blockIdx.y * kToks12;
+
+  for (int e = tid; e < 512; e += kGemmThreads) {
+    const uint32_t u = (uint32_t)e & 255u;
+    if (e < 256) T0[u] = ext_bits<uint64_t>(u);
+    else T1[u] = ext_bits<uint64_t>(u << 8);
+  }
+
+  // Row dr = tid / 2 of the tile; the two threads of a row decode its words 2h
+  // and 2h+1 of the step's group.  Out-of-range offsets read zeros (zero words
+  // decode to t = 0).
+  const int dr = tid >> 1, h = tid & 1;
+  const int row = r0 + dr;
+  const int nsteps = (a.nb + 3) / 4;
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.words, 0, (int)a.buf_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, (int)a.x_bytes, 0x00020000);
+  struct Group {
+    uint4 w;
+    uint32_t e;  // the group's exponent nibbles
+  };
+  auto load_w = [&](int ks) -> Group {
+    const int b0 = ks * 4;
+    const int p = b0 / kPanelBlocks;
+    const int Wps = (int)panel_stored_width(p, a.nb);
+    const int q0 = b0 - p * kPanelBlocks;
+    const bool ok = row < a.Mp && q0 < Wps;
+    const uint32_t off = ok ? (uint32_t)((p * a.Mp * kPanelBlocks + row * Wps + q0) * 4)
+                            : 0x80000000u;
+    const uint32_t eoff =
+        ok ? a.exp_off + (uint32_t)((p * a.Mp * (kPanelBlocks / 4) + row * (Wps / 4) + q0 / 4) * 2)
+           : 0x80000000u;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0);
+    Group g;
+    g.w = make_uint4(v[0], v[1], v[2], v[3]);
+    g.e = __builtin_amdgcn_raw_buffer_load_b16(wrs, eoff, 0, 0);
+    return g;
+  };
+  // X of a step straight into LDS: piece P (16 bytes) of the tile is chunk P % 7
+  // of token P / 7; chunk 6 is padding (an out-of-range load, zeros).
+  auto copy_x = [&](int ks, uint8_t* dst) {
+#pragma unroll
+    for (int i = 0; i < kX12Copies; ++i) {
+      const int P = (kX12Copies * wave + i) * 64 + lane;
+      const int tok = P / 7, c = P - 7 * tok;
+      const int col = ks * kStep12 + 8 * c;
+      const uint32_t off = (c < 6 && t0 + tok < a.ntok && col < a.cols)
+                               ? (uint32_t)((t0 + tok) * a.cols + col) * 2u
+                               : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, (__attribute__((address_space(3))) void*)(dst + (kX12Copies * wave + i) * 1024), 16,
+          off, 0, 0, 0);
+    }
+  };
+  // Word p of a group holds block (p + row) & 3 of the step (rotated groups);
+  // its 12 weights go to LDS as three 8-byte stores.
+  auto put_w = [&](uint8_t* dst, const Group& q) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int p = 2 * h + j;
+      const uint32_t w = h ? (j ? q.w.w : q.w.z) : (j ? q.w.y : q.w.x);
+      _Float16 o[12];
+      decode_c12(w, (q.e >> (4 * p)) & 15u, T0, T1, o);
+      const int slot = (p + row) & 3;
+      uint64_t* d = reinterpret_cast<uint64_t*>(dst + dr * kRow12 + slot * 24);
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        uint64_t v = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v |= (uint64_t)__builtin_bit_cast(uint16_t, o[4 * u + i]) << (16 * i);
+        d[u] = v;
+      }
+    }
+  };
+
+  f32x16 acc[2][kNTiles12];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int n = 0; n < kNTiles12; ++n)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[g][n][v] = 0.f;
+
+  const int arow = lane & 31, kq = lane >> 5;
+  auto mma = [&](const uint8_t* wb, const uint8_t* xb, uint8_t* wnext, const Group& qn) {
+    const uint8_t* wl = wb + (64 * wr + arow) * kRow12 + kq * 16;
+    const uint8_t* xl = xb + (kToks12 / 2 * wt + arow) * kRow12 + kq * 16;
+    half8 A[2][2], B[2][kNTiles12];
+    auto rd = [&](int s) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        A[s & 1][g] = *reinterpret_cast<const half8*>(wl + g * 32 * kRow12 + s * 32);
+#pragma unroll
+      for (int n = 0; n < kNTiles12; ++n)
+        B[s & 1][n] = *reinterpret_cast<const half8*>(xl + n * 32 * kRow12 + s * 32);
+    };
+    rd(0);
+#pragma unroll
+    for (int s = 0; s < kSlices12; ++s) {
+      if (s + 1 < kSlices12) rd(s + 1);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int n = 0; n < kNTiles12; ++n)
+          acc[g][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s & 1][g], B[s & 1][n], acc[g][n],
+                                                             0, 0, 0);
+    }
+    put_w(wnext, qn);
+  };
+
+  // Prologue: steps 0 and 1 in flight, step 0 decoded.
+  Group g3[3];
+  copy_x(0, xbuf[0]);
+  g3[0] = load_w(0);
+  copy_x(1, xbuf[1]);
+  g3[1] = load_w(1);
+  __syncthreads();  // T0/T1 ready (waits for all loads too)
+  put_w(wbuf[0], g3[0]);
+  __syncthreads();
+
+  // Step k (buffers k % 3): copies of step k + 2, MFMAs of step k, decode of
+  // step k + 1, then wait until only step k + 2's nine loads (7 X pieces, the
+  // word group, the exponent word) are in flight and meet at the barrier.
+  auto step = [&](int k, int b) {
+    const int b1 = b == 2 ? 0 : b + 1, b2 = b == 0 ? 2 : b - 1;
+    copy_x(k + 2, xbuf[b2]);
+    g3[b2] = load_w(k + 2);
+    mma(wbuf[b], xbuf[b], wbuf[b1], g3[b1]);
+    __builtin_amdgcn_s_waitcnt(0x0079);  // vmcnt(9) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int ks = 0; ks < nsteps; ks += 3) {
+    step(ks, 0);
+    step(ks + 1, 1);
+    step(ks + 2, 2);
+  }
+
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int n = 0; n < kNTiles12; ++n) {
+      const int tok = t0 + kToks12 / 2 * wt + 32 * n + arow;
+      if (tok >= a.ntok) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rb = r0 + 64 * wr + 32 * g + 8 * j + 4 * kq;
+        __half* dst = a.y + (int64_t)tok * a.rows + rb;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (rb + v < a.rows) dst[v] = __float2half_rn(acc[g][n][4 * j + v] * 0x1p-10f);
+      }
+    }
+}
+
 }  // namespace
 
 int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
                 hipStream_t s) {
-  if (h->C != 8 || xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
+  if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
+  if (h->C == 12) {
+    if (h->cols % 8 != 0 || (uintptr_t)x % 16 != 0) return SEEDLM_E_UNSUPPORTED;
+    if (h->bytes >= (1ULL << 31) || ntok * h->cols * 2 >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;
+    Gemm12Args a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
+                 static_cast<__half*>(y), (int)h->rows, (int)h->cols, (int)h->Mp, (int)h->nb,
+                 (int)ntok, (uint32_t)h->bytes, (uint32_t)h->exp_off, (uint32_t)(ntok * h->cols * 2)};
+    const dim3 grid((unsigned)((h->rows + kTileRows - 1) / kTileRows),
+                    (unsigned)((ntok + kToks12 - 1) / kToks12));
+    hipLaunchKernelGGL(gemm_c12_kernel, grid, dim3(kGemmThreads), 0, s, a);
+    SEEDLM_HIP_CHECK(hipGetLastError());
+    return SEEDLM_OK;
+  }
+  if (h->C != 8) return SEEDLM_E_UNSUPPORTED;
   if (h->cols % 8 != 0 || (uintptr_t)x % 16 != 0) return SEEDLM_E_UNSUPPORTED;
   // 32-bit buffer offsets: the packed words and X must each stay below 2 GiB.
   if (h->nwords * 4 >= (1LL << 31) || ntok * h->cols * 2 >= (1LL << 31))

@@ -94,7 +94,7 @@ int launch_gemv_lut12_group(const seedlm_matrix* const* hs, const void* const* x
                             void* const* ys, int n, int xdt, int ydt, hipStream_t s, int phases);
 int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
                      hipStream_t s);
-// Prefill GEMM (4-bit, fp16 X and Y; E_UNSUPPORTED otherwise).
+// Prefill GEMM (both packed formats, fp16 X and Y; E_UNSUPPORTED otherwise).
 int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
                 hipStream_t s);
 int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,

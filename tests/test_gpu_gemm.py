@@ -1,4 +1,5 @@
-"""GPU prefill GEMM (seedlm_gemm, through the C ABI) against the CPU oracle.
+"""GPU prefill GEMM (seedlm_gemm, through the C ABI) against the CPU oracle, in
+both packed formats (4-bit C = 8, 3-bit C = 12).
 
 Y = X W^T with W from the oracle's float64 decode of the same records and X the
 same fp16 values.  Every token row of Y is a GEMV with fp16 output, so the bar
@@ -36,11 +37,11 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _run(cfg_id, rows, cols, ntok):
+def _run(cfg_id, rows, cols, ntok, C=8, P=3):
     dev = _dev()
     S = _S()
-    s, c, e = gen_records(cfg_id, 0, rows, cols, 8, 3)
-    m = S.seedlm_pack(s, c, e, rows, cols, 8, 3, 16)
+    s, c, e = gen_records(cfg_id, 0, rows, cols, C, P)
+    m = S.seedlm_pack(s, c, e, rows, cols, C, P, 16)
     X = gen_x(cfg_id, 0, ntok, cols, "f16")
     Xd = torch.from_numpy(X).to(dev)
     Y = torch.empty((ntok, rows), dtype=torch.float16, device=dev)
@@ -85,6 +86,55 @@ def test_gemm_full_shape_sampled():
     assert err <= TOL
 
 
+# 3-bit format (C = 12, P = 4): K steps of 48 columns (4 blocks) and 256-token
+# tiles.  cols = 8 mod 12 ends inside a block; nb = 1, 2, 3 mod 4 leave a short
+# last group (zero-padded slots); nb = 33, 37 leave a short last panel.
+@pytest.mark.parametrize("rows,cols,ntok", [
+    (200, 400, 300),   # 34 blocks (last one 4 columns short), two token tiles, ragged
+    (100, 48, 1),      # one K step, one token
+    (130, 440, 17),    # 37 blocks: row tile tail of 2 rows, 1-block last group
+    (8, 24, 5),        # two blocks
+    (1000, 2048, 513),  # 171 blocks (6 panels), ragged tokens
+    (300, 4096, 256),  # exactly one token tile
+])
+def test_gemm_3bit_matches_oracle_everywhere(rows, cols, ntok):
+    _say(f"gemm 3-bit {rows}x{cols} ntok={ntok}")
+    (s, c, e), X, Yg, *_ = _run(63, rows, cols, ntok, C=12, P=4)
+    W = O.decode_rows(s, c, e, cols, 12, 4)
+    Yr = X.astype(np.float64) @ W.T
+    err = _rowwise_err(Yg, Yr)
+    _say(f"  max per-token normwise error {err:.2e}")
+    assert err <= TOL
+
+
+def test_gemm_3bit_layer_shape_sampled():
+    """Llama-3-8B gate projection (14336x4096, 3-bit), 2048 tokens, sampled."""
+    rows, cols, ntok = 14336, 4096, 2048
+    _say(f"gemm 3-bit sampled {rows}x{cols} ntok={ntok}")
+    (s, c, e), X, Yg, *_ = _run(3, rows, cols, ntok, C=12, P=4)
+    rng = np.random.default_rng(4)
+    rs = np.concatenate([[0, rows - 1], rng.choice(rows, 30, replace=False)])
+    ts = np.concatenate([[0, ntok - 1], rng.choice(ntok, 14, replace=False)])
+    W = O.decode_rows(s[rs], c[rs], e[rs], cols, 12, 4)
+    Yr = X[ts].astype(np.float64) @ W.T
+    err = _rowwise_err(Yg[np.ix_(ts, rs)], Yr)
+    _say(f"  sampled max per-token normwise error {err:.2e}")
+    assert err <= TOL
+
+
+def test_gemm_3bit_matches_batched_gemv():
+    """For a few tokens the prefill GEMM and the skinny matrix-core GEMV compute
+    the same exact-decode products (fp32 accumulation, different order)."""
+    dev = _dev()
+    S = _S()
+    rows, cols, ntok = 520, 12 * 90 + 8, 16
+    (s, c, e), X, Yg, m, Xd, _ = _run(64, rows, cols, ntok, C=12, P=4)
+    Yb = torch.empty((ntok, rows), dtype=torch.float16, device=dev)
+    S.seedlm_gemv(m, Xd, Yb, batch=ntok)
+    torch.cuda.synchronize()
+    assert _rowwise_err(Yg, Yb.cpu().numpy().astype(np.float64)) <= TOL
+
+
 def test_gemm_deterministic_and_rejects_unsupported():
     dev = _dev()
     S = _S()
@@ -92,12 +142,17 @@ def test_gemm_deterministic_and_rejects_unsupported():
     S.seedlm_gemm(m, Xd, Y)
     torch.cuda.synchronize()
     assert np.array_equal(Y.cpu().numpy().astype(np.float64), Y1)
-    # fp32 activations, 3-bit format: not supported by this entry point
+    # fp32 activations: not supported by this entry point
     with pytest.raises(S.SeedLMError):
         S.seedlm_gemm(m, Xd.float(), Y)
-    s, c, e = gen_records(62, 1, 64, 96, 12, 4)
-    m3 = S.seedlm_pack(s, c, e, 64, 96, 12, 4, 16)
-    X3 = torch.zeros((8, 96), dtype=torch.float16, device=dev)
-    Y3 = torch.empty((8, 64), dtype=torch.float16, device=dev)
+    # 3-bit: deterministic too; cols not a multiple of 8 is rejected
+    _, _, Y3a, m3, X3, Y3 = _run(62, 300, 480, 260, C=12, P=4)
+    S.seedlm_gemm(m3, X3, Y3)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y3.cpu().numpy().astype(np.float64), Y3a)
+    s, c, e = gen_records(62, 1, 64, 100, 12, 4)
+    m4 = S.seedlm_pack(s, c, e, 64, 100, 12, 4, 16)
+    X4 = torch.zeros((8, 100), dtype=torch.float16, device=dev)
+    Y4 = torch.empty((8, 64), dtype=torch.float16, device=dev)
     with pytest.raises(S.SeedLMError):
-        S.seedlm_gemm(m3, X3, Y3)
+        S.seedlm_gemm(m4, X4, Y4)
