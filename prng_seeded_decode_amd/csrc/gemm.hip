@@ -253,21 +253,44 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
 }
 
 // The 3-bit format (C = 12, P = 4): the same scheme with a K step of 48 columns
-// (one 16-byte group = 4 blocks of 12) and 256-token tiles.  X and W rows of a
-// step are 96 bytes; in LDS they are padded to 112 bytes (7 chunks of 16), and
-// 7t mod 16 takes 16 distinct values over 16 consecutive tokens (and 7t mod 8
-// over 8), so operand reads are free of bank conflicts without a swizzle.
+// (one 16-byte group = 4 blocks of 12).  X and W rows of a step are 96 bytes =
+// 6 chunks of 16 in LDS, logical chunk c of row t at position (c + rot(t)) mod 6
+// with rot(t) = bit 2 ^ bit 3 of t: rows t and t+4 then put a chunk in opposite
+// halves of a 32-byte bank pair and rows t and t+8 or t+12 land 8 chunks
+// apart, so 16 consecutive rows read one chunk from 16 distinct 16-byte bank
+// groups (and any aligned 8 from 8 distinct ones of 128 bytes).
+//
+// Tiles: ROWS x TOKS per workgroup, two threads per W row (2 ROWS threads),
+// waves in a (ROWS / 64) x 2 grid of 64 rows x TOKS / 2 tokens each.  The X
+// slice of a step costs 96 TOKS bytes of copying and the decode 4 ROWS blocks,
+// for the same MFMA work when ROWS TOKS is fixed: copying X is the scarcer of
+// the two here, so large grids take 256 x 256 tiles (eight waves, two per
+// SIMD) and smaller grids 128 x 256 (four waves), which leaves more
+// workgroups.
+//
+// Pipeline over three buffers of each kind: in step k the word loads and the
+// X copy of step k+2 are issued, the MFMAs of step k run, and the decode of
+// step k+1 (into the next W buffer) is spread over them four weights at a
+// time; one wait for step k+1's X copy and one barrier end the step.
 // Each block's exponent nibble comes from the format's separate nibble array
 // (one u16 per group of four blocks, in the order of the group's words).
-constexpr int kStep12 = 48;                  // columns per K step
-constexpr int kSlices12 = kStep12 / 16;      // MFMAs of K = 16 per step
-constexpr int kRow12 = 112;                  // LDS bytes per X token row / W row
-constexpr int kToks12 = 256;                 // tokens per tile
-constexpr int kNTiles12 = kToks12 / 2 / 32;  // 32-token MFMA tiles per wave
-constexpr int kX12Bytes = kToks12 * kRow12;  // 28 KiB
-constexpr int kW12Bytes = kTileRows * kRow12;  // 14 KiB
-constexpr int kX12Copies = kX12Bytes / 1024 / 4;  // 1 KiB LDS copies per wave per step
-static_assert(kX12Bytes % 4096 == 0 && kX12Copies == 7, "X tile layout");
+constexpr int kStep12 = 48;                    // columns per K step
+constexpr int kSlices12 = kStep12 / 16;        // MFMAs of K = 16 per step
+constexpr int kRow12 = 96;                     // LDS bytes per X token row / W row
+
+__device__ inline int rot12(int t) { return ((t >> 2) ^ (t >> 3)) & 1; }
+
+template <int ROWS, int TOKS>
+struct Tile12 {
+  static constexpr int kThreads = 2 * ROWS;
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kNTiles = TOKS / 2 / 32;                // 32-token MFMA tiles per wave
+  static constexpr int kWBytes = ROWS * kRow12;
+  static constexpr int kXBytes = TOKS * kRow12;
+  static constexpr int kXCopies = kXBytes / 1024 / kWaves;     // 1 KiB LDS copies per wave per step
+  static_assert(kXCopies * 1024 * kWaves == kXBytes, "X tile layout");
+  static_assert(3 * (kWBytes + kXBytes) + 4096 <= 160 * 1024, "LDS");
+};
 
 struct Gemm12Args {
   const uint32_t* words;
@@ -277,17 +300,21 @@ struct Gemm12Args {
   uint32_t buf_bytes, exp_off, x_bytes;  // packed buffer size, exponent array offset, X size
 };
 
-__global__ void __launch_bounds__(kGemmThreads, 1) gemm_c12_kernel(const Gemm12Args a) {
+template <int ROWS, int TOKS>
+__global__ void __launch_bounds__(2 * ROWS, 1) gemm_c12_kernel(const Gemm12Args a) {
+  using TL = Tile12<ROWS, TOKS>;
+  constexpr int kNTiles = TL::kNTiles, kXBytes = TL::kXBytes, kWBytes = TL::kWBytes;
+  constexpr int kXCopies = TL::kXCopies, kThreads = TL::kThreads;
   __shared__ uint64_t T0[256], T1[256];
-  __shared__ __attribute__((aligned(16))) uint8_t w0[kW12Bytes], w1[kW12Bytes], w2[kW12Bytes];
-  __shared__ __attribute__((aligned(16))) uint8_t x0[kX12Bytes], x1[kX12Bytes], x2[kX12Bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t w0[kWBytes], w1[kWBytes], w2[kWBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t x0[kXBytes], x1[kXBytes], x2[kXBytes];
   uint8_t* const wbuf[3] = {w0, w1, w2};
   uint8_t* const xbuf[3] = {x0, x1, x2};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wt = wave & 1;
-  const int r0 = blockIdx.x * kTileRows, t0 = blockIdx.y * kToks12;
+  const int r0 = blockIdx.x * ROWS, t0 = blockIdx.y * TOKS;
 
-  for (int e = tid; e < 512; e += kGemmThreads) {
+  for (int e = tid; e < 512; e += kThreads) {
     const uint32_t u = (uint32_t)e & 255u;
     if (e < 256) T0[u] = ext_bits<uint64_t>(u);
     else T1[u] = ext_bits<uint64_t>(u << 8);
@@ -324,111 +351,170 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c12_kernel(const Gemm12A
     g.e = __builtin_amdgcn_raw_buffer_load_b16(wrs, eoff, 0, 0);
     return g;
   };
-  // X of a step straight into LDS: piece P (16 bytes) of the tile is chunk P % 7
-  // of token P / 7; chunk 6 is padding (an out-of-range load, zeros).
-  auto copy_x = [&](int ks, uint8_t* dst) {
+  // X of a step straight into LDS: copy i of this wave fills the 16-byte pieces
+  // P = (kXCopies wave + i) * 64 + lane, i.e. position P % 6 of token P / 6,
+  // which holds chunk (P % 6 - rot(token)) mod 6.  The X offsets of the pieces
+  // move by 96 bytes per step, so they are worked out once; xc = 8 * chunk is
+  // the column inside the step (INT_MAX for tokens past the end).
+  uint32_t xo[kXCopies];
+  int xc[kXCopies];
 #pragma unroll
-    for (int i = 0; i < kX12Copies; ++i) {
-      const int P = (kX12Copies * wave + i) * 64 + lane;
-      const int tok = P / 7, c = P - 7 * tok;
-      const int col = ks * kStep12 + 8 * c;
-      const uint32_t off = (c < 6 && t0 + tok < a.ntok && col < a.cols)
-                               ? (uint32_t)((t0 + tok) * a.cols + col) * 2u
-                               : 0x80000000u;
+  for (int i = 0; i < kXCopies; ++i) {
+    const int P = (kXCopies * wave + i) * 64 + lane;
+    const int tok = P / 6, pos = P - 6 * tok;
+    const int c = pos >= rot12(tok) ? pos - rot12(tok) : pos + 5;
+    const bool ok = t0 + tok < a.ntok;
+    xo[i] = ok ? (uint32_t)((t0 + tok) * a.cols + 8 * c) * 2u : 0u;
+    xc[i] = ok ? 8 * c : 0x7FFFFFFF;
+  }
+  const int xwave = __builtin_amdgcn_readfirstlane(kXCopies * wave);
+  auto copy_x = [&](int ks, uint8_t* dst) {
+    const int lim = a.cols - ks * kStep12;
+#pragma unroll
+    for (int i = 0; i < kXCopies; ++i) {
+      const uint32_t off = xc[i] < lim ? xo[i] + (uint32_t)(ks * kStep12 * 2) : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrs, (__attribute__((address_space(3))) void*)(dst + (kX12Copies * wave + i) * 1024), 16,
-          off, 0, 0, 0);
+          xrs, (__attribute__((address_space(3))) void*)(dst + (xwave + i) * 1024), 16, off, 0, 0,
+          0);
     }
   };
-  // Word p of a group holds block (p + row) & 3 of the step (rotated groups);
-  // its 12 weights go to LDS as three 8-byte stores.
-  auto put_w = [&](uint8_t* dst, const Group& q) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int p = 2 * h + j;
-      const uint32_t w = h ? (j ? q.w.w : q.w.z) : (j ? q.w.y : q.w.x);
-      _Float16 o[12];
-      decode_c12(w, (q.e >> (4 * p)) & 15u, T0, T1, o);
-      const int slot = (p + row) & 3;
-      uint64_t* d = reinterpret_cast<uint64_t*>(dst + dr * kRow12 + slot * 24);
-#pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        uint64_t v = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v |= (uint64_t)__builtin_bit_cast(uint16_t, o[4 * u + i]) << (16 * i);
-        d[u] = v;
-      }
-    }
+  // Word 2h + j of a group holds block (2h + j + row) & 3 of the step (rotated
+  // groups); weights 4q .. 4q+3 of that block are logical bytes 24 slot + 8q of
+  // the W row, stored as one 8-byte write at their rotated chunk.
+  const int rd = rot12(dr);
+  auto w_addr = [&](uint8_t* dst, int j, int q) -> uint64_t* {
+    const int slot = (2 * h + j + dr) & 3;
+    const int b = 24 * slot + 8 * q;
+    int c = (b >> 4) + rd;
+    c = c >= 6 ? c - 6 : c;
+    return reinterpret_cast<uint64_t*>(dst + dr * kRow12 + c * 16 + (b & 15));
+  };
+  auto mine = [&](const Group& q, int j) -> uint32_t {  // word 2h + j of the group
+    return h ? (j ? q.w.w : q.w.z) : (j ? q.w.y : q.w.x);
+  };
+  auto setup = [&](const Group& q, int j) {
+    return dec12_setup(mine(q, j), q.e >> (8 * h + 4 * j) & 15u, T0, T1);
   };
 
-  f32x16 acc[2][kNTiles12];
+  f32x16 acc[2][kNTiles];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int n = 0; n < kNTiles12; ++n)
+    for (int n = 0; n < kNTiles; ++n)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[g][n][v] = 0.f;
 
+  // Operand reads: lane l takes A row / B token l % 32 and the 8 columns of
+  // chunk 2s + l / 32 of slice s, at that row's rotated position.
   const int arow = lane & 31, kq = lane >> 5;
+  int po[kSlices12];
+#pragma unroll
+  for (int s = 0; s < kSlices12; ++s) {
+    const int c = 2 * s + kq + rot12(arow);
+    po[s] = (c >= 6 ? c - 6 : c) * 16;
+  }
+  // MFMAs of one step, with the decode of the next step's two blocks spread
+  // over the three slices (quads 0, 1 of block 0; quad 2 of block 0 and quad 0
+  // of block 1; quads 1, 2 of block 1), alternating one MFMA with a few VALU
+  // instructions.
   auto mma = [&](const uint8_t* wb, const uint8_t* xb, uint8_t* wnext, const Group& qn) {
-    const uint8_t* wl = wb + (64 * wr + arow) * kRow12 + kq * 16;
-    const uint8_t* xl = xb + (kToks12 / 2 * wt + arow) * kRow12 + kq * 16;
-    half8 A[2][2], B[2][kNTiles12];
-    auto rd = [&](int s) {
+    Dec12 d0 = setup(qn, 0);
+    Dec12 d1 = setup(qn, 1);
+    const uint8_t* wl = wb + (64 * wr + arow) * kRow12;
+    const uint8_t* xl = xb + (TOKS / 2 * wt + arow) * kRow12;
+    half8 A[2][2], B[2][kNTiles];
+    auto rd_ops = [&](int s) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
-        A[s & 1][g] = *reinterpret_cast<const half8*>(wl + g * 32 * kRow12 + s * 32);
+        A[s & 1][g] = *reinterpret_cast<const half8*>(wl + g * 32 * kRow12 + po[s]);
 #pragma unroll
-      for (int n = 0; n < kNTiles12; ++n)
-        B[s & 1][n] = *reinterpret_cast<const half8*>(xl + n * 32 * kRow12 + s * 32);
+      for (int n = 0; n < kNTiles; ++n)
+        B[s & 1][n] = *reinterpret_cast<const half8*>(xl + n * 32 * kRow12 + po[s]);
     };
-    rd(0);
+    rd_ops(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < kSlices12; ++s) {
-      if (s + 1 < kSlices12) rd(s + 1);
+      if (s + 1 < kSlices12) rd_ops(s + 1);
+      if (s < 2) dec12_pin(d0);
+      if (s > 0) dec12_pin(d1);
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int n = 0; n < kNTiles12; ++n)
+        for (int n = 0; n < kNTiles; ++n)
           acc[g][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s & 1][g], B[s & 1][n], acc[g][n],
                                                              0, 0, 0);
+      if (s == 0) {
+        *w_addr(wnext, 0, 0) = dec12_quad<0>(d0);
+        *w_addr(wnext, 0, 1) = dec12_quad<4>(d0);
+      } else if (s == 1) {
+        *w_addr(wnext, 0, 2) = dec12_quad<8>(d0);
+        *w_addr(wnext, 1, 0) = dec12_quad<0>(d1);
+      } else {
+        *w_addr(wnext, 1, 1) = dec12_quad<4>(d1);
+        *w_addr(wnext, 1, 2) = dec12_quad<8>(d1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 + kNTiles, 0);
+#pragma unroll
+      for (int m = 0; m < 2 * kNTiles; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 96 / (2 * kNTiles), 0);  // then VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);  // slices stay in order
     }
-    put_w(wnext, qn);
   };
 
-  // Prologue: steps 0 and 1 in flight, step 0 decoded.
-  Group g3[3];
+  // Prologue: the words and X of steps 0 and 1 in flight; step 0 decoded.
+  Group gq[3];
+  gq[0] = load_w(0);
+  gq[1] = load_w(1);
   copy_x(0, xbuf[0]);
-  g3[0] = load_w(0);
   copy_x(1, xbuf[1]);
-  g3[1] = load_w(1);
   __syncthreads();  // T0/T1 ready (waits for all loads too)
-  put_w(wbuf[0], g3[0]);
+  {
+    const Dec12 d0 = setup(gq[0], 0);
+    const Dec12 d1 = setup(gq[0], 1);
+    *w_addr(wbuf[0], 0, 0) = dec12_quad<0>(d0);
+    *w_addr(wbuf[0], 0, 1) = dec12_quad<4>(d0);
+    *w_addr(wbuf[0], 0, 2) = dec12_quad<8>(d0);
+    *w_addr(wbuf[0], 1, 0) = dec12_quad<0>(d1);
+    *w_addr(wbuf[0], 1, 1) = dec12_quad<4>(d1);
+    *w_addr(wbuf[0], 1, 2) = dec12_quad<8>(d1);
+  }
   __syncthreads();
 
-  // Step k (buffers k % 3): copies of step k + 2, MFMAs of step k, decode of
-  // step k + 1, then wait until only step k + 2's nine loads (7 X pieces, the
-  // word group, the exponent word) are in flight and meet at the barrier.
+  // Step k (buffers b = k % 3, b1 = (k+1) % 3, b2 = (k+2) % 3): the word
+  // loads of step k+2 into gq[b2] (whose words were decoded in step k-1) and
+  // the X copy of step k+2 into xbuf[b2] (read in step k-1, before the last
+  // barrier); MFMAs of step k with step k+1 decoded into wbuf[b1]; then wait
+  // until step k+1's X copy has landed and meet at the barrier.  vmcnt counts
+  // in issue order: the word loads go before the copy, so that the compiler's
+  // own wait for the words decoded in step k+1 does not also wait for step
+  // k+2's copy, and the final wait leaves only step k+2's loads in flight.
   auto step = [&](int k, int b) {
     const int b1 = b == 2 ? 0 : b + 1, b2 = b == 0 ? 2 : b - 1;
+    gq[b2] = load_w(k + 2);
+    __builtin_amdgcn_sched_barrier(0);
     copy_x(k + 2, xbuf[b2]);
-    g3[b2] = load_w(k + 2);
-    mma(wbuf[b], xbuf[b], wbuf[b1], g3[b1]);
-    __builtin_amdgcn_s_waitcnt(0x0079);  // vmcnt(9) expcnt(7) lgkmcnt(0)
+    mma(wbuf[b], xbuf[b], wbuf[b1], gq[b1]);
+    __builtin_amdgcn_s_waitcnt(0x0070 | (kXCopies + 2));  // vmcnt(kXCopies + 2) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
   };
+  // Whole rounds of three steps (one loop exit); steps past the end multiply
+  // zeros.
   for (int ks = 0; ks < nsteps; ks += 3) {
     step(ks, 0);
     step(ks + 1, 1);
     step(ks + 2, 2);
   }
 
+  // Y[t][r]: lane holds token 32n + l%32 and rows 32g + 8j + 4(l/32) + v.
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int n = 0; n < kNTiles12; ++n) {
-      const int tok = t0 + kToks12 / 2 * wt + 32 * n + arow;
+    for (int n = 0; n < kNTiles; ++n) {
+      const int tok = t0 + TOKS / 2 * wt + 32 * n + arow;
       if (tok >= a.ntok) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -439,6 +525,12 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c12_kernel(const Gemm12A
           if (rb + v < a.rows) dst[v] = __float2half_rn(acc[g][n][4 * j + v] * 0x1p-10f);
       }
     }
+}
+
+template <int ROWS, int TOKS>
+void launch_c12(const Gemm12Args& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.rows + ROWS - 1) / ROWS), (unsigned)((a.ntok + TOKS - 1) / TOKS));
+  hipLaunchKernelGGL((gemm_c12_kernel<ROWS, TOKS>), grid, dim3(2 * ROWS), 0, s, a);
 }
 
 }  // namespace
@@ -452,9 +544,10 @@ int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, in
     Gemm12Args a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
                  static_cast<__half*>(y), (int)h->rows, (int)h->cols, (int)h->Mp, (int)h->nb,
                  (int)ntok, (uint32_t)h->bytes, (uint32_t)h->exp_off, (uint32_t)(ntok * h->cols * 2)};
-    const dim3 grid((unsigned)((h->rows + kTileRows - 1) / kTileRows),
-                    (unsigned)((ntok + kToks12 - 1) / kToks12));
-    hipLaunchKernelGGL(gemm_c12_kernel, grid, dim3(kGemmThreads), 0, s, a);
+    // 256 x 256 tiles where they give every compute unit a workgroup
+    const int64_t big = ((h->rows + 255) / 256) * ((ntok + 255) / 256);
+    if (big >= device_cu_count()) launch_c12<256, 256>(a, s);
+    else launch_c12<128, 256>(a, s);
     SEEDLM_HIP_CHECK(hipGetLastError());
     return SEEDLM_OK;
   }

@@ -53,6 +53,63 @@ __device__ inline half8 decode_c8(uint32_t w, const uint32_t* T0, const uint32_t
   return decode_c8_ext(w, ext_c8(w, T0, T1));
 }
 
+// Decode state of a 3-bit block: its stream bits 0..63, coefficients, the
+// offset term and the scale.  dec12_quad then produces the weights four at a
+// time, so that a caller can spread one block's decode over other work.
+struct Dec12 {
+  uint32_t s0, s1, s2;  // stream bits 0..31, 16..47, 32..63
+  int t[4];
+  int base;             // -2^15 (t0 + t1 + t2 + t3)
+  float sc;
+};
+
+__device__ inline Dec12 dec12_setup(uint32_t w, uint32_t g, const uint64_t* T0,
+                                    const uint64_t* T1) {
+  Dec12 d;
+  const uint64_t ext = T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];  // stream bits 16..79
+  d.s0 = (w & 0xFFFFu) | ((uint32_t)ext << 16);
+  d.s1 = (uint32_t)ext;
+  d.s2 = (uint32_t)(ext >> 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) d.t[j] = ((int)(w << (12 - 4 * j))) >> 28;
+  d.base = -32768 * (d.t[0] + d.t[1] + d.t[2] + d.t[3]);
+  d.sc = block_scale(g);
+  return d;
+}
+
+// Ties a block's decode state to this point of the program: the compiler must
+// assume the stream words, offset and scale change here, so weights computed
+// from them are not moved above it (and the scheduler can interleave them with
+// the MFMAs that follow).  The coefficients stay out of it, so that the
+// compiler still knows they are 4-bit and multiplies with v_mul_i32_i24.
+// Emits no instruction.
+__device__ inline void dec12_pin(Dec12& d) {
+  asm volatile("" : "+v"(d.s0), "+v"(d.s1), "+v"(d.s2), "+v"(d.base), "+v"(d.sc));
+}
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+// fp16 weights I0 .. I0+3 (x 2^10) of a decoded block, lowest column in the low
+// 16 bits.
+template <int I0>
+__device__ inline uint64_t dec12_quad(const Dec12& d) {
+  half4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = I0 + k;
+    int I = d.base;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = 12 * j + i;  // state index, window b[n .. n+15]
+      const int z = n <= 16 ? (int)ubfe(d.s0, n, 16)
+                            : (n <= 32 ? (int)ubfe(d.s1, n - 16, 16) : (int)ubfe(d.s2, n - 32, 16));
+      I += d.t[j] * z;
+    }
+    o[k] = (_Float16)((float)I * d.sc);
+  }
+  return __builtin_bit_cast(uint64_t, o);
+}
+
 // Twelve fp16 weights (x 2^10) of a 3-bit block, written to o[0..11].
 __device__ inline void decode_c12(uint32_t w, uint32_t g, const uint64_t* T0, const uint64_t* T1,
                                   _Float16* o) {
