@@ -12,8 +12,9 @@ rotated so that consecutive steps do not find their weights in the 256 MB MALL.
 
 Prints one JSON line: effective weights/s (value), compressed HBM GB/s and its
 fraction of 8 TB/s, the roofline of the fused kernel (HIP events on the launch
-stream), the same-chip fp16 GEMV baseline and its speed-up, and the CPU oracle
-timed on a bounded sample of the same workload.
+stream), the measured streaming-read ceiling of the device and the kernel's
+fraction of it, the same-chip fp16 GEMV baseline and its speed-up, and the CPU
+oracle timed on a bounded sample of the same workload.
 
     python bench.py --encode [--encode-bits 4|3] [--steps K] [--warmup W]
 
@@ -86,6 +87,8 @@ def parse_args():
     p.add_argument("--copies", type=int, default=2)
     p.add_argument("--no-fp16", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-read-ceiling", action="store_true",
+                   help="skip the streaming-read ceiling measurement")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--per-matrix", action="store_true",
                    help="also time one seedlm_gemv per matrix (extra launches of the same kernels)")
@@ -708,6 +711,29 @@ def main():
                 "speedup_vs_best_fp16": round(best / ms_per_step, 3)}
         del Ws
 
+    # ---- measured streaming-read ceiling: a plain 16-byte-load read of a 2 GiB
+    # buffer (8x the 256 MB MALL), the rate a bandwidth-bound kernel can approach
+    ceiling = None
+    if not args.no_read_ceiling:
+        rb = torch.zeros(2 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(S.STREAM_READ_SINK, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            S.seedlm_stream_read(rb, sink, stream=stream)
+        torch.cuda.synchronize()
+        rev = []
+        for _ in range(10):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            S.seedlm_stream_read(rb, sink, stream=stream)
+            b.record(stream)
+            rev.append((a, b))
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(b) for a, b in rev])) * 1e-3
+        ceiling = {"GBps": round(rb.numel() / t / 1e9, 1), "buffer_bytes": rb.numel(),
+                   "kernel": "seedlm_stream_read: contiguous range per workgroup, 16-byte loads"}
+        del rb, sink
+
     decode = None
     if args.decode:
         # seedlm_decode of the largest matrix into a dense fp32 W: reads the packed
@@ -774,6 +800,8 @@ def main():
                         else None),
         },
         "fp16_baseline": fp16,
+        "read_ceiling": ceiling,
+        "pct_read_ceiling": (round(100 * float(achieved) / ceiling["GBps"], 2) if ceiling else None),
     }
     if decode:
         out["decode"] = decode

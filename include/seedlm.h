@@ -224,6 +224,23 @@ SEEDLM_API int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t r
                                 int64_t cols, int batch, void* stream);
 
 /*
+ * seedlm_stream_read -- measurement baseline, not part of the method: reads
+ * `bytes` of device memory at `buf` once with 16-byte loads (a plain streaming
+ * read; on a buffer larger than the last-level cache its rate is the HBM read
+ * ceiling a bandwidth-bound kernel can approach on this device) and folds the
+ * data into per-workgroup XOR checksums.
+ *   buf   device memory, 16-byte aligned; bytes > 0 and a multiple of 16
+ *   sink  device uint32[SEEDLM_STREAM_READ_SINK], caller-owned; the launch
+ *         writes one checksum per workgroup into its leading entries (at most
+ *         all of them) and leaves the rest untouched, so the XOR of a sink that
+ *         started at zero equals the XOR of the buffer's 32-bit words
+ * Asynchronous on `stream`.  Errors: SEEDLM_E_INVALID (null pointer, size or
+ * alignment), SEEDLM_E_DEVICE (launch failure).
+ */
+#define SEEDLM_STREAM_READ_SINK 8192
+SEEDLM_API int seedlm_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
  * seedlm_gemm -- Y = X W^T for any number of activation rows (prefill), with W
  * rebuilt from the handle's records inside the kernel and never stored in HBM
  * (paperhub.cn rebuttal text before Eq. (1): weights are reconstructed on the

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     F32,
     MAX_BATCH,
     OK,
+    STREAM_READ_SINK,
     VARIANT_AUTO,
     VARIANT_MFMA,
     VARIANT_LUT,
@@ -33,5 +34,6 @@ from ._binding import (  # noqa: F401
     seedlm_gemv_many,
     seedlm_pack,
     seedlm_pack_host,
+    seedlm_stream_read,
     status_string,
 )

@@ -41,6 +41,7 @@ EXPORTED = (
     "seedlm_export",
     "seedlm_status_string",
     "seedlm_fp16_gemv",
+    "seedlm_stream_read",
     "seedlm_gemm",
     "seedlm_encoder_create",
     "seedlm_encoder_destroy",
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
     L.seedlm_status_string.argtypes = [i32]
     L.seedlm_status_string.restype = ctypes.c_char_p
     L.seedlm_fp16_gemv.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    L.seedlm_stream_read.argtypes = [vp, i64, vp, vp]
     L.seedlm_gemm.argtypes = [vp, vp, vp, i64, i32, i32, vp]
     L.seedlm_encoder_create.argtypes = [i32, i32, i32, i32, ctypes.POINTER(vp)]
     L.seedlm_encoder_destroy.argtypes = [vp]
@@ -287,6 +289,23 @@ def seedlm_export(m: SeedLMMatrix) -> bytes:
     _check(lib().seedlm_export(m.handle, ctypes.cast(buf, ctypes.c_void_p), ctypes.byref(n)),
            "seedlm_export")
     return buf.raw[: n.value]
+
+
+STREAM_READ_SINK = 8192
+
+
+def seedlm_stream_read(buf, sink, stream=None):
+    """Baseline: read the device tensor buf once (plain streaming read) and write
+    per-workgroup XOR checksums into sink (device int32[STREAM_READ_SINK])."""
+    if not (buf.is_cuda and sink.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf and sink must be device tensors, buf contiguous")
+    if sink.numel() * sink.element_size() < 4 * STREAM_READ_SINK:
+        raise ValueError("sink must hold STREAM_READ_SINK 32-bit words")
+    _check(lib().seedlm_stream_read(ctypes.c_void_p(buf.data_ptr()),
+                                    buf.numel() * buf.element_size(),
+                                    ctypes.c_void_p(sink.data_ptr()), _stream_ptr(stream)),
+           "seedlm_stream_read")
+    return sink
 
 
 def seedlm_fp16_gemv(W, x, y, batch=None, stream=None):

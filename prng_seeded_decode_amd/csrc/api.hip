@@ -161,6 +161,12 @@ int seedlm_decode(seedlm_handle h, float* W_out, void* stream) {
   return launch_decode(h, W_out, static_cast<hipStream_t>(stream));
 }
 
+int seedlm_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes <= 0 || bytes % 16 != 0 || (uintptr_t)buf % 16 != 0)
+    return SEEDLM_E_INVALID;
+  return launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
+}
+
 int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,
                      int batch, void* stream) {
   if (!W || !x || !y || rows <= 0 || cols <= 0 || cols % 8 != 0) return SEEDLM_E_INVALID;

@@ -97,6 +97,7 @@ int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, 
 // Prefill GEMM (both packed formats, fp16 X and Y; E_UNSUPPORTED otherwise).
 int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
                 hipStream_t s);
+int launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,
                      int batch, hipStream_t s);
 int build_ext_table(seedlm_matrix* h);

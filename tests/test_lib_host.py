@@ -102,6 +102,11 @@ def test_device_entry_points_reject_null_handles_without_touching_the_gpu():
     assert L.seedlm_fp16_gemv(None, x, x, 4, 8, 1, None) == S.E_INVALID
     assert L.seedlm_fp16_gemv(x, x, x, 4, 12, 1, None) == S.E_INVALID
     assert L.seedlm_gemm(None, x, x, 4, S.F16, S.F16, None) == S.E_INVALID
+    assert L.seedlm_stream_read(None, 16, x, None) == S.E_INVALID
+    assert L.seedlm_stream_read(x, 16, None, None) == S.E_INVALID
+    assert L.seedlm_stream_read(x, 0, x, None) == S.E_INVALID
+    assert L.seedlm_stream_read(x, 24, x, None) == S.E_INVALID
+    assert L.seedlm_stream_read(ctypes.c_void_p(8), 16, x, None) == S.E_INVALID
     h = ctypes.c_void_p()
     assert L.seedlm_encoder_create(8, 5, 16, 4, ctypes.byref(h)) == S.E_UNSUPPORTED
     assert L.seedlm_encoder_create(12, 3, 16, 4, ctypes.byref(h)) == S.E_UNSUPPORTED
