@@ -252,7 +252,7 @@ SEEDLM_API int seedlm_stream_read(const void* buf, int64_t bytes, uint32_t* sink
  *   ntok >= 1.  Both packed formats (C = 8 and C = 12) with cols a multiple of
  *   8, fp16 X and Y only; other dtypes return SEEDLM_E_UNSUPPORTED (for up to
  *   16 rows seedlm_gemv covers them), as do X or the packed buffer of 2 GiB or
- *   more.
+ *   more and ntok above 16,776,960.
  * Asynchronous on `stream`; no workspace, so calls may overlap.
  * Errors: SEEDLM_E_INVALID (null, ntok < 1), SEEDLM_E_UNSUPPORTED (format,
  * dtype, alignment), SEEDLM_E_DEVICE (launch failure).

@@ -538,6 +538,8 @@ void launch_c12(const Gemm12Args& a, hipStream_t s) {
 int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
                 hipStream_t s) {
   if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
+  // token tiles go on grid.y, which holds at most 65535 workgroups
+  if ((ntok + 255) / 256 > 65535) return SEEDLM_E_UNSUPPORTED;
   if (h->C == 12) {
     if (h->cols % 8 != 0 || (uintptr_t)x % 16 != 0) return SEEDLM_E_UNSUPPORTED;
     if (h->bytes >= (1ULL << 31) || ntok * h->cols * 2 >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;

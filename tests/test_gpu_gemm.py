@@ -9,6 +9,8 @@ block-group and token tails included, for both token tilings: 256 tokens per
 workgroup on small grids, 512 on large ones); the full 8192x8192, 2048-token
 shape on sampled rows and tokens, which the oracle computes one by one.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -156,3 +158,9 @@ def test_gemm_deterministic_and_rejects_unsupported():
     Y4 = torch.empty((8, 64), dtype=torch.float16, device=dev)
     with pytest.raises(S.SeedLMError):
         S.seedlm_gemm(m4, X4, Y4)
+    # more token tiles than grid.y holds: rejected before any launch (the
+    # pointers are never read)
+    for mm in (m, m3):
+        assert S.lib().seedlm_gemm(mm.handle, ctypes.c_void_p(Xd.data_ptr()),
+                                   ctypes.c_void_p(Y.data_ptr()), 65535 * 256 + 1, S.F16, S.F16,
+                                   None) == S.E_UNSUPPORTED
