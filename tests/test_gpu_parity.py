@@ -296,22 +296,24 @@ def test_gemv_many_rejects_a_repeated_handle():
         S.seedlm_gemv_many([m, m], [x, x], ys)
 
 
-def test_full_layer_gemv_many_sampled():
-    # The launch configuration the benchmark times: the 70B layer in one call.
+@pytest.mark.parametrize("cid", [4, 3, 2], ids=["llama3_70b_4bit", "llama3_8b_3bit",
+                                                "llama2_7b_4bit"])
+def test_full_layer_gemv_many_sampled(cid):
+    # The launch configuration the benchmark times: a whole layer in one call.
     S = _S()
     dev = _dev()
-    cfg = CONFIGS[4]
+    cfg = CONFIGS[cid]
     mats, recs, xs, ys = [], [], [], []
     for mid, mat in enumerate(cfg.matrices):
-        s, c, e = gen_records(4, mid, mat.rows, mat.cols, cfg.C, cfg.P)
+        s, c, e = gen_records(cid, mid, mat.rows, mat.cols, cfg.C, cfg.P)
         mats.append(_pack(s, c, e, mat.rows, mat.cols, cfg.C, cfg.P))
-        rng = np.random.default_rng([4, mid, 888])
+        rng = np.random.default_rng([cid, mid, 888])
         pick = _sample_rows(mat.rows, rng, n=8)
         recs.append((pick, O.decode_rows(s[pick], c[pick], e[pick], mat.cols, cfg.C, cfg.P)))
-        x = gen_x(4, mid, 1, mat.cols, "f16")
+        x = gen_x(cid, mid, 1, mat.cols, "f16")
         xs.append(x)
         ys.append(torch.empty((1, mat.rows), dtype=torch.float16, device=dev))
-    _say("gemv_many over the Llama-3-70B layer")
+    _say(f"gemv_many over the {cfg.name} layer")
     S.seedlm_gemv_many(mats, [torch.from_numpy(x).to(dev) for x in xs], ys)
     torch.cuda.synchronize()
     for (pick, W_ref), x, y in zip(recs, xs, ys):
