@@ -20,14 +20,16 @@
 // to six MFMAs, 8 weights each.  Any assignment of blocks to k groups is a
 // valid MFMA as long as A and B agree; B (x) is read from LDS to match.
 //
-// Rows: a wave owns 64 rows r0..r0+63 (r0 a multiple of 8) and runs four MFMA
-// row groups rho = 0..3 of 16 rows {r0 + rho + 4i}.  The packed layout rotates
-// each 4-slot group by (row mod 4); inside one row group that rotation is the
-// same for all 16 rows, so a k group holds the same block for every row and the
-// shared B operand is right.
+// Rows: a row group is 16 rows {row0 + rho + 4i}; the packed layout rotates
+// each 4-slot group by (row mod 4) = rho, which is the same for all 16 rows,
+// so a k group holds the same block for every row and the shared B operand is
+// right.  Two tilings: a wave runs four row groups over its own 64 rows
+// (256-row tiles), or one row group, the four waves covering 64 rows
+// (64-row tiles, four times the workgroups for matrices too small to fill
+// the GPU otherwise).
 //
-// Work split: a workgroup (4 waves, 256 rows) takes a contiguous chunk of
-// panels; chunks write fp32 partials into the handle's workspace and
+// Work split: a workgroup (4 waves, 256 or 64 rows) takes a contiguous chunk
+// of panels; chunks write fp32 partials into the handle's workspace and
 // reduce_chunks_kernel adds them in a fixed order (deterministic).  With a
 // single chunk the kernel writes y directly.
 #include <hip/hip_fp16.h>
@@ -39,9 +41,9 @@
 namespace seedlm {
 namespace {
 
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
@@ -77,10 +79,13 @@ struct MfmaArgs {
   int tiles, chunk_panels, chunks;
 };
 
-template <int C>
-__global__ void __launch_bounds__(kThreads)
+template <int C, int RW>
+__global__ void __launch_bounds__(kThreads, 4)
 gemv_mfma_kernel(const MfmaArgs a) {
+  static_assert(RW == 1 || RW == 4, "row groups per wave");
   using F = Fmt<C>;
+  constexpr int kUnits = 2 * RW;             // units per panel and wave
+  constexpr int kPU = RW == 1 ? 2 : 1;       // panels per unrolled loop body
   using Ext = typename F::Ext;
   __shared__ Ext T0[256], T1[256];
   __shared__ __attribute__((aligned(16))) _Float16 xs[2][kBatchPad * F::kStride];
@@ -91,7 +96,11 @@ gemv_mfma_kernel(const MfmaArgs a) {
   const int chunk = (int)(blockIdx.x / (unsigned)a.tiles);
   const int pa = chunk * a.chunk_panels;
   const int pb = min(a.np, pa + a.chunk_panels);
-  const int r0 = tile * kRowsPerTile + wave * kRowsPerWave;  // multiple of 8
+  // Row group rr of this wave: rows row0 + rho + 4 i, i = 0..15, with rho =
+  // rr (four groups over 64 rows per wave) or the wave (one group per wave,
+  // 64-row tiles); row0 is a multiple of 64, so rho = row mod 4.
+  const int row0 = RW == 4 ? tile * 4 * kRowsPerWave + wave * kRowsPerWave : tile * 64;
+  auto rho_of = [&](int rr) { return RW == 4 ? rr : wave; };
   const int64_t Mp = a.Mp;
 
   for (int e = tid; e < 512; e += kThreads) {
@@ -100,26 +109,34 @@ gemv_mfma_kernel(const MfmaArgs a) {
     else T1[u] = ext_bits<Ext>(u << 8);
   }
 
-  // x staging: panel p's columns for batch rows 0..15 (zero outside x).
-  constexpr int kPer = kBatchPad * F::kCols / kThreads;  // halves per thread
-  _Float16 xr[kPer];
+  // x staging: thread t holds batch row t / 16 and the kPer consecutive panel
+  // columns (t % 16) kPer ..; buffer loads read zeros for padding rows (an
+  // out-of-range offset) and columns past the row's end are set to zero.
+  // Pairs are packed into 32-bit registers and stored as 16-byte writes.
+  constexpr int kPer = F::kCols / 16;  // halves per thread
+  static_assert(kThreads == 16 * kBatchPad && kPer % 8 == 0, "x staging layout");
+  const int xb = tid >> 4, xc0 = (tid & 15) * kPer;
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.x, 0, (int)((uint32_t)a.batch * (uint32_t)a.cols * 2u), 0x00020000);
+  uint32_t xr[kPer / 2];
   auto fetch_x = [&](int p) {
+    const int col0 = p * F::kCols + xc0;
+    const int lim = a.cols - col0;  // columns k < lim of this run lie inside the row
+    const uint32_t base = xb < a.batch ? (uint32_t)(xb * a.cols + col0) * 2u : 0x80000000u;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = tid + k * kThreads;
-      const int b = e / F::kCols, c = e % F::kCols;
-      const int64_t col = (int64_t)p * F::kCols + c;
-      xr[k] = (b < a.batch && col < a.cols)
-                  ? (_Float16)__half2float(a.x[(int64_t)b * a.cols + col])
-                  : (_Float16)0.f;
+    for (int k = 0; k < kPer; k += 2) {
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+          xrsrc, k < lim ? base + 2u * k : 0x80000000u, 0, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+          xrsrc, k + 1 < lim ? base + 2u * (k + 1) : 0x80000000u, 0, 0);
+      xr[k / 2] = (lo & 0xFFFFu) | (hi << 16);
     }
   };
   auto store_x = [&](int buf) {
+    uint4* dst = reinterpret_cast<uint4*>(&xs[buf][xb * F::kStride + xc0]);
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = tid + k * kThreads;
-      xs[buf][(e / F::kCols) * F::kStride + e % F::kCols] = xr[k];
-    }
+    for (int k = 0; k < kPer / 8; ++k)
+      dst[k] = make_uint4(xr[4 * k], xr[4 * k + 1], xr[4 * k + 2], xr[4 * k + 3]);
   };
   fetch_x(pa);
   store_x(pa & 1);
@@ -127,17 +144,17 @@ gemv_mfma_kernel(const MfmaArgs a) {
 
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.words, 0, (int)a.buf_bytes, 0x00020000);
-  floatx4 acc[4];
+  floatx4 acc[RW];
 #pragma unroll
-  for (int rho = 0; rho < 4; ++rho) acc[rho] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int rr = 0; rr < RW; ++rr) acc[rr] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Load unit k = 2*rho + h of panel p: the 16-byte record group (slots
-  // 4g .. 4g+3, g = 4h + q) of row r0 + rho + 4*i16, and its exponent nibbles
-  // (3-bit).  Units are loaded two ahead into a 4-slot ring; the ring crosses
-  // panel boundaries, and loads past the last panel read zeros.
+  // Load unit k = 2*rr + h of panel p: the 16-byte record group (slots
+  // 4g .. 4g+3, g = 4h + q) of row row0 + rho + 4*i16, and its exponent
+  // nibbles (3-bit).  Units are loaded two ahead into a 4-slot ring; the ring
+  // crosses panel boundaries, and loads past the last panel read zeros.
   auto unit_load = [&](int p, int k, v4u& wd, uint32_t& ev) {
-    const int rho = k >> 1, h = k & 1;
-    const int r = r0 + rho + 4 * i16;
+    const int rho = rho_of(k >> 1), h = k & 1;
+    const int r = row0 + rho + 4 * i16;
     const int g = 4 * h + q;
     const int Wp = (int)panel_stored_width(p, a.nb);
     const bool ok = p < pb && r < a.Mp && 4 * g < Wp;
@@ -156,7 +173,7 @@ gemv_mfma_kernel(const MfmaArgs a) {
     }
   };
   auto unit_compute = [&](const _Float16* xp, int k, const v4u wd, uint32_t ev) {
-    const int rho = k >> 1, h = k & 1;
+    const int rr = k >> 1, rho = rho_of(rr), h = k & 1;
     const int g = 4 * h + q;  // slot group of this lane: slots 4g .. 4g+3
     if constexpr (C == 8) {
 #pragma unroll
@@ -165,27 +182,31 @@ gemv_mfma_kernel(const MfmaArgs a) {
         const int slot = 4 * g + ((n + rho) & 3);
         const half8 A = decode_c8(wd[n], T0, T1);
         const half8 B = *reinterpret_cast<const half8*>(xp + 8 * slot);
-        acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rho], 0, 0, 0);
+        acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rr], 0, 0, 0);
       }
     } else {
-      _Float16 wv[48];
-#pragma unroll
-      for (int n = 0; n < 4; ++n) decode_c12(wd[n], (ev >> (4 * n)) & 0xFu, T0, T1, wv + 12 * n);
+      // The 48 weights of the four blocks in twelve quads of four; MFMA m takes
+      // quads 2m and 2m+1 (quad qd = weights 4 (qd % 3) .. +3 of block qd / 3)
+      // and the x columns of the same weights.  A block is set up when its
+      // first quad is needed, so at most two block states are live.
+      Dec12 d[2];
 #pragma unroll
       for (int m = 0; m < 6; ++m) {
-        half8 A, B;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) A[u] = wv[8 * m + u];
-        // x columns of weights 8m .. 8m+7: two runs of four inside blocks
+        u64x2 aq;
+        half4 bq[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int u = 8 * m + 4 * hh;
-          const int slot = 4 * g + ((u / 12 + rho) & 3);
-          const half4 xv = *reinterpret_cast<const half4*>(xp + 12 * slot + u % 12);
-#pragma unroll
-          for (int k2 = 0; k2 < 4; ++k2) B[4 * hh + k2] = xv[k2];
+          const int qd = 2 * m + hh, n = qd / 3, qq = qd % 3;
+          if (qq == 0) d[n & 1] = dec12_setup(wd[n], (ev >> (4 * n)) & 0xFu, T0, T1);
+          aq[hh] = qq == 0 ? dec12_quad<0>(d[n & 1])
+                           : (qq == 1 ? dec12_quad<4>(d[n & 1]) : dec12_quad<8>(d[n & 1]));
+          // word n of the group holds slot 4g + ((n + row) & 3), row = rho mod 4
+          const int slot = 4 * g + ((n + rho) & 3);
+          bq[hh] = *reinterpret_cast<const half4*>(xp + 12 * slot + 4 * qq);
         }
-        acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rho], 0, 0, 0);
+        const half8 A = __builtin_bit_cast(half8, aq);
+        const half8 B = __builtin_shufflevector(bq[0], bq[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[rr], 0, 0, 0);
       }
     }
   };
@@ -194,18 +215,26 @@ gemv_mfma_kernel(const MfmaArgs a) {
   uint32_t eRing[4];
   unit_load(pa, 0, ring[0], eRing[0]);
   unit_load(pa, 1, ring[1], eRing[1]);
-  for (int p = pa; p < pb; ++p) {
-    if (p + 1 < pb) fetch_x(p + 1);  // lands while this panel computes
-    const _Float16* xp = xs[p & 1] + i16 * F::kStride;
+  // kPU panels per loop body, so that the ring slot of every unit is known at
+  // compile time; a body's second panel is skipped when it lies past the chunk.
+  for (int p0 = pa; p0 < pb; p0 += kPU) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int kn = k + 2;
-      unit_load(kn < 8 ? p : p + 1, kn & 7, ring[kn & 3], eRing[kn & 3]);
-      unit_compute(xp, k, ring[k & 3], eRing[k & 3]);
-    }
-    if (p + 1 < pb) {
-      store_x((p + 1) & 1);
-      __syncthreads();
+    for (int pu = 0; pu < kPU; ++pu) {
+      const int p = p0 + pu;
+      if (pu == 0 || p < pb) {
+        if (p + 1 < pb) fetch_x(p + 1);  // lands while this panel computes
+        const _Float16* xp = xs[p & 1] + i16 * F::kStride;
+#pragma unroll
+        for (int k = 0; k < kUnits; ++k) {
+          const int kk = pu * kUnits + k, kn = k + 2;  // kk: unit index in the body
+          unit_load(p + kn / kUnits, kn % kUnits, ring[(kk + 2) & 3], eRing[(kk + 2) & 3]);
+          unit_compute(xp, k, ring[kk & 3], eRing[kk & 3]);
+        }
+        if (p + 1 < pb) {
+          store_x((p + 1) & 1);
+          __syncthreads();
+        }
+      }
     }
   }
 
@@ -213,12 +242,12 @@ gemv_mfma_kernel(const MfmaArgs a) {
   const int b = i16;
   if (b < a.batch) {
 #pragma unroll
-    for (int rho = 0; rho < 4; ++rho) {
+    for (int rr = 0; rr < RW; ++rr) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int r = r0 + rho + 4 * (4 * q + v);
+        const int r = row0 + rho_of(rr) + 4 * (4 * q + v);
         if (r < a.rows) {
-          const float val = acc[rho][v] * 0x1p-10f;
+          const float val = acc[rr][v] * 0x1p-10f;
           if (a.chunks == 1)
             a.y[(int64_t)b * a.rows + r] = __float2half_rn(val);
           else
@@ -266,7 +295,7 @@ int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, 
                      hipStream_t s) {
   if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
   if (batch < 1 || batch > kBatchPad) return SEEDLM_E_INVALID;
-  if (h->bytes >= 0x80000000ull || h->Mp >= (1 << 30) || h->cols >= (1LL << 31))
+  if (h->bytes >= 0x80000000ull || h->Mp >= (1 << 30) || (int64_t)batch * h->cols * 2 >= (1LL << 31))
     return SEEDLM_E_UNSUPPORTED;
   MfmaArgs a{};
   a.words = static_cast<const uint32_t*>(h->d_buf);
@@ -281,9 +310,13 @@ int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, 
   a.nb = (int)h->nb;
   a.np = (int)h->np;
   a.batch = batch;
-  a.tiles = (int)((h->Mp + kRowsPerTile - 1) / kRowsPerTile);
-  // Split the panels so that there are about four workgroups per CU.
+  // 256-row tiles (four row groups per wave) where they give about four
+  // workgroups per CU over the panels, 64-row tiles (one row group per wave)
+  // for the smaller matrices; then split the panels into chunks to reach that.
   const int64_t want = 4LL * device_cu_count();
+  const bool wide = ((h->Mp + kRowsPerTile - 1) / kRowsPerTile) * h->np >= want;
+  const int tile_rows = wide ? kRowsPerTile : 64;
+  a.tiles = (int)((h->Mp + tile_rows - 1) / tile_rows);
   int64_t chunks = (want + a.tiles - 1) / a.tiles;
   if (chunks < 1) chunks = 1;
   if (chunks > a.np) chunks = a.np;
@@ -291,10 +324,13 @@ int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, 
   a.chunks = (a.np + a.chunk_panels - 1) / a.chunk_panels;
   if ((size_t)a.chunks * batch * h->Mp * sizeof(float) > h->work_bytes) return SEEDLM_E_INVALID;
   const dim3 grid((unsigned)(a.tiles * a.chunks));
-  if (h->C == 8)
-    hipLaunchKernelGGL(gemv_mfma_kernel<8>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(gemv_mfma_kernel<12>, grid, dim3(kThreads), 0, s, a);
+  if (h->C == 8) {
+    if (wide) hipLaunchKernelGGL((gemv_mfma_kernel<8, 4>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemv_mfma_kernel<8, 1>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (wide) hipLaunchKernelGGL((gemv_mfma_kernel<12, 4>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemv_mfma_kernel<12, 1>), grid, dim3(kThreads), 0, s, a);
+  }
   SEEDLM_HIP_CHECK(hipGetLastError());
   if (a.chunks > 1) {
     hipLaunchKernelGGL(reduce_chunks_kernel, dim3((unsigned)((a.rows + 63) / 64), (unsigned)batch),
