@@ -135,12 +135,13 @@ SEEDLM_API int seedlm_gemv(seedlm_handle h, const void* x, void* y, int batch,
                            int x_dtype, int y_dtype, void* stream);
 
 /*
- * seedlm_gemv_many -- y[i] = W_i x[i] for n matrices, same result as n calls
- * of seedlm_gemv on `stream`.  Consecutive batch-1 matrices of one format are
- * run together (up to 8 per launch) so that small matrices share the GPU and the
- * per-launch cost is paid once; a decoder layer's q/k/v/o/gate/up/down is the
- * intended use (the pages' inference step, applied to every weight matrix:
- * paperhub.cn rebuttal text before Eq. (1)).
+ * seedlm_gemv_many -- y[i] = W_i x[i] for n matrices, the same results as n
+ * calls of seedlm_gemv on `stream`.  Up to 8 consecutive matrices are run
+ * together -- at batch 1
+ * those of one format, at batch > 1 with fp16 x and y any of them -- so that
+ * small matrices share the GPU and the per-launch cost is paid once; a decoder
+ * layer's q/k/v/o/gate/up/down is the intended use (the pages' inference step,
+ * applied to every weight matrix: paperhub.cn rebuttal text before Eq. (1)).
  *   handles  host array of n distinct handles (each call uses its handle's
  *            workspace, so a handle may appear only once)
  *   x, y     host arrays of n device pointers, layouts as for seedlm_gemv
@@ -152,7 +153,7 @@ SEEDLM_API int seedlm_gemv_many(const seedlm_handle* handles, const void* const*
 
 /*
  * seedlm_gemv_many_begin / seedlm_gemv_many_end -- seedlm_gemv_many split in
- * its two launches: _begin runs the fused decode-GEMV kernel (per-panel row
+ * two: _begin runs the fused decode-GEMV kernels (per-panel or per-chunk row
  * partials into the handles' workspaces), _end adds the partials into y.  Called
  * back to back with identical arguments they equal seedlm_gemv_many; the split
  * lets a caller time or overlap the two halves.  Between the two calls the

@@ -111,20 +111,27 @@ int gemv_many_phases(const seedlm_handle* handles, const void* const* x, void* c
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   int i = 0;
+  const bool mfma = batch > 1 && x_dtype == SEEDLM_F16 && y_dtype == SEEDLM_F16;
   while (i < n) {
-    // Group consecutive batch-1 matrices of one format (up to 8) into one
-    // launch pair.
+    // Group up to 8 consecutive matrices: at batch 1 those of one format (the
+    // table-lookup kernels), at batch > 1 with fp16 x and y any of them (the
+    // matrix-core kernel, which launches per format itself).
     const int C = handles[i]->C;
     int k = 0;
     while (batch == 1 && i + k < n && k < 8 && handles[i + k]->C == C &&
            handles[i + k]->bytes < 0x80000000ull)
       ++k;
+    while (mfma && i + k < n && k < 8) ++k;
     if (k >= 1) {
       const seedlm_matrix* hs[8];
       for (int j = 0; j < k; ++j) hs[j] = handles[i + j];
-      const int st =
-          C == 8 ? launch_gemv_lut_group(hs, x + i, y + i, k, x_dtype, y_dtype, false, s, phases)
-                 : launch_gemv_lut12_group(hs, x + i, y + i, k, x_dtype, y_dtype, s, phases);
+      int st;
+      if (mfma)
+        st = launch_gemv_mfma_group(hs, x + i, y + i, k, batch, x_dtype, y_dtype, s, phases);
+      else if (C == 8)
+        st = launch_gemv_lut_group(hs, x + i, y + i, k, x_dtype, y_dtype, false, s, phases);
+      else
+        st = launch_gemv_lut12_group(hs, x + i, y + i, k, x_dtype, y_dtype, s, phases);
       if (st != SEEDLM_OK) return st;
       i += k;
     } else {

@@ -77,11 +77,22 @@ struct MfmaArgs {
   uint32_t exp_off;    // byte offset of the 3-bit exponent nibbles
   int rows, cols, Mp, nb, np, batch;
   int tiles, chunk_panels, chunks;
+  int wg_begin;   // first workgroup of this matrix in its main launch
+  int red_begin;  // first reduce workgroup (64 rows) of this matrix
+};
+
+// Up to kMaxMfmaGroup matrices share a launch: workgroups are numbered matrix
+// after matrix (a matrix's own split is unchanged), so small matrices run
+// beside large ones and the per-launch cost is paid once.
+constexpr int kMaxMfmaGroup = 8;
+struct MfmaGroup {
+  MfmaArgs m[kMaxMfmaGroup];
+  int n;
 };
 
 template <int C, int RW>
 __global__ void __launch_bounds__(kThreads, 4)
-gemv_mfma_kernel(const MfmaArgs a) {
+gemv_mfma_kernel(const MfmaGroup grp) {
   static_assert(RW == 1 || RW == 4, "row groups per wave");
   using F = Fmt<C>;
   constexpr int kUnits = 2 * RW;             // units per panel and wave
@@ -92,8 +103,12 @@ gemv_mfma_kernel(const MfmaArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, q = lane >> 4;
-  const int tile = (int)(blockIdx.x % (unsigned)a.tiles);
-  const int chunk = (int)(blockIdx.x / (unsigned)a.tiles);
+  int mi = 0;
+  while (mi + 1 < grp.n && (int)blockIdx.x >= grp.m[mi + 1].wg_begin) ++mi;
+  const MfmaArgs& a = grp.m[mi];
+  const int local = (int)blockIdx.x - a.wg_begin;
+  const int tile = local % a.tiles;
+  const int chunk = local / a.tiles;
   const int pa = chunk * a.chunk_panels;
   const int pb = min(a.np, pa + a.chunk_panels);
   // Row group rr of this wave: rows row0 + rho + 4 i, i = 0..15, with rho =
@@ -258,16 +273,21 @@ gemv_mfma_kernel(const MfmaArgs a) {
   }
 }
 
-// y[b][r] = sum over chunks c of partial[c][b][r]; a workgroup owns 64 rows of
-// one batch column, lane = row, wave w adds chunks w, w+4, ... (16 loads in
+// y[b][r] = sum over chunks c of partial[c][b][r] for the group's matrices
+// that were split into chunks; a workgroup owns 64 rows of one matrix and one
+// batch column, lane = row, wave w adds chunks w, w+4, ... (16 loads in
 // flight), the four sums combine as (w0+w1)+(w2+w3).  Fixed order.
-__global__ void __launch_bounds__(256) reduce_chunks_kernel(const float* __restrict__ partial,
-                                                            __half* __restrict__ y, int rows,
-                                                            int Mp, int batch, int chunks) {
+__global__ void __launch_bounds__(256) reduce_chunks_kernel(const MfmaGroup grp) {
   __shared__ float wsum[4][64];
+  int mi = 0;
+  while (mi + 1 < grp.n && (int)blockIdx.x >= grp.m[mi + 1].red_begin) ++mi;
+  const MfmaArgs& a = grp.m[mi];
+  const float* __restrict__ partial = a.partial;
+  __half* __restrict__ y = a.y;
+  const int rows = a.rows, Mp = a.Mp, batch = a.batch, chunks = a.chunks;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int b = (int)blockIdx.y;
-  const int r = (int)blockIdx.x * 64 + lane;
+  const int r = ((int)blockIdx.x - a.red_begin) * 64 + lane;
   const int rr = r < rows ? r : rows - 1;  // in-bounds load; no store below
   const float* __restrict__ src = partial + (int64_t)b * Mp + rr;
   const int64_t cstride = (int64_t)batch * Mp;
@@ -291,13 +311,17 @@ __global__ void __launch_bounds__(256) reduce_chunks_kernel(const float* __restr
 
 }  // namespace
 
-int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
-                     hipStream_t s) {
-  if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
-  if (batch < 1 || batch > kBatchPad) return SEEDLM_E_INVALID;
-  if (h->bytes >= 0x80000000ull || h->Mp >= (1 << 30) || (int64_t)batch * h->cols * 2 >= (1LL << 31))
+namespace {
+
+// The split of one matrix: tiling (256-row tiles where they give about four
+// workgroups per CU over the panels, 64-row tiles for smaller matrices) and
+// panel chunks to reach that many workgroups.
+int plan_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, MfmaArgs& a,
+              bool& wide) {
+  if (h->bytes >= 0x80000000ull || h->Mp >= (1 << 30) ||
+      (int64_t)batch * h->cols * 2 >= (1LL << 31))
     return SEEDLM_E_UNSUPPORTED;
-  MfmaArgs a{};
+  a = MfmaArgs{};
   a.words = static_cast<const uint32_t*>(h->d_buf);
   a.x = static_cast<const __half*>(x);
   a.partial = h->d_work;
@@ -310,11 +334,8 @@ int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, 
   a.nb = (int)h->nb;
   a.np = (int)h->np;
   a.batch = batch;
-  // 256-row tiles (four row groups per wave) where they give about four
-  // workgroups per CU over the panels, 64-row tiles (one row group per wave)
-  // for the smaller matrices; then split the panels into chunks to reach that.
   const int64_t want = 4LL * device_cu_count();
-  const bool wide = ((h->Mp + kRowsPerTile - 1) / kRowsPerTile) * h->np >= want;
+  wide = ((h->Mp + kRowsPerTile - 1) / kRowsPerTile) * h->np >= want;
   const int tile_rows = wide ? kRowsPerTile : 64;
   a.tiles = (int)((h->Mp + tile_rows - 1) / tile_rows);
   int64_t chunks = (want + a.tiles - 1) / a.tiles;
@@ -323,21 +344,80 @@ int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, 
   a.chunk_panels = (int)((a.np + chunks - 1) / chunks);
   a.chunks = (a.np + a.chunk_panels - 1) / a.chunk_panels;
   if ((size_t)a.chunks * batch * h->Mp * sizeof(float) > h->work_bytes) return SEEDLM_E_INVALID;
-  const dim3 grid((unsigned)(a.tiles * a.chunks));
-  if (h->C == 8) {
-    if (wide) hipLaunchKernelGGL((gemv_mfma_kernel<8, 4>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((gemv_mfma_kernel<8, 1>), grid, dim3(kThreads), 0, s, a);
-  } else {
-    if (wide) hipLaunchKernelGGL((gemv_mfma_kernel<12, 4>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((gemv_mfma_kernel<12, 1>), grid, dim3(kThreads), 0, s, a);
+  if ((int64_t)a.tiles * a.chunks >= (1LL << 30)) return SEEDLM_E_UNSUPPORTED;
+  return SEEDLM_OK;
+}
+
+template <int C, int RW>
+void launch_main(const MfmaGroup& g, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_mfma_kernel<C, RW>), dim3((unsigned)grid), dim3(kThreads), 0, s, g);
+}
+
+}  // namespace
+
+int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs,
+                           void* const* ys, int n, int batch, int xdt, int ydt, hipStream_t s,
+                           int phases) {
+  if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
+  if (batch < 1 || batch > kBatchPad) return SEEDLM_E_INVALID;
+  if (n < 1 || n > kMaxMfmaGroup) return SEEDLM_E_INVALID;
+  MfmaArgs args[kMaxMfmaGroup];
+  bool wide[kMaxMfmaGroup];
+  for (int i = 0; i < n; ++i) {
+    if (hs[i]->C != 8 && hs[i]->C != 12) return SEEDLM_E_UNSUPPORTED;
+    const int st = plan_mfma(hs[i], xs[i], ys[i], batch, args[i], wide[i]);
+    if (st != SEEDLM_OK) return st;
   }
-  SEEDLM_HIP_CHECK(hipGetLastError());
-  if (a.chunks > 1) {
-    hipLaunchKernelGGL(reduce_chunks_kernel, dim3((unsigned)((a.rows + 63) / 64), (unsigned)batch),
-                       dim3(256), 0, s, a.partial, a.y, a.rows, a.Mp, batch, a.chunks);
-    SEEDLM_HIP_CHECK(hipGetLastError());
+  if (phases & 1) {
+    // One launch per (format, tiling) present.
+    for (int C : {8, 12}) {
+      for (bool w : {true, false}) {
+        MfmaGroup g{};
+        int64_t grid = 0;
+        for (int i = 0; i < n; ++i) {
+          if (hs[i]->C != C || wide[i] != w) continue;
+          g.m[g.n] = args[i];
+          g.m[g.n].wg_begin = (int)grid;
+          grid += (int64_t)args[i].tiles * args[i].chunks;
+          ++g.n;
+        }
+        if (g.n == 0) continue;
+        if (grid >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;
+        if (C == 8) {
+          if (w) launch_main<8, 4>(g, (int)grid, s);
+          else launch_main<8, 1>(g, (int)grid, s);
+        } else {
+          if (w) launch_main<12, 4>(g, (int)grid, s);
+          else launch_main<12, 1>(g, (int)grid, s);
+        }
+        SEEDLM_HIP_CHECK(hipGetLastError());
+      }
+    }
+  }
+  if (phases & 2) {
+    // One reduce launch over the matrices that were split into chunks (the
+    // others wrote y directly).
+    MfmaGroup g{};
+    int64_t red = 0;
+    for (int i = 0; i < n; ++i) {
+      if (args[i].chunks == 1) continue;
+      g.m[g.n] = args[i];
+      g.m[g.n].red_begin = (int)red;
+      red += (args[i].rows + 63) / 64;
+      ++g.n;
+    }
+    if (g.n > 0) {
+      hipLaunchKernelGGL(reduce_chunks_kernel, dim3((unsigned)red, (unsigned)batch), dim3(256), 0,
+                         s, g);
+      SEEDLM_HIP_CHECK(hipGetLastError());
+    }
   }
   return SEEDLM_OK;
+}
+
+int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
+                     hipStream_t s) {
+  return launch_gemv_mfma_group(&h, &x, &y, 1, batch, xdt, ydt, s, 3);
 }
 
 }  // namespace seedlm

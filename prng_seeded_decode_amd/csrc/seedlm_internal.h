@@ -94,6 +94,11 @@ int launch_gemv_lut12_group(const seedlm_matrix* const* hs, const void* const* x
                             void* const* ys, int n, int xdt, int ydt, hipStream_t s, int phases);
 int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
                      hipStream_t s);
+// Up to 8 matrices at batch > 1 (fp16): phases & 1 the decode-GEMM launches
+// (one per format and tiling present), phases & 2 one reduction launch.
+int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs,
+                           void* const* ys, int n, int batch, int xdt, int ydt, hipStream_t s,
+                           int phases);
 // Prefill GEMM (both packed formats, fp16 X and Y; E_UNSUPPORTED otherwise).
 int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
                 hipStream_t s);
