@@ -127,17 +127,30 @@ gemv_mfma_kernel(const MfmaGroup grp) {
   // x staging: thread t holds batch row t / 16 and the kPer consecutive panel
   // columns (t % 16) kPer ..; buffer loads read zeros for padding rows (an
   // out-of-range offset) and columns past the row's end are set to zero.
-  // Pairs are packed into 32-bit registers and stored as 16-byte writes.
+  // With cols a multiple of 8 the run is read with 16-byte loads, otherwise
+  // two bytes at a time; pairs sit in 32-bit registers and go to LDS as
+  // 16-byte writes.
   constexpr int kPer = F::kCols / 16;  // halves per thread
   static_assert(kThreads == 16 * kBatchPad && kPer % 8 == 0, "x staging layout");
   const int xb = tid >> 4, xc0 = (tid & 15) * kPer;
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)a.x, 0, (int)((uint32_t)a.batch * (uint32_t)a.cols * 2u), 0x00020000);
   uint32_t xr[kPer / 2];
+  const bool x16 = a.cols % 8 == 0;  // 16-byte aligned runs of 8 columns
   auto fetch_x = [&](int p) {
     const int col0 = p * F::kCols + xc0;
     const int lim = a.cols - col0;  // columns k < lim of this run lie inside the row
     const uint32_t base = xb < a.batch ? (uint32_t)(xb * a.cols + col0) * 2u : 0x80000000u;
+    if (x16) {  // lim is then a multiple of 8: a run of 8 is wholly in or out
+#pragma unroll
+      for (int k = 0; k < kPer; k += 8) {
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(
+            xrsrc, k < lim ? base + 2u * k : 0x80000000u, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xr[k / 2 + j] = v[j];
+      }
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < kPer; k += 2) {
       const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
