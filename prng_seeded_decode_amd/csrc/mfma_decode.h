@@ -22,6 +22,16 @@ __device__ inline uint32_t ubfe(uint32_t v, uint32_t off, uint32_t w) {
 // the fp16 range factor 2^10.
 __device__ inline float block_scale(uint32_t g) { return __uint_as_float((g + 107u) << 23); }
 
+// a * b + c for a, b within 24-bit signed range (a coefficient and a 16-bit
+// window): one v_mad_i32_i24, which the compiler does not form by itself (it
+// emits v_mul_i32_i24 and sums with v_add3_u32, two instructions more per
+// weight).
+__device__ inline int mad24(int a, int b, int c) {
+  int d;
+  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // Stream bits 16..47 of a 4-bit block's seed from the two GF(2) byte tables.
 __device__ inline uint32_t ext_c8(uint32_t w, const uint32_t* T0, const uint32_t* T1) {
   return T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];
@@ -42,7 +52,7 @@ __device__ inline half8 decode_c8_ext(uint32_t w, uint32_t ext) {
     const int z0 = (int)ubfe(lo, i, 16);       // z_i
     const int z1 = (int)ubfe(lo, 8 + i, 16);   // z_{8+i}
     const int z2 = (int)ubfe(ext, i, 16);      // z_{16+i}
-    const int I = t0 * z0 + t1 * z1 + t2 * z2 + base;
+    const int I = mad24(t2, z2, mad24(t1, z1, mad24(t0, z0, base)));
     out[i] = (_Float16)((float)I * sc);
   }
   return out;
@@ -103,7 +113,7 @@ __device__ inline uint64_t dec12_quad(const Dec12& d) {
       const int n = 12 * j + i;  // state index, window b[n .. n+15]
       const int z = n <= 16 ? (int)ubfe(d.s0, n, 16)
                             : (n <= 32 ? (int)ubfe(d.s1, n - 16, 16) : (int)ubfe(d.s2, n - 32, 16));
-      I += d.t[j] * z;
+      I = mad24(d.t[j], z, I);
     }
     o[k] = (_Float16)((float)I * d.sc);
   }
