@@ -32,6 +32,14 @@ __device__ inline int mad24(int a, int b, int c) {
   return d;
 }
 
+// The integer sums start from kMagic, the bits of the float 1.5 * 2^23: for
+// |I| < 2^22 the bits of kMagic + I are the float 1.5 * 2^23 + I, exactly, so
+// fma(bits as float, scale, -1.5 * 2^23 * scale) is I * scale before its one
+// rounding, to fp16 -- the same value as converting I and scaling, in one
+// instruction (v_fma_mixlo_f16) instead of a conversion and a multiply.
+constexpr int kMagic = 0x4B400000;
+constexpr float kMagicF = 12582912.0f;  // 1.5 * 2^23
+
 // Stream bits 16..47 of a 4-bit block's seed from the two GF(2) byte tables.
 __device__ inline uint32_t ext_c8(uint32_t w, const uint32_t* T0, const uint32_t* T1) {
   return T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];
@@ -44,8 +52,9 @@ __device__ inline half8 decode_c8_ext(uint32_t w, uint32_t ext) {
   const int t0 = ((int)(w << 12)) >> 28;
   const int t1 = ((int)(w << 8)) >> 28;
   const int t2 = ((int)(w << 4)) >> 28;
-  const int base = -32768 * (t0 + t1 + t2);
+  const int base = kMagic - 32768 * (t0 + t1 + t2);
   const float sc = block_scale(w >> 28);
+  const float off = -kMagicF * sc;
   half8 out;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -53,7 +62,7 @@ __device__ inline half8 decode_c8_ext(uint32_t w, uint32_t ext) {
     const int z1 = (int)ubfe(lo, 8 + i, 16);   // z_{8+i}
     const int z2 = (int)ubfe(ext, i, 16);      // z_{16+i}
     const int I = mad24(t2, z2, mad24(t1, z1, mad24(t0, z0, base)));
-    out[i] = (_Float16)((float)I * sc);
+    out[i] = (_Float16)__builtin_fmaf(__int_as_float(I), sc, off);
   }
   return out;
 }
@@ -69,8 +78,9 @@ __device__ inline half8 decode_c8(uint32_t w, const uint32_t* T0, const uint32_t
 struct Dec12 {
   uint32_t s0, s1, s2;  // stream bits 0..31, 16..47, 32..63
   int t[4];
-  int base;             // -2^15 (t0 + t1 + t2 + t3)
+  int base;             // kMagic - 2^15 (t0 + t1 + t2 + t3)
   float sc;
+  float off;            // -1.5 * 2^23 * sc
 };
 
 __device__ inline Dec12 dec12_setup(uint32_t w, uint32_t g, const uint64_t* T0,
@@ -82,8 +92,9 @@ __device__ inline Dec12 dec12_setup(uint32_t w, uint32_t g, const uint64_t* T0,
   d.s2 = (uint32_t)(ext >> 16);
 #pragma unroll
   for (int j = 0; j < 4; ++j) d.t[j] = ((int)(w << (12 - 4 * j))) >> 28;
-  d.base = -32768 * (d.t[0] + d.t[1] + d.t[2] + d.t[3]);
+  d.base = kMagic - 32768 * (d.t[0] + d.t[1] + d.t[2] + d.t[3]);
   d.sc = block_scale(g);
+  d.off = -kMagicF * d.sc;
   return d;
 }
 
@@ -115,35 +126,9 @@ __device__ inline uint64_t dec12_quad(const Dec12& d) {
                             : (n <= 32 ? (int)ubfe(d.s1, n - 16, 16) : (int)ubfe(d.s2, n - 32, 16));
       I = mad24(d.t[j], z, I);
     }
-    o[k] = (_Float16)((float)I * d.sc);
+    o[k] = (_Float16)__builtin_fmaf(__int_as_float(I), d.sc, d.off);
   }
   return __builtin_bit_cast(uint64_t, o);
-}
-
-// Twelve fp16 weights (x 2^10) of a 3-bit block, written to o[0..11].
-__device__ inline void decode_c12(uint32_t w, uint32_t g, const uint64_t* T0, const uint64_t* T1,
-                                  _Float16* o) {
-  const uint64_t ext = T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];  // stream bits 16..79
-  const uint32_t s0 = (w & 0xFFFFu) | ((uint32_t)ext << 16);    // bits 0..31
-  const uint32_t s1 = (uint32_t)ext;                            // bits 16..47
-  const uint32_t s2 = (uint32_t)(ext >> 16);                    // bits 32..63
-  int t[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) t[j] = ((int)(w << (12 - 4 * j))) >> 28;
-  const int base = -32768 * (t[0] + t[1] + t[2] + t[3]);
-  const float sc = block_scale(g);
-#pragma unroll
-  for (int i = 0; i < 12; ++i) {
-    int I = base;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = 12 * j + i;  // state index, window b[n .. n+15]
-      const int z = n <= 16 ? (int)ubfe(s0, n, 16)
-                            : (n <= 32 ? (int)ubfe(s1, n - 16, 16) : (int)ubfe(s2, n - 32, 16));
-      I += t[j] * z;
-    }
-    o[i] = (_Float16)((float)I * sc);
-  }
 }
 
 }  // namespace seedlm
