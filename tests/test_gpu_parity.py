@@ -321,32 +321,36 @@ def test_full_layer_gemv_many_sampled(cid):
         assert O.normwise_error(yv, O.gemv(W_ref, x)) <= TOL["f16"]
 
 
-def test_gemv_many_graph_replays_match_eager():
-    # A captured step (main + reduce launches) replayed several times, with
-    # eager work and synchronizations between the replays; every replay must
-    # give the eager call's bits.
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gemv_many_graph_replays_match_eager(batch):
+    # A captured step (main + reduce launches; at batch 4 the grouped
+    # matrix-core launches, both tilings and both formats) replayed several
+    # times, with eager work and synchronizations between the replays; every
+    # replay must give the eager call's bits.
     S = _S()
     dev = _dev()
     rng = np.random.default_rng(777)
     shapes = [(8, 3, 512, 2048), (8, 3, 128, 2048), (8, 3, 1024, 640 + 5)]
+    if batch > 1:
+        shapes += [(12, 4, 300, 12 * 40 + 8), (8, 3, 8192, 8192)]  # the last: 256-row tiles
     mats, xs = [], []
     for C, P, rows, cols in shapes:
         s, c, e = _random_records(rng, rows, cols, C, P)
         mats.append(_pack(s, c, e, rows, cols, C, P))
-        xs.append(torch.from_numpy(rng.standard_normal((1, cols)).astype(np.float16)).to(dev))
-    ys = [torch.empty((1, m.rows), dtype=torch.float16, device=dev) for m in mats]
+        xs.append(torch.from_numpy(rng.standard_normal((batch, cols)).astype(np.float16)).to(dev))
+    ys = [torch.empty((batch, m.rows), dtype=torch.float16, device=dev) for m in mats]
     ref = [torch.empty_like(y) for y in ys]
-    S.seedlm_gemv_many(mats, xs, ref)
+    S.seedlm_gemv_many(mats, xs, ref, batch=batch)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        S.seedlm_gemv_many(mats, xs, ys, stream=torch.cuda.current_stream())
+        S.seedlm_gemv_many(mats, xs, ys, batch=batch, stream=torch.cuda.current_stream())
     for k in range(4):
         for y in ys:
             y.fill_(float("nan"))
         # eager work between replays: the same matrices into other outputs
         other = [torch.empty_like(y) for y in ys]
-        S.seedlm_gemv_many(mats, xs, other)
+        S.seedlm_gemv_many(mats, xs, other, batch=batch)
         torch.cuda.synchronize()
         _say(f"graph replay {k}")
         g.replay()
