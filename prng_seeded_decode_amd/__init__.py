@@ -30,6 +30,8 @@ from ._binding import (  # noqa: F401
     seedlm_export,
     seedlm_fp16_gemv,
     seedlm_gemm,
+    seedlm_gemm_decoded,
+    seedlm_gemm_decoded_bytes,
     seedlm_gemv,
     seedlm_gemv_many,
     seedlm_pack,

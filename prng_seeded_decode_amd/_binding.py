@@ -43,6 +43,8 @@ EXPORTED = (
     "seedlm_fp16_gemv",
     "seedlm_stream_read",
     "seedlm_gemm",
+    "seedlm_gemm_decoded",
+    "seedlm_gemm_decoded_bytes",
     "seedlm_encoder_create",
     "seedlm_encoder_destroy",
     "seedlm_encode",
@@ -98,6 +100,8 @@ def lib() -> ctypes.CDLL:
     L.seedlm_fp16_gemv.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     L.seedlm_stream_read.argtypes = [vp, i64, vp, vp]
     L.seedlm_gemm.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+    L.seedlm_gemm_decoded.argtypes = [vp, vp, vp, i64, i32, i32, vp, ctypes.c_size_t, vp]
+    L.seedlm_gemm_decoded_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     L.seedlm_encoder_create.argtypes = [i32, i32, i32, i32, ctypes.POINTER(vp)]
     L.seedlm_encoder_destroy.argtypes = [vp]
     L.seedlm_encode.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp]
@@ -279,6 +283,29 @@ def seedlm_gemm(m: SeedLMMatrix, X, Y, stream=None):
     _check(lib().seedlm_gemm(m.handle, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(Y.data_ptr()),
                              X.shape[0], _dtype_code(X), _dtype_code(Y), _stream_ptr(stream)),
            "seedlm_gemm")
+    return Y
+
+
+def seedlm_gemm_decoded_bytes(m: SeedLMMatrix) -> int:
+    """Workspace bytes seedlm_gemm_decoded needs for m (rows * cols * 2)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().seedlm_gemm_decoded_bytes(m.handle, ctypes.byref(n)), "seedlm_gemm_decoded_bytes")
+    return n.value
+
+
+def seedlm_gemm_decoded(m: SeedLMMatrix, X, Y, workspace, stream=None):
+    """Y = X W^T through a decoded fp16 copy of W in `workspace` (a device
+    tensor of at least seedlm_gemm_decoded_bytes(m) bytes) and rocBLAS."""
+    if X.dim() != 2 or X.shape[1] != m.cols or Y.numel() != X.shape[0] * m.rows:
+        raise ValueError("X must be [ntok][cols] and Y hold ntok*rows elements")
+    if not (X.is_cuda and Y.is_cuda and workspace.is_cuda and X.is_contiguous() and
+            Y.is_contiguous() and workspace.is_contiguous()):
+        raise ValueError("X, Y and workspace must be contiguous device tensors")
+    _check(lib().seedlm_gemm_decoded(m.handle, ctypes.c_void_p(X.data_ptr()),
+                                     ctypes.c_void_p(Y.data_ptr()), X.shape[0], _dtype_code(X),
+                                     _dtype_code(Y), ctypes.c_void_p(workspace.data_ptr()),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream_ptr(stream)), "seedlm_gemm_decoded")
     return Y
 
 

@@ -187,6 +187,19 @@ int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok, int x_dty
   return launch_gemm(h, X, Y, ntok, x_dtype, y_dtype, static_cast<hipStream_t>(stream));
 }
 
+int seedlm_gemm_decoded_bytes(seedlm_handle h, size_t* bytes) {
+  if (!h || !bytes) return SEEDLM_E_INVALID;
+  *bytes = decoded_bytes(h);
+  return SEEDLM_OK;
+}
+
+int seedlm_gemm_decoded(seedlm_handle h, const void* X, void* Y, int64_t ntok, int x_dtype,
+                        int y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h || !X || !Y || !workspace || ntok < 1) return SEEDLM_E_INVALID;
+  return launch_gemm_decoded(h, X, Y, ntok, x_dtype, y_dtype, workspace, workspace_bytes,
+                             static_cast<hipStream_t>(stream));
+}
+
 int seedlm_encoder_create(int C, int P, int K, int Q, seedlm_encoder_handle* out) {
   if (!out) return SEEDLM_E_INVALID;
   *out = nullptr;

@@ -164,3 +164,71 @@ def test_gemm_deterministic_and_rejects_unsupported():
         assert S.lib().seedlm_gemm(mm.handle, ctypes.c_void_p(Xd.data_ptr()),
                                    ctypes.c_void_p(Y.data_ptr()), 65535 * 256 + 1, S.F16, S.F16,
                                    None) == S.E_UNSUPPORTED
+
+
+# seedlm_gemm_decoded: W rebuilt once into a caller workspace as fp16(w * 2^10),
+# then rocBLAS.  The workspace is checked bit for bit against the oracle's
+# float64 weights times 2^10 rounded to fp16 (round to nearest even, as the
+# kernel's conversion); the product at the GEMV bar per token row.
+@pytest.mark.parametrize("C,P,rows,cols,ntok", [
+    (8, 3, 200, 296, 300),      # 37 blocks: a full and a 5-block panel, ragged tokens
+    (8, 3, 130, 520, 17),       # rows not a multiple of 8
+    (12, 4, 200, 400, 300),     # 34 blocks, the last 4 columns short
+    (12, 4, 130, 440, 513),     # 37 blocks, last block 8 columns
+    (12, 4, 1000, 2048, 600),   # 171 blocks over 6 panels
+])
+def test_gemm_decoded_matches_oracle_and_exact_workspace(C, P, rows, cols, ntok):
+    dev = _dev()
+    S = _S()
+    s, c, e = gen_records(65, 0, rows, cols, C, P)
+    m = S.seedlm_pack(s, c, e, rows, cols, C, P, 16)
+    X = gen_x(65, 0, ntok, cols, "f16")
+    Xd = torch.from_numpy(X).to(dev)
+    Y = torch.empty((ntok, rows), dtype=torch.float16, device=dev)
+    nbytes = S.seedlm_gemm_decoded_bytes(m)
+    assert nbytes == rows * cols * 2
+    ws = torch.full((nbytes // 2,), float("nan"), dtype=torch.float16, device=dev)
+    _say(f"gemm decoded C={C} {rows}x{cols} ntok={ntok}")
+    S.seedlm_gemm_decoded(m, Xd, Y, ws)
+    torch.cuda.synchronize()
+    W = O.decode_rows(s, c, e, cols, C, P)
+    want = (W * 1024.0).astype(np.float16)
+    got = ws.cpu().numpy().reshape(rows, cols)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), "decoded workspace must be exact"
+    err = _rowwise_err(Y.cpu().numpy().astype(np.float64), X.astype(np.float64) @ W.T)
+    _say(f"  max per-token normwise error {err:.2e}")
+    assert err <= TOL
+
+
+def test_gemm_decoded_full_shape_sampled_and_rejects():
+    """Llama-3-70B gate projection (28672x8192, 4-bit), 2048 tokens, sampled; and
+    the argument checks."""
+    dev = _dev()
+    S = _S()
+    rows, cols, ntok = 28672, 8192, 2048
+    s, c, e = gen_records(4, 4, rows, cols, 8, 3)
+    m = S.seedlm_pack(s, c, e, rows, cols, 8, 3, 16)
+    X = gen_x(4, 4, ntok, cols, "f16")
+    Xd = torch.from_numpy(X).to(dev)
+    Y = torch.empty((ntok, rows), dtype=torch.float16, device=dev)
+    ws = torch.empty((rows * cols,), dtype=torch.float16, device=dev)
+    _say(f"gemm decoded sampled {rows}x{cols} ntok={ntok}")
+    S.seedlm_gemm_decoded(m, Xd, Y, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rs = np.concatenate([[0, rows - 1], rng.choice(rows, 30, replace=False)])
+    ts = np.concatenate([[0, ntok - 1], rng.choice(ntok, 14, replace=False)])
+    W = O.decode_rows(s[rs], c[rs], e[rs], cols, 8, 3)
+    Yr = X[ts].astype(np.float64) @ W.T
+    Yg = Y.cpu().numpy().astype(np.float64)
+    assert _rowwise_err(Yg[np.ix_(ts, rs)], Yr) <= TOL
+    # the fused kernel computes the same product
+    Yf = torch.empty_like(Y)
+    S.seedlm_gemm(m, Xd, Yf)
+    torch.cuda.synchronize()
+    assert _rowwise_err(Yg, Yf.cpu().numpy().astype(np.float64)) <= TOL
+    # workspace one element short; fp32 activations
+    with pytest.raises(S.SeedLMError):
+        S.seedlm_gemm_decoded(m, Xd, Y, ws[: rows * cols - 1])
+    with pytest.raises(S.SeedLMError):
+        S.seedlm_gemm_decoded(m, Xd.float(), Y, ws)
