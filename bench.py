@@ -365,9 +365,9 @@ def gemm_main(args):
     achieved = alg_flops / kern_s / 1e12
     layer_weights = sum(m.rows * m.cols for m in cfg.matrices)
     # the same step through seedlm_gemm_decoded: W rebuilt into one shared fp16
-    # workspace per matrix in turn, then rocBLAS
-    ws = torch.empty((max(m.rows * m.cols for m in cfg.matrices),), dtype=torch.float16,
-                     device=dev)
+    # workspace per matrix in turn (with the GEMM's scratch), then hipBLASLt
+    ws = torch.empty((max(S.seedlm_gemm_decoded_bytes(m) for m in mats) // 2,),
+                     dtype=torch.float16, device=dev)
 
     def step_decoded():
         for m, x, y in zip(mats, xs, ys):
@@ -433,7 +433,7 @@ def gemm_main(args):
         },
         "dense_fp16_baseline": dense,
         "decoded_path": {
-            "entry": "seedlm_gemm_decoded (exact fp16 rebuild into a workspace, then rocBLAS)",
+            "entry": "seedlm_gemm_decoded (exact fp16 rebuild into a workspace, then hipBLASLt)",
             "ms_per_step": round(dec_ms, 4),
             "tokens_per_s": ntok / (dec_ms * 1e-3),
             "TFLOPs": round(2.0 * layer_weights * ntok / (dec_ms * 1e-3) / 1e12, 1),

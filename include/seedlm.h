@@ -264,28 +264,35 @@ SEEDLM_API int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok
 /*
  * seedlm_gemm_decoded -- the same product through a decoded copy of W: the
  * matrix is rebuilt once, exactly, into `workspace` as fp16(w * 2^10) (the
- * values the matrix-core kernels feed their MFMAs), then multiplied by
- * rocBLAS gemm_ex (fp16 operands, fp32 accumulation, alpha = 2^-10).  With
+ * values the matrix-core kernels feed their MFMAs), then multiplied by a
+ * hipBLASLt matmul (fp16 operands, fp32 accumulation, alpha = 2^-10).  With
  * hundreds of activation rows or more the product is compute-bound and this
  * path is faster than seedlm_gemm; below that seedlm_gemm is.  The weights are
  * still rebuilt from the records (paperhub.cn rebuttal text before Eq. (1));
  * the copy lives only in the caller's workspace, for the duration of the call.
  *   X, Y       as for seedlm_gemm (fp16, cols a multiple of 8, X 16-byte aligned)
  *   workspace  device memory, 16-byte aligned, caller-owned, at least
- *              seedlm_gemm_decoded_bytes(h) bytes (rows * cols * 2); on return
- *              it holds the decoded matrix, row-major
- * Asynchronous on `stream`.  Uses one rocBLAS handle per device, created on the
- * first call (which also loads rocBLAS's kernels); calls from several host
- * threads serialise on a lock while they enqueue.
+ *              rows * cols * 2 bytes; on return its first rows * cols * 2
+ *              bytes hold the decoded matrix, row-major.  Bytes past the
+ *              matrix (from the next multiple of 256, up to 32 MiB) serve as
+ *              the GEMM's scratch; seedlm_gemm_decoded_bytes(h) is the size
+ *              that includes the full 32 MiB
+ * Asynchronous on `stream`.  Uses one hipBLASLt handle per device, created on
+ * the first call, and caches one matmul plan per device, shape and scratch
+ * size (the first call with a new shape also runs the library's heuristic
+ * query); calls from several host threads serialise on a lock while they
+ * enqueue.  Calls that share a workspace must not overlap.
  * Errors: SEEDLM_E_INVALID (null pointer, ntok < 1, workspace too small),
  * SEEDLM_E_UNSUPPORTED (dtype, alignment, cols not a multiple of 8, sizes of
- * 2^31 or more), SEEDLM_E_DEVICE (launch or rocBLAS failure).
+ * 2^31 or more), SEEDLM_E_DEVICE (launch failure, or no hipBLASLt algorithm
+ * for the shape).
  */
 SEEDLM_API int seedlm_gemm_decoded(seedlm_handle h, const void* X, void* Y, int64_t ntok,
                                    int x_dtype, int y_dtype, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
-/* seedlm_gemm_decoded_bytes -- the workspace seedlm_gemm_decoded needs for h. */
+/* seedlm_gemm_decoded_bytes -- the workspace size for seedlm_gemm_decoded on h:
+ * the decoded matrix rounded up to 256 bytes, plus 32 MiB of GEMM scratch. */
 SEEDLM_API int seedlm_gemm_decoded_bytes(seedlm_handle h, size_t* bytes);
 
 /*

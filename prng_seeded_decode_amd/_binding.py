@@ -287,7 +287,8 @@ def seedlm_gemm(m: SeedLMMatrix, X, Y, stream=None):
 
 
 def seedlm_gemm_decoded_bytes(m: SeedLMMatrix) -> int:
-    """Workspace bytes seedlm_gemm_decoded needs for m (rows * cols * 2)."""
+    """Workspace bytes for seedlm_gemm_decoded on m: the decoded matrix (rows * cols * 2,
+    rounded up to 256) plus 32 MiB of GEMM scratch."""
     n = ctypes.c_size_t(0)
     _check(lib().seedlm_gemm_decoded_bytes(m.handle, ctypes.byref(n)), "seedlm_gemm_decoded_bytes")
     return n.value
@@ -295,7 +296,8 @@ def seedlm_gemm_decoded_bytes(m: SeedLMMatrix) -> int:
 
 def seedlm_gemm_decoded(m: SeedLMMatrix, X, Y, workspace, stream=None):
     """Y = X W^T through a decoded fp16 copy of W in `workspace` (a device
-    tensor of at least seedlm_gemm_decoded_bytes(m) bytes) and rocBLAS."""
+    tensor of at least rows * cols * 2 bytes; seedlm_gemm_decoded_bytes(m) adds the GEMM's
+    scratch) and hipBLASLt."""
     if X.dim() != 2 or X.shape[1] != m.cols or Y.numel() != X.shape[0] * m.rows:
         raise ValueError("X must be [ntok][cols] and Y hold ntok*rows elements")
     if not (X.is_cuda and Y.is_cuda and workspace.is_cuda and X.is_contiguous() and

@@ -189,7 +189,7 @@ int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok, int x_dty
 
 int seedlm_gemm_decoded_bytes(seedlm_handle h, size_t* bytes) {
   if (!h || !bytes) return SEEDLM_E_INVALID;
-  *bytes = decoded_bytes(h);
+  *bytes = decoded_workspace_bytes(h);
   return SEEDLM_OK;
 }
 

@@ -103,8 +103,11 @@ int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs
 int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
                 hipStream_t s);
 int launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
-// Prefill through a decoded fp16 copy of W in a caller workspace and rocBLAS.
+// Prefill through a decoded fp16 copy of W in a caller workspace and hipBLASLt.
 size_t decoded_bytes(const seedlm_matrix* h);
+// GEMM scratch offered from a decoded-path workspace, past the decoded matrix.
+constexpr size_t kDecodedScratchBytes = 32u << 20;
+size_t decoded_workspace_bytes(const seedlm_matrix* h);
 int launch_gemm_decoded(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt,
                         int ydt, void* ws, size_t ws_bytes, hipStream_t s);
 int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,

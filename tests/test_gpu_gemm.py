@@ -167,7 +167,7 @@ def test_gemm_deterministic_and_rejects_unsupported():
 
 
 # seedlm_gemm_decoded: W rebuilt once into a caller workspace as fp16(w * 2^10),
-# then rocBLAS.  The workspace is checked bit for bit against the oracle's
+# then hipBLASLt.  The workspace is checked bit for bit against the oracle's
 # float64 weights times 2^10 rounded to fp16 (round to nearest even, as the
 # kernel's conversion); the product at the GEMV bar per token row.
 @pytest.mark.parametrize("C,P,rows,cols,ntok", [
@@ -186,14 +186,14 @@ def test_gemm_decoded_matches_oracle_and_exact_workspace(C, P, rows, cols, ntok)
     Xd = torch.from_numpy(X).to(dev)
     Y = torch.empty((ntok, rows), dtype=torch.float16, device=dev)
     nbytes = S.seedlm_gemm_decoded_bytes(m)
-    assert nbytes == rows * cols * 2
+    assert nbytes == ((rows * cols * 2 + 255) // 256) * 256 + (32 << 20)
     ws = torch.full((nbytes // 2,), float("nan"), dtype=torch.float16, device=dev)
     _say(f"gemm decoded C={C} {rows}x{cols} ntok={ntok}")
     S.seedlm_gemm_decoded(m, Xd, Y, ws)
     torch.cuda.synchronize()
     W = O.decode_rows(s, c, e, cols, C, P)
     want = (W * 1024.0).astype(np.float16)
-    got = ws.cpu().numpy().reshape(rows, cols)
+    got = ws[: rows * cols].cpu().numpy().reshape(rows, cols)
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), "decoded workspace must be exact"
     err = _rowwise_err(Y.cpu().numpy().astype(np.float64), X.astype(np.float64) @ W.T)
     _say(f"  max per-token normwise error {err:.2e}")
@@ -227,6 +227,14 @@ def test_gemm_decoded_full_shape_sampled_and_rejects():
     S.seedlm_gemm(m, Xd, Yf)
     torch.cuda.synchronize()
     assert _rowwise_err(Yg, Yf.cpu().numpy().astype(np.float64)) <= TOL
+    # the workspace above leaves the GEMM no scratch; again with the full size
+    ws2 = torch.empty((S.seedlm_gemm_decoded_bytes(m) // 2,), dtype=torch.float16, device=dev)
+    Y2 = torch.empty_like(Y)
+    S.seedlm_gemm_decoded(m, Xd, Y2, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(ws2[: rows * cols], ws)
+    assert _rowwise_err(Y2.cpu().numpy().astype(np.float64), Yg) <= TOL
+    del ws2, Y2
     # workspace one element short; fp32 activations
     with pytest.raises(S.SeedLMError):
         S.seedlm_gemm_decoded(m, Xd, Y, ws[: rows * cols - 1])
