@@ -543,7 +543,7 @@ def main():
     if args.warmup is None:
         args.warmup = 3 if args.encode else (20 if args.gemm else 200)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU per process only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.encode:
