@@ -200,6 +200,74 @@ def test_gemm_decoded_matches_oracle_and_exact_workspace(C, P, rows, cols, ntok)
     assert err <= TOL
 
 
+@pytest.mark.parametrize("C,P,rows,cols,ntok,extra", [
+    (8, 3, 264, 512, 1, 1000),     # one token; scratch not a multiple of 256
+    (12, 4, 96, 480, 5, 37),       # five tokens; 37 bytes past the matrix: no scratch
+    (8, 3, 72, 136, 3, 0),         # exactly the decoded size
+])
+def test_gemm_decoded_few_tokens_and_odd_scratch(C, P, rows, cols, ntok, extra):
+    """Token counts below the GEMV batch limit and workspaces whose scratch part is
+    short, ragged or absent: the product is still at the GEMV bar."""
+    dev = _dev()
+    S = _S()
+    s, c, e = gen_records(66, 0, rows, cols, C, P)
+    m = S.seedlm_pack(s, c, e, rows, cols, C, P, 16)
+    X = gen_x(66, 0, ntok, cols, "f16")
+    Xd = torch.from_numpy(X).to(dev)
+    Y = torch.empty((ntok, rows), dtype=torch.float16, device=dev)
+    ws = torch.empty((rows * cols * 2 + extra,), dtype=torch.uint8, device=dev)
+    _say(f"gemm decoded C={C} {rows}x{cols} ntok={ntok} extra={extra}")
+    S.seedlm_gemm_decoded(m, Xd, Y, ws)
+    torch.cuda.synchronize()
+    W = O.decode_rows(s, c, e, cols, C, P)
+    assert _rowwise_err(Y.cpu().numpy().astype(np.float64), X.astype(np.float64) @ W.T) <= TOL
+
+
+def test_gemm_decoded_from_two_host_threads():
+    """Two host threads call seedlm_gemm_decoded at once (the binding releases the
+    interpreter lock during the call), each on its own stream and workspace, over
+    shapes whose plans are not cached yet; every result matches a call made alone."""
+    import threading
+
+    dev = _dev()
+    S = _S()
+    shapes = [(8, 3, 520, 1024, 40), (12, 4, 384, 960, 24)]
+    jobs = []
+    for k, (C, P, rows, cols, ntok) in enumerate(shapes):
+        s, c, e = gen_records(67, k, rows, cols, C, P)
+        m = S.seedlm_pack(s, c, e, rows, cols, C, P, 16)
+        Xd = torch.from_numpy(gen_x(67, k, ntok, cols, "f16")).to(dev)
+        ws = torch.empty((S.seedlm_gemm_decoded_bytes(m),), dtype=torch.uint8, device=dev)
+        outs = [torch.empty((ntok, rows), dtype=torch.float16, device=dev) for _ in range(6)]
+        jobs.append((m, Xd, ws, outs, torch.cuda.Stream(device=dev)))
+    torch.cuda.synchronize()  # inputs uploaded before the side streams read them
+    errors = []
+
+    def work(job):
+        m, Xd, ws, outs, st = job
+        try:
+            for Y in outs:
+                S.seedlm_gemm_decoded(m, Xd, Y, ws, stream=st)
+            st.synchronize()
+        except Exception as ex:  # reported by the main thread
+            errors.append(ex)
+
+    _say("gemm decoded from two threads")
+    ts = [threading.Thread(target=work, args=(j,)) for j in jobs]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors
+    for m, Xd, ws, outs, _ in jobs:
+        alone = torch.empty_like(outs[0])
+        S.seedlm_gemm_decoded(m, Xd, alone, ws)
+        torch.cuda.synchronize()
+        ref = alone.cpu().numpy().astype(np.float64)
+        for Y in outs:
+            assert _rowwise_err(Y.cpu().numpy().astype(np.float64), ref) <= 1e-3
+
+
 def test_gemm_decoded_full_shape_sampled_and_rejects():
     """Llama-3-70B gate projection (28672x8192, 4-bit), 2048 tokens, sampled; and
     the argument checks."""
