@@ -282,10 +282,11 @@ SEEDLM_API int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok
  * size (the first call with a new shape also runs the library's heuristic
  * query); calls from several host threads serialise on a lock while they
  * enqueue.  Calls that share a workspace must not overlap.
- * Errors: SEEDLM_E_INVALID (null pointer, ntok < 1, workspace too small),
- * SEEDLM_E_UNSUPPORTED (dtype, alignment, cols not a multiple of 8, sizes of
- * 2^31 or more), SEEDLM_E_DEVICE (launch failure, or no hipBLASLt algorithm
- * for the shape).
+ * Call it with the device that h was packed on current.
+ * Errors: SEEDLM_E_INVALID (null pointer, ntok < 1, workspace too small,
+ * another device current), SEEDLM_E_UNSUPPORTED (dtype, alignment, cols not a
+ * multiple of 8, sizes of 2^31 or more), SEEDLM_E_DEVICE (launch failure, or no
+ * hipBLASLt algorithm for the shape).
  */
 SEEDLM_API int seedlm_gemm_decoded(seedlm_handle h, const void* X, void* Y, int64_t ntok,
                                    int x_dtype, int y_dtype, void* workspace,

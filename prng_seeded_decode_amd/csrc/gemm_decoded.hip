@@ -192,6 +192,10 @@ int launch_gemm_decoded(const seedlm_matrix* h, const void* x, void* y, int64_t 
   if (h->rows >= (1LL << 31) || h->cols >= (1LL << 31) || ntok >= (1LL << 31))
     return SEEDLM_E_UNSUPPORTED;
   if (h->Mp * kPanelBlocks >= (1LL << 31) || h->np >= 65536) return SEEDLM_E_UNSUPPORTED;
+  // The GEMM handle is per device and binds to the current one when created.
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SEEDLM_E_DEVICE;
+  if (cur != h->device) return SEEDLM_E_INVALID;
   // about eight workgroups per CU over all panels
   const int64_t per_panel = (h->Mp * kPanelBlocks + kDecThreads - 1) / kDecThreads;
   const int64_t gx = std::max<int64_t>(
