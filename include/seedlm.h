@@ -286,7 +286,7 @@ SEEDLM_API int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok
  * Errors: SEEDLM_E_INVALID (null pointer, ntok < 1, workspace too small,
  * another device current), SEEDLM_E_UNSUPPORTED (dtype, alignment, cols not a
  * multiple of 8, sizes of 2^31 or more), SEEDLM_E_DEVICE (launch failure, or no
- * hipBLASLt algorithm for the shape).
+ * hipBLASLt algorithm for the shape: then nothing has been enqueued).
  */
 SEEDLM_API int seedlm_gemm_decoded(seedlm_handle h, const void* X, void* Y, int64_t ntok,
                                    int x_dtype, int y_dtype, void* workspace,

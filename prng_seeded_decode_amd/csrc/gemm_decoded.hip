@@ -196,28 +196,14 @@ int launch_gemm_decoded(const seedlm_matrix* h, const void* x, void* y, int64_t 
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return SEEDLM_E_DEVICE;
   if (cur != h->device) return SEEDLM_E_INVALID;
-  // about eight workgroups per CU over all panels
-  const int64_t per_panel = (h->Mp * kPanelBlocks + kDecThreads - 1) / kDecThreads;
-  const int64_t gx = std::max<int64_t>(
-      1, std::min<int64_t>(per_panel, (8LL * device_cu_count() + h->np - 1) / h->np));
-  const dim3 grid((unsigned)gx, (unsigned)h->np);
-  if (h->C == 8)
-    hipLaunchKernelGGL(decode_f16_kernel<8>, grid, dim3(kDecThreads), 0, s,
-                       static_cast<const uint32_t*>(h->d_buf), 0u, static_cast<_Float16*>(ws),
-                       (int)h->rows, (int)h->cols, (int)h->Mp, (int)h->nb);
-  else
-    hipLaunchKernelGGL(decode_f16_kernel<12>, grid, dim3(kDecThreads), 0, s,
-                       static_cast<const uint32_t*>(h->d_buf), (uint32_t)h->exp_off,
-                       static_cast<_Float16*>(ws), (int)h->rows, (int)h->cols, (int)h->Mp,
-                       (int)h->nb);
-  SEEDLM_HIP_CHECK(hipGetLastError());
-
   // The workspace past the decoded matrix, up to kDecodedScratchBytes, is
   // offered to the GEMM as scratch.
   const size_t off = scratch_offset(h);
   const size_t scratch_max =
       ws_bytes > off ? std::min(ws_bytes - off, kDecodedScratchBytes) & ~(size_t)255 : 0;
   void* scratch = scratch_max ? static_cast<char*>(ws) + off : nullptr;
+  // The plan comes first, so that a shape the library cannot run fails before
+  // anything is enqueued.
   Blas& B = blas();
   std::lock_guard<std::mutex> lock(B.mu);
   if (h->device < 0 || h->device >= 64) return SEEDLM_E_DEVICE;
@@ -237,6 +223,22 @@ int launch_gemm_decoded(const seedlm_matrix* h, const void* x, void* y, int64_t 
     if (!make_plan(lt, h->rows, h->cols, ntok, scratch_max, p)) return SEEDLM_E_DEVICE;
     found = B.plans.emplace(key, p).first;
   }
+  // about eight workgroups per CU over all panels
+  const int64_t per_panel = (h->Mp * kPanelBlocks + kDecThreads - 1) / kDecThreads;
+  const int64_t gx = std::max<int64_t>(
+      1, std::min<int64_t>(per_panel, (8LL * device_cu_count() + h->np - 1) / h->np));
+  const dim3 grid((unsigned)gx, (unsigned)h->np);
+  if (h->C == 8)
+    hipLaunchKernelGGL(decode_f16_kernel<8>, grid, dim3(kDecThreads), 0, s,
+                       static_cast<const uint32_t*>(h->d_buf), 0u, static_cast<_Float16*>(ws),
+                       (int)h->rows, (int)h->cols, (int)h->Mp, (int)h->nb);
+  else
+    hipLaunchKernelGGL(decode_f16_kernel<12>, grid, dim3(kDecThreads), 0, s,
+                       static_cast<const uint32_t*>(h->d_buf), (uint32_t)h->exp_off,
+                       static_cast<_Float16*>(ws), (int)h->rows, (int)h->cols, (int)h->Mp,
+                       (int)h->nb);
+  SEEDLM_HIP_CHECK(hipGetLastError());
+
   const Plan& p = found->second;
   const float alpha = 0x1p-10f, beta = 0.f;
   const hipblasStatus_t st =
