@@ -45,22 +45,35 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-LUT_SOURCES = [os.path.join(ROOT, "prng_seeded_decode_amd", "csrc", f)
-               for f in ("gemv_lut.hip", "lut_common.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lut_kernel_llama3_70b_layer_4bit_traffic.txt")
+def _csrc(*names):
+    return [os.path.join(ROOT, "prng_seeded_decode_amd", "csrc", f) for f in names]
 
 
-def measured_traffic():
+# Committed HBM-traffic counter summaries of the batch-1 fused kernels, per workload
+# (config id), with the kernel sources they were taken on.
+TRAFFIC_FILES = {
+    4: (os.path.join(ROOT, "profiles", "gemv_lut_kernel_llama3_70b_layer_4bit_traffic.txt"),
+        _csrc("gemv_lut.hip", "lut_common.h")),
+    3: (os.path.join(ROOT, "profiles", "gemv_lut12_kernel_llama3_8b_layer_3bit_counters.txt"),
+        _csrc("gemv_lut12.hip", "lut_common.h")),
+}
+
+
+def measured_traffic(config_id):
     """HBM bytes per launch of the fused kernel from the committed counter summary,
-    or None when the kernel source has changed since the counters were taken."""
+    or None when there is none for the workload or the kernel source has changed
+    since the counters were taken."""
     import hashlib
 
+    if config_id not in TRAFFIC_FILES:
+        return None
+    path_txt, sources = TRAFFIC_FILES[config_id]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path_txt) as f:
             kv = dict(line.split(None, 1) for line in f
                       if line.strip() and not line.startswith("#"))
         h = hashlib.sha256()
-        for path in LUT_SOURCES:
+        for path in sources:
             with open(path, "rb") as f:
                 h.update(f.read())
         digest = h.hexdigest()
@@ -821,9 +834,9 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(float(achieved) / HBM_PEAK_GBPS, 4),
-            # counters were taken on the default workload (Llama-3-70B layer, batch 1)
-            "traffic": (measured_traffic() if kern_ms and args.config == 4 and batch == 1
-                        else None),
+            # counters were taken at batch 1 with the default kernel choice
+            "traffic": (measured_traffic(args.config)
+                        if kern_ms and batch == 1 and args.variant == 0 else None),
         },
         "fp16_baseline": fp16,
         "read_ceiling": ceiling,
