@@ -89,15 +89,20 @@ def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    # The part needs tens of milliseconds of load to reach its steady clocks: after
-    # 10 warm-up steps of the batch-1 layer the next 50 ran ~20% slower than the
-    # same steps later on.  Default: 200 steps of the decode-GEMV (~25 ms), 20 of
-    # the prefill GEMM (~100 ms), 3 seed searches (~300 ms).
+    # Warm-up steps (default 20; 3 seed searches).  The decode-GEMV modes then run
+    # a fixed-duration settle phase (--settle-ms) before timing: the part needs
+    # tens of milliseconds of load to reach its steady clocks, so a step count
+    # alone would make the result depend on the step's length.
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--config", type=int, default=4)
     p.add_argument("--batch", type=int, default=1)
     p.add_argument("--variant", type=int, default=0)
-    p.add_argument("--copies", type=int, default=2)
+    p.add_argument("--copies", type=int, default=0,
+                   help="rotated copies of the packed layer (default: enough to exceed 600 MB, "
+                        "2 to 64)")
+    p.add_argument("--settle-ms", type=float, default=150.0,
+                   help="wall-clock milliseconds of the same steps run after the warm-up and "
+                        "before timing, so that the GPU clocks have settled")
     p.add_argument("--no-fp16", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-read-ceiling", action="store_true",
@@ -554,7 +559,7 @@ def sweep_main(args):
 def main():
     args = parse_args()
     if args.warmup is None:
-        args.warmup = 3 if args.encode else (20 if args.gemm else 200)
+        args.warmup = 3 if args.encode else 20
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU per process only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -582,6 +587,12 @@ def main():
     batch = args.batch
 
     # ---- pack the layer (copies for rotation) ----
+    if args.copies <= 0:
+        # Enough copies that consecutive steps never find their weights in the
+        # 256 MB MALL (above 600 MB in all), between 2 and 64.
+        nbytes = sum(mat.rows * -(-mat.cols // cfg.C) * (4.5 if cfg.C == 12 else 4.0)
+                     for mat in cfg.matrices)
+        args.copies = int(min(64, max(2, -(-600e6 // nbytes))))
     mats = []  # per matrix: dict
     for mid, mat in enumerate(cfg.matrices):
         s, c, e = gen_records(cfg.config_id, mid, mat.rows, mat.cols, cfg.C, cfg.P)
@@ -620,15 +631,16 @@ def main():
 
     graphs = []
     if args.graph:
-        # Capture one step per rotated copy; the library's launches go to the
-        # capturing stream, so a replay runs the same kernels with no host work.
+        # Capture one step per rotated copy on a stream of our own; an eager
+        # step on it first gives it its scratch (no allocation while capturing).
+        cs = torch.cuda.Stream()
         for k in range(args.copies):
-            eager_step(k)
+            eager_step(k, st=cs)
         torch.cuda.synchronize()
         for k in range(args.copies):
             g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                eager_step(k, st=torch.cuda.current_stream())
+            with torch.cuda.graph(g, stream=cs):
+                eager_step(k, st=cs)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -638,23 +650,55 @@ def main():
         else:
             eager_step(k, phase)
 
-    # ---- whole-step timing ----
+    # ---- clock settle, then whole-step timing ----
     # The collector stays off while launches are timed: a collection pause in the
     # host loop could otherwise leave the GPU idle inside a timed interval.
     import gc
+
+    def settle(step_fn):
+        """Run step_fn for args.settle_ms of wall-clock time (the part needs tens
+        of milliseconds of load to reach its steady clocks); returns the count."""
+        n, t0 = 0, time.perf_counter()
+        while True:
+            for _ in range(10):
+                step_fn(n)
+                n += 1
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= args.settle_ms:
+                return n
 
     gc.disable()
     for k in range(args.warmup):
         run_step(k)
     torch.cuda.synchronize()
+    settle_steps = settle(run_step)
+    # One timed loop: events bracket the K steps (the step time) and, inside the
+    # same loop, every step's fused decode-GEMV launch records its own start and
+    # end (seedlm_bench_time_next_call: the events ride on the kernel dispatch,
+    # so they hold the kernel's execution and not the launch gap before it), so
+    # the dominant kernel's time comes from the very launches the step covers.
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    timed_kernel = args.variant == 0 and not graphs
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps if timed_kernel else 0)]
+    for a, b in kev:  # torch creates an event at its first record
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
     ev0.record(stream)
     for k in range(args.steps):
+        if timed_kernel:
+            S.seedlm_bench_time_next_call(*kev[k])
         run_step(k)
     ev1.record(stream)
     ev1.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in kev]
+    if kern_ms and float(np.mean(kern_ms)) > ms_per_step:
+        raise RuntimeError(f"kernel time {np.mean(kern_ms):.4f} ms exceeds the step time "
+                           f"{ms_per_step:.4f} ms: the timing is broken")
+    gc.enable()
 
     # ---- per-matrix timing: one seedlm_gemv per matrix, events around each ----
     per = {d["mat"].name: [] for d in mats}
@@ -672,20 +716,7 @@ def main():
     for name, a, b in evs:
         per[name].append(a.elapsed_time(b))
 
-    # ---- the dominant kernel alone: events around the fused decode-GEMV launch
-    # of each step (seedlm_gemv_many_begin), the panel reduction outside them ----
-    kern_ms = []
-    if args.variant == 0:
-        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for k, (a, b) in enumerate(kev):
-            a.record(stream)
-            run_step(k, "begin")
-            b.record(stream)
-            run_step(k, "end")
-        torch.cuda.synchronize()
-        kern_ms = [a.elapsed_time(b) for a, b in kev]
-    gc.enable()
+    torch.cuda.synchronize()
 
     layer_weights = sum(d["mat"].rows * d["mat"].cols for d in mats)
     layer_bytes = sum(d["bytes"] for d in mats)
@@ -711,6 +742,9 @@ def main():
     else:  # per-matrix variants: the step's launches together
         achieved = alg_bytes / (ms_per_step * 1e-3) / 1e9
     t_step = ms_per_step * 1e-3
+    traffic = (measured_traffic(args.config)
+               if kern_ms and batch == 1 and args.variant == 0 else None)
+    matrix_names = ",".join(mat.name for mat in cfg.matrices)
 
     # ---- fp16 baselines on the same shapes ----
     fp16 = None
@@ -736,6 +770,7 @@ def main():
             for k in range(args.warmup):
                 fp16_step(k, own)
             torch.cuda.synchronize()
+            settle(lambda k, own=own: fp16_step(k, own))
             ev0.record(stream)
             for k in range(args.steps):
                 fp16_step(k, own)
@@ -809,24 +844,34 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # the arithmetic of the path: fp32 table lookups and sums at batch 1
+        # (and for fp32 activations); fp16 MFMA operands with fp32 accumulation
+        # for an fp16 batch > 1
+        "dtype": "f16" if (batch > 1 and cfg.x_dtype == "f16") else "f32",
         "data": "synthetic",
         "config": {
-            "workload": (f"{cfg.name}: q,k,v,o,gate,up,down fused decode-GEMV, "
+            "workload": (f"{cfg.name}: {matrix_names} fused decode-GEMV, "
                          f"SeedLM C={cfg.C} P={cfg.P} K={cfg.K}, batch {batch}, "
                          f"x/y {cfg.x_dtype}"),
             "batch": batch,
+            "io_dtype": cfg.x_dtype,
             "compressed_bytes_per_step": layer_bytes,
             "weights_per_step": layer_weights,
             "rotated_copies": args.copies,
             "variant": args.variant,
             "graph": bool(graphs),
         },
+        "clock_settle": {"ms": args.settle_ms, "steps": settle_steps},
         "compressed_GBps": round(layer_bytes / t_step / 1e9, 1),
         "pct_hbm_peak": round(100 * layer_bytes / t_step / 1e9 / HBM_PEAK_GBPS, 2),
         "activation_bytes_per_step": act_bytes,
         "per_matrix": per_matrix or None,
         "kernel_us_per_launch": round(float(np.mean(kern_ms)) * 1e3, 2) if kern_ms else None,
+        "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 2) if kern_ms else None,
+        "kernel_timing": ("HIP events recorded by the fused decode-GEMV launch of each timed "
+                          "step itself (hipExtLaunchKernel start/stop events on the launch "
+                          "stream), inside the timed loop" if kern_ms else
+                          "the step's launches together"),
         "kernel_alg_bytes_per_launch": int(alg_bytes),
         "roofline": {
             "bound": "hbm",
@@ -835,9 +880,13 @@ def main():
             "unit": "GB/s",
             "frac": round(float(achieved) / HBM_PEAK_GBPS, 4),
             # counters were taken at batch 1 with the default kernel choice
-            "traffic": (measured_traffic(args.config)
-                        if kern_ms and batch == 1 and args.variant == 0 else None),
+            "traffic": traffic,
         },
+        "traffic_source": (f"stored: FETCH_SIZE + WRITE_SIZE per launch from two rocprofv3 "
+                           f"--pmc runs of this workload, scaled by a plain copy kernel's "
+                           f"reading ({os.path.relpath(TRAFFIC_FILES[args.config][0], ROOT)}); "
+                           f"valid while the kernel sources hash as they did then"
+                           if traffic is not None else None),
         "fp16_baseline": fp16,
         "read_ceiling": ceiling,
         "pct_read_ceiling": (round(100 * float(achieved) / ceiling["GBps"], 2) if ceiling else None),

@@ -104,9 +104,12 @@ SEEDLM_API int seedlm_pack_host(const uint16_t* seeds, const int8_t* coeffs,
 
 /*
  * seedlm_pack -- validate and pack records, upload them to the current device
- * and return a handle that owns the device copy (plus a small workspace for
- * split-reduction partials).  Synchronous.  The caller keeps ownership of the
- * host arrays (layouts as for seedlm_pack_host).
+ * and return a handle that owns the device copy and nothing else: the device
+ * memory of a packed matrix is its compressed bytes (seedlm_info).  The handle
+ * is immutable, so any calls may share it concurrently.  Synchronous.  The
+ * caller keeps ownership of the host arrays (layouts as for seedlm_pack_host).
+ * The first pack on a device also builds that device's 256 KiB table of LFSR
+ * extension bits (a measurement variant reads it; seedlm_bench.h).
  * Errors: as seedlm_pack_host, plus SEEDLM_E_NOMEM and SEEDLM_E_DEVICE.
  * Source: as seedlm_pack_host.
  */
@@ -125,11 +128,20 @@ SEEDLM_API int seedlm_pack(const uint16_t* seeds, const int8_t* coeffs,
  *   batch in [1, SEEDLM_MAX_BATCH].  batch 1 runs the fused decode-GEMV;
  *   batch > 1 decodes each weight tile once and contracts it on the matrix
  *   cores in fp16 with fp32 accumulation.
- * Asynchronous on `stream`.  Calls that share a handle use the handle's
- * workspace and must not overlap in time (serialise them on one stream).
- * Inputs must be finite.
- * Errors: SEEDLM_E_INVALID (null, batch out of range),
- * SEEDLM_E_UNSUPPORTED (dtype), SEEDLM_E_DEVICE (launch failure).
+ * Asynchronous on `stream`.  The kernels that split a row's reduction over
+ * workgroups write fp32 partials into scratch that the library keeps per
+ * (device, stream): calls on one stream share it in stream order, and calls on
+ * different streams -- with the same handle or not -- use different scratch, so
+ * they may overlap.  The first call on a stream, or one that needs more
+ * scratch than any earlier call on that stream, allocates it (hipMalloc: not
+ * inside graph capture, so run one call on a stream before capturing it);
+ * outgrown scratch stays allocated, so graphs captured from earlier calls stay
+ * valid, until seedlm_scratch_release frees all of it.
+ * seedlm_gemv_scratch_bytes gives a call's size.  Call with the device h was
+ * packed on current.  Inputs must be finite.
+ * Errors: SEEDLM_E_INVALID (null, batch out of range, another device current),
+ * SEEDLM_E_UNSUPPORTED (dtype), SEEDLM_E_NOMEM (scratch), SEEDLM_E_DEVICE
+ * (launch failure).
  */
 SEEDLM_API int seedlm_gemv(seedlm_handle h, const void* x, void* y, int batch,
                            int x_dtype, int y_dtype, void* stream);
@@ -142,10 +154,10 @@ SEEDLM_API int seedlm_gemv(seedlm_handle h, const void* x, void* y, int batch,
  * small matrices share the GPU and the per-launch cost is paid once; a decoder
  * layer's q/k/v/o/gate/up/down is the intended use (the pages' inference step,
  * applied to every weight matrix: paperhub.cn rebuttal text before Eq. (1)).
- *   handles  host array of n distinct handles (each call uses its handle's
- *            workspace, so a handle may appear only once)
+ *   handles  host array of n handles (a handle may appear more than once)
  *   x, y     host arrays of n device pointers, layouts as for seedlm_gemv
- * Errors: as seedlm_gemv; SEEDLM_E_INVALID for a repeated handle.
+ * Scratch as for seedlm_gemv: the partials of all n matrices, on `stream`.
+ * Errors: as seedlm_gemv.
  */
 SEEDLM_API int seedlm_gemv_many(const seedlm_handle* handles, const void* const* x,
                                 void* const* y, int n, int batch, int x_dtype, int y_dtype,
@@ -154,10 +166,10 @@ SEEDLM_API int seedlm_gemv_many(const seedlm_handle* handles, const void* const*
 /*
  * seedlm_gemv_many_begin / seedlm_gemv_many_end -- seedlm_gemv_many split in
  * two: _begin runs the fused decode-GEMV kernels (per-panel or per-chunk row
- * partials into the handles' workspaces), _end adds the partials into y.  Called
- * back to back with identical arguments they equal seedlm_gemv_many; the split
- * lets a caller time or overlap the two halves.  Between the two calls the
- * handles must not be used by any other call.
+ * partials into the stream's scratch), _end adds the partials into y.  Called
+ * with identical arguments on one stream they equal seedlm_gemv_many; the
+ * split lets a caller time the two halves.  Between the two calls no other
+ * gemv call may use that stream (it would reuse the scratch).
  */
 SEEDLM_API int seedlm_gemv_many_begin(const seedlm_handle* handles, const void* const* x,
                                       void* const* y, int n, int batch, int x_dtype,
@@ -167,12 +179,33 @@ SEEDLM_API int seedlm_gemv_many_end(const seedlm_handle* handles, const void* co
                                     void* stream);
 
 /*
+ * seedlm_gemv_scratch_bytes -- the scratch bytes seedlm_gemv_many(handles, n,
+ * batch, x_dtype, y_dtype) needs on its stream (0 when no kernel of the call
+ * splits a reduction).  Host only; no GPU use.  A layer's batch-1 call needs
+ * 4 bytes per (32-block panel, row) of each matrix: 13.4 MB for a Llama-3-70B
+ * layer beside its 428 MB of packed weights.
+ * Errors: SEEDLM_E_INVALID (null, batch), SEEDLM_E_UNSUPPORTED (dtype).
+ */
+SEEDLM_API int seedlm_gemv_scratch_bytes(const seedlm_handle* handles, int n, int batch,
+                                         int x_dtype, int y_dtype, size_t* bytes);
+
+/*
+ * seedlm_scratch_release -- free the gemv scratch of every stream on every
+ * device (each device is synchronised first; graphs captured from earlier
+ * calls must not be replayed afterwards).  Later calls allocate again.  Call
+ * it after destroying a stream that gemv calls used, before a new stream could
+ * take over its handle value.  Errors: SEEDLM_E_DEVICE.
+ */
+SEEDLM_API int seedlm_scratch_release(void);
+
+/*
  * seedlm_decode -- write the dense weights W[rows][cols] as fp32 (row-major,
  * caller-owned device memory).  Bit-exact: the block's integer sum times a
- * power of two is exact in fp32.  Asynchronous on `stream`.
+ * power of two is exact in fp32.  Asynchronous on `stream`; no scratch.  Call
+ * with the device h was packed on current.
  * Source: the block reconstruction of the abstract (paperdance.org) and the
  * "Approach" section (atlas.scime.ai).
- * Errors: SEEDLM_E_INVALID, SEEDLM_E_DEVICE.
+ * Errors: SEEDLM_E_INVALID (null, another device current), SEEDLM_E_DEVICE.
  */
 SEEDLM_API int seedlm_decode(seedlm_handle h, float* W_out, void* stream);
 
@@ -190,58 +223,6 @@ SEEDLM_API int seedlm_export(seedlm_handle h, void* host, size_t* bytes);
 SEEDLM_API const char* seedlm_status_string(int status);
 
 /*
- * Kernel variants, for A/B measurement.  The default (SEEDLM_VARIANT_AUTO) is
- * what seedlm_gemv runs: LUT for batch 1 (both formats), MFMA for every other
- * fp16-x/fp16-y call, SIMPLE otherwise (fp32 x or fp32 y, where the 1e-5 bar
- * needs fp32 weights).
- *   SEEDLM_VARIANT_LUT     batch 1, both formats: basis bits from GF(2) byte
- *                          tables in LDS, dot with x through activation byte
- *                          tables in LDS (per panel of 32 blocks for 4-bit,
- *                          per half panel for 3-bit)
- *   SEEDLM_VARIANT_TABLE   as LUT, basis bits from a 2^16-entry table in L2
- *   SEEDLM_VARIANT_SIMPLE  any shape: one wave per row, per-lane LFSR stepping,
- *                          fp32 weights
- *   SEEDLM_VARIANT_MFMA    fp16 x and y, any batch: each block decoded once to
- *                          fp16 (weights x 2^10) in MFMA operand registers,
- *                          v_mfma_f32_16x16x32_f16 over the batch (padded to
- *                          16); SEEDLM_E_UNSUPPORTED for other dtypes
- */
-#define SEEDLM_VARIANT_AUTO 0
-#define SEEDLM_VARIANT_LUT 1
-#define SEEDLM_VARIANT_TABLE 2
-#define SEEDLM_VARIANT_SIMPLE 3
-#define SEEDLM_VARIANT_MFMA 4
-SEEDLM_API int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch,
-                                   int x_dtype, int y_dtype, int variant, void* stream);
-
-/*
- * seedlm_fp16_gemv -- measurement baseline, not part of the method: a plain
- * fp16 GEMV y[batch][rows] = W[rows][cols] x[batch][cols] with fp16 W, x, y
- * and fp32 accumulation, used as the speed-up denominator (the pages compare
- * against an FP16 design: atlas.scime.ai "Key results").
- * All pointers are device memory; cols must be a multiple of 8.
- */
-SEEDLM_API int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t rows,
-                                int64_t cols, int batch, void* stream);
-
-/*
- * seedlm_stream_read -- measurement baseline, not part of the method: reads
- * `bytes` of device memory at `buf` once with 16-byte loads (a plain streaming
- * read; on a buffer larger than the last-level cache its rate is the HBM read
- * ceiling a bandwidth-bound kernel can approach on this device) and folds the
- * data into per-workgroup XOR checksums.
- *   buf   device memory, 16-byte aligned; bytes > 0 and a multiple of 16
- *   sink  device uint32[SEEDLM_STREAM_READ_SINK], caller-owned; the launch
- *         writes one checksum per workgroup into its leading entries (at most
- *         all of them) and leaves the rest untouched, so the XOR of a sink that
- *         started at zero equals the XOR of the buffer's 32-bit words
- * Asynchronous on `stream`.  Errors: SEEDLM_E_INVALID (null pointer, size or
- * alignment), SEEDLM_E_DEVICE (launch failure).
- */
-#define SEEDLM_STREAM_READ_SINK 8192
-SEEDLM_API int seedlm_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
-
-/*
  * seedlm_gemm -- Y = X W^T for any number of activation rows (prefill), with W
  * rebuilt from the handle's records inside the kernel and never stored in HBM
  * (paperhub.cn rebuttal text before Eq. (1): weights are reconstructed on the
@@ -254,8 +235,10 @@ SEEDLM_API int seedlm_stream_read(const void* buf, int64_t bytes, uint32_t* sink
  *   8, fp16 X and Y only; other dtypes return SEEDLM_E_UNSUPPORTED (for up to
  *   16 rows seedlm_gemv covers them), as do X or the packed buffer of 2 GiB or
  *   more and ntok above 16,776,960.
- * Asynchronous on `stream`; no workspace, so calls may overlap.
- * Errors: SEEDLM_E_INVALID (null, ntok < 1), SEEDLM_E_UNSUPPORTED (format,
+ * Asynchronous on `stream`; no scratch, so calls may overlap.  Call with the
+ * device h was packed on current.
+ * Errors: SEEDLM_E_INVALID (null, ntok < 1, another device current),
+ * SEEDLM_E_UNSUPPORTED (format,
  * dtype, alignment), SEEDLM_E_DEVICE (launch failure).
  */
 SEEDLM_API int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok,

@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     SeedLMMatrix,
     lib,
     pack_host_status,
+    seedlm_bench_time_next_call,
     seedlm_decode,
     seedlm_encode,
     seedlm_export,
@@ -34,8 +35,10 @@ from ._binding import (  # noqa: F401
     seedlm_gemm_decoded_bytes,
     seedlm_gemv,
     seedlm_gemv_many,
+    seedlm_gemv_scratch_bytes,
     seedlm_pack,
     seedlm_pack_host,
+    seedlm_scratch_release,
     seedlm_stream_read,
     status_string,
 )

@@ -35,11 +35,14 @@ EXPORTED = (
     "seedlm_gemv_many",
     "seedlm_gemv_many_begin",
     "seedlm_gemv_many_end",
+    "seedlm_gemv_scratch_bytes",
+    "seedlm_scratch_release",
     "seedlm_decode",
     "seedlm_destroy",
     "seedlm_info",
     "seedlm_export",
     "seedlm_status_string",
+    "seedlm_bench_time_next_call",
     "seedlm_fp16_gemv",
     "seedlm_stream_read",
     "seedlm_gemm",
@@ -91,12 +94,15 @@ def lib() -> ctypes.CDLL:
     L.seedlm_gemv_many.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
     L.seedlm_gemv_many_begin.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
     L.seedlm_gemv_many_end.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    L.seedlm_gemv_scratch_bytes.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.seedlm_scratch_release.argtypes = []
     L.seedlm_decode.argtypes = [vp, vp, vp]
     L.seedlm_destroy.argtypes = [vp]
     L.seedlm_info.argtypes = [vp, ctypes.POINTER(_Info)]
     L.seedlm_export.argtypes = [vp, vp, ctypes.POINTER(sz)]
     L.seedlm_status_string.argtypes = [i32]
     L.seedlm_status_string.restype = ctypes.c_char_p
+    L.seedlm_bench_time_next_call.argtypes = [vp, vp]
     L.seedlm_fp16_gemv.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     L.seedlm_stream_read.argtypes = [vp, i64, vp, vp]
     L.seedlm_gemm.argtypes = [vp, vp, vp, i64, i32, i32, vp]
@@ -234,10 +240,7 @@ def seedlm_gemv(m: SeedLMMatrix, x, y, batch=None, stream=None, variant=VARIANT_
     return y
 
 
-def seedlm_gemv_many(mats, xs, ys, batch=1, stream=None, phase="all"):
-    """ys[i] = W_i xs[i] for several packed matrices, in as few launches as possible.
-
-    phase "begin" / "end" runs only seedlm_gemv_many_begin / _end."""
+def _many_args(mats, xs, ys, batch):
     n = len(mats)
     if not (len(xs) == n and len(ys) == n):
         raise ValueError("mats, xs and ys must have the same length")
@@ -253,12 +256,34 @@ def seedlm_gemv_many(mats, xs, ys, batch=1, stream=None, phase="all"):
     Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
     xdt = _dtype_code(xs[0]) if n else F16
     ydt = _dtype_code(ys[0]) if n else F16
+    return (ctypes.cast(H, ctypes.c_void_p), ctypes.cast(X, ctypes.c_void_p),
+            ctypes.cast(Y, ctypes.c_void_p), n, batch, xdt, ydt)
+
+
+def seedlm_gemv_many(mats, xs, ys, batch=1, stream=None, phase="all"):
+    """ys[i] = W_i xs[i] for several packed matrices, in as few launches as possible.
+
+    phase "begin" / "end" runs only seedlm_gemv_many_begin / _end."""
     fn = {"all": lib().seedlm_gemv_many, "begin": lib().seedlm_gemv_many_begin,
           "end": lib().seedlm_gemv_many_end}[phase]
-    _check(fn(ctypes.cast(H, ctypes.c_void_p), ctypes.cast(X, ctypes.c_void_p),
-              ctypes.cast(Y, ctypes.c_void_p), n, batch, xdt, ydt, _stream_ptr(stream)),
-           "seedlm_gemv_many")
+    _check(fn(*_many_args(mats, xs, ys, batch), _stream_ptr(stream)), "seedlm_gemv_many")
     return ys
+
+
+def seedlm_gemv_scratch_bytes(mats, batch=1, x_dtype=F16, y_dtype=F16) -> int:
+    """Scratch bytes a seedlm_gemv_many call over mats needs on its stream."""
+    n = len(mats)
+    H = (ctypes.c_void_p * n)(*[m.handle.value for m in mats])
+    out = ctypes.c_size_t(0)
+    _check(lib().seedlm_gemv_scratch_bytes(ctypes.cast(H, ctypes.c_void_p), n, batch, x_dtype,
+                                           y_dtype, ctypes.byref(out)),
+           "seedlm_gemv_scratch_bytes")
+    return out.value
+
+
+def seedlm_scratch_release():
+    """Free the library's per-stream gemv scratch (synchronises the devices)."""
+    _check(lib().seedlm_scratch_release(), "seedlm_scratch_release")
 
 
 def seedlm_decode(m: SeedLMMatrix, W_out, stream=None):
@@ -335,6 +360,16 @@ def seedlm_stream_read(buf, sink, stream=None):
                                     ctypes.c_void_p(sink.data_ptr()), _stream_ptr(stream)),
            "seedlm_stream_read")
     return sink
+
+
+def seedlm_bench_time_next_call(start, stop):
+    """Measurement only: the next gemv call of this thread records torch.cuda.Event
+    `start` when its first main kernel starts and `stop` when its last one ends.
+    The events must exist already (torch creates an event at its first record)."""
+    ptr = [ctypes.c_void_p(e.cuda_event) if e is not None else None for e in (start, stop)]
+    if any(p is not None and not p.value for p in ptr):
+        raise ValueError("record each event once before handing it to the library")
+    _check(lib().seedlm_bench_time_next_call(*ptr), "seedlm_bench_time_next_call")
 
 
 def seedlm_fp16_gemv(W, x, y, batch=None, stream=None):

@@ -1,6 +1,7 @@
 // C-ABI entry points that launch kernels: argument checks and kernel choice.
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "lfsr_device.h"
 #include "seedlm_internal.h"
@@ -30,26 +31,264 @@ __global__ void ext_table_kernel(uint32_t* __restrict__ table) {
   if (s < 65536u) table[s] = (ext_bits<uint32_t>(s) & 0x00FFFFFFu) | ((s >> 8) << 24);
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_table_mu;
+uint32_t* g_ext_table[kMaxDevices] = {nullptr};
+
 bool dtype_ok(int d) { return d == SEEDLM_F32 || d == SEEDLM_F16; }
 
-int check_common(seedlm_handle h, const void* x, void* y, int batch, int xdt, int ydt) {
-  if (!h || !x || !y) return SEEDLM_E_INVALID;
+// Calls launch on the current device, which must be the one h was packed on.
+bool on_handle_device(const seedlm_matrix* h) {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess && dev == h->device;
+}
+
+// ---- per-stream scratch for the split reductions ----
+//
+// A call's partials live in a buffer of the library keyed by (device, stream),
+// never in a handle: calls on one stream run one after another on the GPU, so
+// they can share it, and calls on different streams get different buffers.  A
+// buffer that is too small is replaced by one at least twice its size; the old
+// one stays allocated (retired) until seedlm_scratch_release, so launches still
+// in flight, and graphs captured from earlier calls, keep valid memory.
+struct StreamScratch {
+  int device;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+std::mutex g_scratch_mu;
+std::vector<StreamScratch> g_scratch;
+std::vector<StreamScratch> g_retired;
+
+int stream_scratch(int dev, hipStream_t s, size_t bytes, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  StreamScratch* e = nullptr;
+  for (StreamScratch& c : g_scratch)
+    if (c.device == dev && c.stream == s) e = &c;
+  if (e && e->bytes >= bytes) {
+    *out = e->ptr;
+    return SEEDLM_OK;
+  }
+  size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+  if (e && want < 2 * e->bytes) want = 2 * e->bytes;
+  void* p = nullptr;
+  if (hipMalloc(&p, want) != hipSuccess) return SEEDLM_E_NOMEM;
+  if (e) {
+    g_retired.push_back(*e);
+    e->ptr = p;
+    e->bytes = want;
+  } else {
+    g_scratch.push_back(StreamScratch{dev, s, p, want});
+  }
+  *out = p;
+  return SEEDLM_OK;
+}
+
+// ---- timing events of the main kernels (measurement only) ----
+struct TimingEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local TimingEvents t_pending;  // set for the next call
+thread_local TimingEvents t_active;   // handed out during a call's main launches
+
+// ---- kernel choice and grouping ----
+
+enum Kind { kLut8, kLut12, kMfma, kSimple, kTable };
+
+struct Group {
+  int begin, count;
+  Kind kind;
+};
+
+// Matrices of one call are cut into launch groups: at batch 1 up to 8
+// consecutive matrices of one format (the table-lookup kernels), at batch > 1
+// with fp16 x and y up to 8 of any format (the matrix-core kernel, which
+// launches per format itself), otherwise one matrix at a time through the
+// exact per-lane kernel.  A variant other than AUTO applies to a single matrix.
+int make_groups(const seedlm_handle* hs, int n, int batch, int xdt, int ydt, int variant,
+                std::vector<Group>& out) {
+  const bool f16 = xdt == SEEDLM_F16 && ydt == SEEDLM_F16;
+  if (variant != SEEDLM_VARIANT_AUTO) {
+    if (n != 1) return SEEDLM_E_INVALID;
+    const int C = hs[0]->C;
+    switch (variant) {
+      case SEEDLM_VARIANT_LUT:
+        if (batch != 1) return SEEDLM_E_UNSUPPORTED;
+        out.push_back({0, 1, C == 8 ? kLut8 : kLut12});
+        return SEEDLM_OK;
+      case SEEDLM_VARIANT_TABLE:
+        if (batch != 1 || C != 8) return SEEDLM_E_UNSUPPORTED;
+        out.push_back({0, 1, kTable});
+        return SEEDLM_OK;
+      case SEEDLM_VARIANT_SIMPLE:
+        out.push_back({0, 1, kSimple});
+        return SEEDLM_OK;
+      case SEEDLM_VARIANT_MFMA:
+        if (!f16) return SEEDLM_E_UNSUPPORTED;
+        out.push_back({0, 1, kMfma});
+        return SEEDLM_OK;
+      default:
+        return SEEDLM_E_UNSUPPORTED;
+    }
+  }
+  int i = 0;
+  while (i < n) {
+    const int C = hs[i]->C;
+    int k = 0;
+    Kind kind = kSimple;
+    if (batch == 1) {
+      kind = C == 8 ? kLut8 : kLut12;
+      while (i + k < n && k < 8 && hs[i + k]->C == C) ++k;
+    } else if (f16) {
+      kind = kMfma;
+      while (i + k < n && k < 8) ++k;
+    } else {
+      k = 1;
+    }
+    out.push_back({i, k, kind});
+    i += k;
+  }
+  return SEEDLM_OK;
+}
+
+constexpr int64_t kScratchAlign = 64;  // floats (256 bytes) between matrices
+
+int64_t partial_floats(Kind kind, const seedlm_matrix* h, int batch) {
+  int64_t f = 0;
+  switch (kind) {
+    case kLut8:
+    case kTable: f = lut_partial_floats(h); break;
+    case kLut12: f = lut12_partial_floats(h); break;
+    case kMfma: f = mfma_partial_floats(h, batch); break;
+    default: f = 0;
+  }
+  return (f + kScratchAlign - 1) / kScratchAlign * kScratchAlign;
+}
+
+int64_t total_partial_floats(const seedlm_handle* hs, const std::vector<Group>& groups,
+                             int batch) {
+  int64_t total = 0;
+  for (const Group& g : groups)
+    for (int j = 0; j < g.count; ++j) total += partial_floats(g.kind, hs[g.begin + j], batch);
+  return total;
+}
+
+int check_call(const seedlm_handle* hs, const void* const* x, void* const* y, int n, int batch,
+               int xdt, int ydt) {
+  if (!hs || !x || !y || n < 0) return SEEDLM_E_INVALID;
   if (batch < 1 || batch > SEEDLM_MAX_BATCH) return SEEDLM_E_INVALID;
   if (!dtype_ok(xdt) || !dtype_ok(ydt)) return SEEDLM_E_UNSUPPORTED;
+  for (int i = 0; i < n; ++i)
+    if (!hs[i] || !x[i] || !y[i]) return SEEDLM_E_INVALID;
+  int dev = -1;
+  if (n > 0 && hipGetDevice(&dev) != hipSuccess) return SEEDLM_E_DEVICE;
+  for (int i = 0; i < n; ++i)
+    if (hs[i]->device != dev) return SEEDLM_E_INVALID;  // packed on another device
+  return SEEDLM_OK;
+}
+
+// Where a call's partials go.
+enum ScratchSource { kStreamScratch };
+
+// The body of every gemv entry point: phases & 1 runs the main kernels, phases
+// & 2 the reductions of the split ones.  The exact per-lane kernel has no
+// reduction and runs whole in phase 1.
+int run_gemv(const seedlm_handle* hs, const void* const* x, void* const* y, int n, int batch,
+             int xdt, int ydt, int variant, void* stream, int phases, ScratchSource src) {
+  // Timing events asked for apply to this call's main kernels only.
+  struct ActiveEvents {
+    explicit ActiveEvents(bool main) {
+      if (main) {
+        t_active = t_pending;
+        t_pending = TimingEvents{};
+      }
+    }
+    ~ActiveEvents() { t_active = TimingEvents{}; }
+  } active_events(phases & 1);
+  int st = check_call(hs, x, y, n, batch, xdt, ydt);
+  if (st != SEEDLM_OK || n == 0) return st;
+  std::vector<Group> groups;
+  st = make_groups(hs, n, batch, xdt, ydt, variant, groups);
+  if (st != SEEDLM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t total = total_partial_floats(hs, groups, batch);
+  float* base = nullptr;
+  if (total > 0 && src == kStreamScratch) {
+    void* p = nullptr;
+    st = stream_scratch(hs[0]->device, s, (size_t)total * sizeof(float), &p);
+    if (st != SEEDLM_OK) return st;
+    base = static_cast<float*>(p);
+  }
+  int64_t off = 0;
+  for (const Group& g : groups) {
+    const seedlm_matrix* gh[8];
+    float* parts[8];
+    for (int j = 0; j < g.count; ++j) {
+      gh[j] = hs[g.begin + j];
+      const int64_t f = partial_floats(g.kind, gh[j], batch);
+      parts[j] = f > 0 ? base + off : nullptr;
+      off += f;
+    }
+    const void* const* gx = x + g.begin;
+    void* const* gy = y + g.begin;
+    switch (g.kind) {
+      case kLut8:
+      case kTable: {
+        const uint32_t* table = nullptr;
+        if (g.kind == kTable) {
+          table = ext_table(gh[0]->device);
+          if (!table) return SEEDLM_E_DEVICE;
+        }
+        st = launch_gemv_lut_group(gh, gx, gy, parts, g.count, xdt, ydt, table, s, phases);
+        break;
+      }
+      case kLut12:
+        st = launch_gemv_lut12_group(gh, gx, gy, parts, g.count, xdt, ydt, s, phases);
+        break;
+      case kMfma:
+        st = launch_gemv_mfma_group(gh, gx, gy, parts, g.count, batch, xdt, ydt, s, phases);
+        break;
+      case kSimple:
+        st = (phases & 1) ? launch_gemv_simple(gh[0], gx[0], gy[0], batch, xdt, ydt, s)
+                          : SEEDLM_OK;
+        break;
+    }
+    if (st != SEEDLM_OK) return st;
+  }
   return SEEDLM_OK;
 }
 
 }  // namespace
 
 // The 2^16-entry table of extension bits b[16..47] (the TABLE variant keeps it
-// resident in L2 / the MALL instead of rebuilding the bits per block).
-int build_ext_table(seedlm_matrix* h) {
-  if (h->d_ext_table) return SEEDLM_OK;
-  SEEDLM_HIP_CHECK(hipMalloc((void**)&h->d_ext_table, 65536 * sizeof(uint32_t)));
-  hipLaunchKernelGGL(ext_table_kernel, dim3(256), dim3(256), 0, 0, h->d_ext_table);
-  SEEDLM_HIP_CHECK(hipGetLastError());
-  SEEDLM_HIP_CHECK(hipDeviceSynchronize());
+// resident in L2 / the MALL instead of rebuilding the bits per block), one per
+// device, built synchronously by the first seedlm_pack there.
+int ensure_ext_table(int device) {
+  if (device < 0 || device >= kMaxDevices) return SEEDLM_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_table_mu);
+  if (g_ext_table[device]) return SEEDLM_OK;
+  uint32_t* t = nullptr;
+  if (hipMalloc((void**)&t, 65536 * sizeof(uint32_t)) != hipSuccess) return SEEDLM_E_NOMEM;
+  hipLaunchKernelGGL(ext_table_kernel, dim3(256), dim3(256), 0, 0, t);
+  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(nullptr) != hipSuccess) {
+    (void)hipFree(t);
+    return SEEDLM_E_DEVICE;
+  }
+  g_ext_table[device] = t;
   return SEEDLM_OK;
+}
+
+void main_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = t_active.start;
+  *stop = t_active.stop;
+  t_active.start = nullptr;  // only the first main launch records the start
+}
+
+const uint32_t* ext_table(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_table_mu);
+  return g_ext_table[device];
 }
 
 }  // namespace seedlm
@@ -60,111 +299,75 @@ extern "C" {
 
 int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch, int x_dtype,
                         int y_dtype, int variant, void* stream) {
-  int st = check_common(h, x, y, batch, x_dtype, y_dtype);
-  if (st != SEEDLM_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (variant) {
-    case SEEDLM_VARIANT_AUTO:
-      if (batch == 1 && h->C == 8) return launch_gemv_lut(h, x, y, x_dtype, y_dtype, false, s);
-      if (batch == 1 && h->C == 12)
-        return launch_gemv_lut12_group(&h, &x, &y, 1, x_dtype, y_dtype, s, 3);
-      if (x_dtype == SEEDLM_F16 && y_dtype == SEEDLM_F16)
-        return launch_gemv_mfma(h, x, y, batch, x_dtype, y_dtype, s);
-      return launch_gemv_simple(h, x, y, batch, x_dtype, y_dtype, s);
-    case SEEDLM_VARIANT_LUT:
-      if (batch != 1) return SEEDLM_E_UNSUPPORTED;
-      if (h->C == 12) return launch_gemv_lut12_group(&h, &x, &y, 1, x_dtype, y_dtype, s, 3);
-      return launch_gemv_lut(h, x, y, x_dtype, y_dtype, false, s);
-    case SEEDLM_VARIANT_TABLE: {
-      if (batch != 1 || h->C != 8) return SEEDLM_E_UNSUPPORTED;
-      st = build_ext_table(h);
-      if (st != SEEDLM_OK) return st;
-      return launch_gemv_lut(h, x, y, x_dtype, y_dtype, true, s);
-    }
-    case SEEDLM_VARIANT_SIMPLE:
-      return launch_gemv_simple(h, x, y, batch, x_dtype, y_dtype, s);
-    case SEEDLM_VARIANT_MFMA:
-      return launch_gemv_mfma(h, x, y, batch, x_dtype, y_dtype, s);
-    default:
-      return SEEDLM_E_UNSUPPORTED;
-  }
+  return run_gemv(&h, &x, &y, 1, batch, x_dtype, y_dtype, variant, stream, 3, kStreamScratch);
 }
 
 int seedlm_gemv(seedlm_handle h, const void* x, void* y, int batch, int x_dtype, int y_dtype,
                 void* stream) {
-  return seedlm_gemv_variant(h, x, y, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, stream);
+  return run_gemv(&h, &x, &y, 1, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, stream, 3,
+                  kStreamScratch);
 }
-
-namespace {
-
-// Shared body of seedlm_gemv_many{,_begin,_end}: phases & 1 runs the main
-// kernels, phases & 2 the panel reductions.  Matrices outside the grouped
-// batch-1 paths run their whole seedlm_gemv in phase 1.
-int gemv_many_phases(const seedlm_handle* handles, const void* const* x, void* const* y, int n,
-                     int batch, int x_dtype, int y_dtype, void* stream, int phases) {
-  if (!handles || !x || !y || n < 0) return SEEDLM_E_INVALID;
-  for (int i = 0; i < n; ++i) {
-    const int st = check_common(handles[i], x[i], y[i], batch, x_dtype, y_dtype);
-    if (st != SEEDLM_OK) return st;
-    for (int j = 0; j < i; ++j)
-      if (handles[j] == handles[i]) return SEEDLM_E_INVALID;  // shared workspace
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int i = 0;
-  const bool mfma = batch > 1 && x_dtype == SEEDLM_F16 && y_dtype == SEEDLM_F16;
-  while (i < n) {
-    // Group up to 8 consecutive matrices: at batch 1 those of one format (the
-    // table-lookup kernels), at batch > 1 with fp16 x and y any of them (the
-    // matrix-core kernel, which launches per format itself).
-    const int C = handles[i]->C;
-    int k = 0;
-    while (batch == 1 && i + k < n && k < 8 && handles[i + k]->C == C &&
-           handles[i + k]->bytes < 0x80000000ull)
-      ++k;
-    while (mfma && i + k < n && k < 8) ++k;
-    if (k >= 1) {
-      const seedlm_matrix* hs[8];
-      for (int j = 0; j < k; ++j) hs[j] = handles[i + j];
-      int st;
-      if (mfma)
-        st = launch_gemv_mfma_group(hs, x + i, y + i, k, batch, x_dtype, y_dtype, s, phases);
-      else if (C == 8)
-        st = launch_gemv_lut_group(hs, x + i, y + i, k, x_dtype, y_dtype, false, s, phases);
-      else
-        st = launch_gemv_lut12_group(hs, x + i, y + i, k, x_dtype, y_dtype, s, phases);
-      if (st != SEEDLM_OK) return st;
-      i += k;
-    } else {
-      if (phases & 1) {
-        const int st = seedlm_gemv_variant(handles[i], x[i], y[i], batch, x_dtype, y_dtype,
-                                           SEEDLM_VARIANT_AUTO, stream);
-        if (st != SEEDLM_OK) return st;
-      }
-      ++i;
-    }
-  }
-  return SEEDLM_OK;
-}
-
-}  // namespace
 
 int seedlm_gemv_many(const seedlm_handle* handles, const void* const* x, void* const* y, int n,
                      int batch, int x_dtype, int y_dtype, void* stream) {
-  return gemv_many_phases(handles, x, y, n, batch, x_dtype, y_dtype, stream, 3);
+  return run_gemv(handles, x, y, n, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, stream, 3,
+                  kStreamScratch);
 }
 
 int seedlm_gemv_many_begin(const seedlm_handle* handles, const void* const* x, void* const* y,
                            int n, int batch, int x_dtype, int y_dtype, void* stream) {
-  return gemv_many_phases(handles, x, y, n, batch, x_dtype, y_dtype, stream, 1);
+  return run_gemv(handles, x, y, n, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, stream, 1,
+                  kStreamScratch);
 }
 
 int seedlm_gemv_many_end(const seedlm_handle* handles, const void* const* x, void* const* y,
                          int n, int batch, int x_dtype, int y_dtype, void* stream) {
-  return gemv_many_phases(handles, x, y, n, batch, x_dtype, y_dtype, stream, 2);
+  return run_gemv(handles, x, y, n, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, stream, 2,
+                  kStreamScratch);
+}
+
+int seedlm_gemv_scratch_bytes(const seedlm_handle* handles, int n, int batch, int x_dtype,
+                              int y_dtype, size_t* bytes) {
+  if (!handles || n < 0 || !bytes) return SEEDLM_E_INVALID;
+  if (batch < 1 || batch > SEEDLM_MAX_BATCH) return SEEDLM_E_INVALID;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return SEEDLM_E_UNSUPPORTED;
+  for (int i = 0; i < n; ++i)
+    if (!handles[i]) return SEEDLM_E_INVALID;
+  std::vector<Group> groups;
+  const int st = make_groups(handles, n, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, groups);
+  if (st != SEEDLM_OK) return st;
+  *bytes = (size_t)total_partial_floats(handles, groups, batch) * sizeof(float);
+  return SEEDLM_OK;
+}
+
+int seedlm_bench_time_next_call(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return SEEDLM_E_INVALID;
+  t_pending.start = static_cast<hipEvent_t>(start_event);
+  t_pending.stop = static_cast<hipEvent_t>(stop_event);
+  return SEEDLM_OK;
+}
+
+int seedlm_scratch_release(void) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return SEEDLM_E_DEVICE;
+  int rc = SEEDLM_OK;
+  for (std::vector<StreamScratch>* list : {&g_scratch, &g_retired}) {
+    for (StreamScratch& e : *list) {
+      if (!e.ptr) continue;
+      if (hipSetDevice(e.device) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+          hipFree(e.ptr) != hipSuccess)
+        rc = SEEDLM_E_DEVICE;
+    }
+    list->clear();
+  }
+  if (hipSetDevice(cur) != hipSuccess) rc = SEEDLM_E_DEVICE;
+  return rc;
 }
 
 int seedlm_decode(seedlm_handle h, float* W_out, void* stream) {
   if (!h || !W_out) return SEEDLM_E_INVALID;
+  if (!on_handle_device(h)) return SEEDLM_E_INVALID;
   return launch_decode(h, W_out, static_cast<hipStream_t>(stream));
 }
 
@@ -184,6 +387,7 @@ int seedlm_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_
 int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok, int x_dtype, int y_dtype,
                 void* stream) {
   if (!h || !X || !Y || ntok < 1) return SEEDLM_E_INVALID;
+  if (!on_handle_device(h)) return SEEDLM_E_INVALID;
   return launch_gemm(h, X, Y, ntok, x_dtype, y_dtype, static_cast<hipStream_t>(stream));
 }
 

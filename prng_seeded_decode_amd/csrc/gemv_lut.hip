@@ -378,8 +378,8 @@ __global__ void __launch_bounds__(kThreads, 1)
   }
 }
 
-bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys, int n,
-                LutGroup& grp) {
+bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys,
+                float* const* partials, int n, LutGroup& grp) {
   if (n < 1 || n > kMaxGroup) return false;
   grp = LutGroup{};
   grp.n = n;
@@ -387,10 +387,11 @@ bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* con
     const seedlm_matrix* h = hs[i];
     if (h->C != 8 || h->P != 3 || h->bytes >= 0x80000000ull) return false;
     if (h->Mp >= (1 << 28) || h->cols >= (1 << 30)) return false;
+    if (h->np * h->Mp * 4 >= (1LL << 31)) return false;  // partial offsets are 32-bit
     LutMatrix& M = grp.m[i];
     M.words = static_cast<const uint32_t*>(h->d_buf);
     M.x = xs[i];
-    M.partial = h->d_work;
+    M.partial = partials[i];
     M.y = ys[i];
     M.words_bytes = (uint32_t)h->bytes;
     M.Mp = (int)h->Mp;
@@ -405,38 +406,35 @@ bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* con
 
 template <typename XT, bool kGT>
 void launch_main(const LutGroup& grp, const uint32_t* table, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_lut_kernel<XT, kGT>), dim3((unsigned)grp.grid), dim3(kThreads), 0, s,
-                     grp, table);
+  hipEvent_t e0, e1;
+  main_launch_events(&e0, &e1);
+  hipExtLaunchKernelGGL((gemv_lut_kernel<XT, kGT>), dim3((unsigned)grp.grid), dim3(kThreads), 0,
+                        s, e0, e1, 0, grp, table);
 }
 
 }  // namespace
 
+// One fp32 partial per (panel, padded row).
+int64_t lut_partial_floats(const seedlm_matrix* h) { return h->np * h->Mp; }
+
 int launch_gemv_lut_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys,
-                          int n, int xdt, int ydt, bool global_table, hipStream_t s, int phases) {
+                          float* const* partials, int n, int xdt, int ydt,
+                          const uint32_t* ext_table, hipStream_t s, int phases) {
   LutGroup grp;
-  if (!fill_group(hs, xs, ys, n, grp)) return SEEDLM_E_UNSUPPORTED;
+  if (!fill_group(hs, xs, ys, partials, n, grp)) return SEEDLM_E_UNSUPPORTED;
   if (phases & 1) {
-    const uint32_t* table = nullptr;
-    if (global_table) {
-      if (n != 1 || !hs[0]->d_ext_table) return SEEDLM_E_INVALID;
-      table = hs[0]->d_ext_table;
-    }
+    const bool global_table = ext_table != nullptr;
     if (xdt == SEEDLM_F32) {
-      if (global_table) launch_main<float, true>(grp, table, s);
-      else launch_main<float, false>(grp, table, s);
+      if (global_table) launch_main<float, true>(grp, ext_table, s);
+      else launch_main<float, false>(grp, ext_table, s);
     } else {
-      if (global_table) launch_main<__half, true>(grp, table, s);
-      else launch_main<__half, false>(grp, table, s);
+      if (global_table) launch_main<__half, true>(grp, ext_table, s);
+      else launch_main<__half, false>(grp, ext_table, s);
     }
     SEEDLM_HIP_CHECK(hipGetLastError());
   }
   if (phases & 2) return launch_reduce(grp, ydt, s);
   return SEEDLM_OK;
-}
-
-int launch_gemv_lut(const seedlm_matrix* h, const void* x, void* y, int xdt, int ydt,
-                    bool global_table, hipStream_t s) {
-  return launch_gemv_lut_group(&h, &x, &y, 1, xdt, ydt, global_table, s, 3);
 }
 
 }  // namespace seedlm

@@ -407,8 +407,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
   }
 }
 
-bool fill_group12(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys, int n,
-                  LutGroup& grp) {
+int64_t units_of(const seedlm_matrix* h) { return (h->nb + kSlots - 1) / kSlots; }
+
+bool fill_group12(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys,
+                  float* const* partials, int n, LutGroup& grp) {
   if (n < 1 || n > kMaxGroup) return false;
   grp = LutGroup{};
   grp.n = n;
@@ -416,12 +418,12 @@ bool fill_group12(const seedlm_matrix* const* hs, const void* const* xs, void* c
     const seedlm_matrix* h = hs[i];
     if (h->C != 12 || h->P != 4 || h->bytes >= 0x80000000ull) return false;
     if (h->Mp >= (1 << 27) || h->cols >= (1 << 30)) return false;
-    const int64_t units = (h->nb + kSlots - 1) / kSlots;
-    if ((size_t)units * h->Mp * sizeof(float) > h->work_bytes) return false;
+    const int64_t units = units_of(h);
+    if (units * h->Mp * 4 >= (1LL << 31)) return false;  // partial offsets are 32-bit
     LutMatrix& M = grp.m[i];
     M.words = static_cast<const uint32_t*>(h->d_buf);
     M.x = xs[i];
-    M.partial = h->d_work;
+    M.partial = partials[i];
     M.y = ys[i];
     M.words_bytes = (uint32_t)h->bytes;
     M.exp_off = (uint32_t)h->exp_off;
@@ -437,17 +439,23 @@ bool fill_group12(const seedlm_matrix* const* hs, const void* const* xs, void* c
 
 }  // namespace
 
+// One fp32 partial per (column unit, padded row).
+int64_t lut12_partial_floats(const seedlm_matrix* h) { return units_of(h) * h->Mp; }
+
 int launch_gemv_lut12_group(const seedlm_matrix* const* hs, const void* const* xs,
-                            void* const* ys, int n, int xdt, int ydt, hipStream_t s, int phases) {
+                            void* const* ys, float* const* partials, int n, int xdt, int ydt,
+                            hipStream_t s, int phases) {
   LutGroup grp;
-  if (!fill_group12(hs, xs, ys, n, grp)) return SEEDLM_E_UNSUPPORTED;
+  if (!fill_group12(hs, xs, ys, partials, n, grp)) return SEEDLM_E_UNSUPPORTED;
   if (phases & 1) {
+    hipEvent_t e0, e1;
+    main_launch_events(&e0, &e1);
     if (xdt == SEEDLM_F32)
-      hipLaunchKernelGGL((gemv_lut12_kernel<float>), dim3((unsigned)grp.grid), dim3(kThreads), 0,
-                         s, grp);
+      hipExtLaunchKernelGGL((gemv_lut12_kernel<float>), dim3((unsigned)grp.grid), dim3(kThreads),
+                            0, s, e0, e1, 0, grp);
     else
-      hipLaunchKernelGGL((gemv_lut12_kernel<__half>), dim3((unsigned)grp.grid), dim3(kThreads), 0,
-                         s, grp);
+      hipExtLaunchKernelGGL((gemv_lut12_kernel<__half>), dim3((unsigned)grp.grid), dim3(kThreads),
+                            0, s, e0, e1, 0, grp);
     SEEDLM_HIP_CHECK(hipGetLastError());
   }
   if (phases & 2) return launch_reduce(grp, ydt, s);

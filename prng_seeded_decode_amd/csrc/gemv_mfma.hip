@@ -29,9 +29,10 @@
 // the GPU otherwise).
 //
 // Work split: a workgroup (4 waves, 256 or 64 rows) takes a contiguous chunk
-// of panels; chunks write fp32 partials into the handle's workspace and
+// of panels; chunks write fp32 partials and
 // reduce_chunks_kernel adds them in a fixed order (deterministic).  With a
-// single chunk the kernel writes y directly.
+// single chunk the kernel writes y directly.  The partials live in scratch
+// that the caller passes per matrix (chunks * batch * Mp floats).
 #include <hip/hip_fp16.h>
 
 #include "lfsr_device.h"
@@ -329,15 +330,15 @@ namespace {
 // The split of one matrix: tiling (256-row tiles where they give about four
 // workgroups per CU over the panels, 64-row tiles for smaller matrices) and
 // panel chunks to reach that many workgroups.
-int plan_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, MfmaArgs& a,
-              bool& wide) {
+int plan_mfma(const seedlm_matrix* h, const void* x, void* y, float* partial, int batch,
+              MfmaArgs& a, bool& wide) {
   if (h->bytes >= 0x80000000ull || h->Mp >= (1 << 30) ||
       (int64_t)batch * h->cols * 2 >= (1LL << 31))
     return SEEDLM_E_UNSUPPORTED;
   a = MfmaArgs{};
   a.words = static_cast<const uint32_t*>(h->d_buf);
   a.x = static_cast<const __half*>(x);
-  a.partial = h->d_work;
+  a.partial = partial;
   a.y = static_cast<__half*>(y);
   a.buf_bytes = (uint32_t)h->bytes;
   a.exp_off = (uint32_t)h->exp_off;
@@ -356,21 +357,30 @@ int plan_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, MfmaArg
   if (chunks > a.np) chunks = a.np;
   a.chunk_panels = (int)((a.np + chunks - 1) / chunks);
   a.chunks = (a.np + a.chunk_panels - 1) / a.chunk_panels;
-  if ((size_t)a.chunks * batch * h->Mp * sizeof(float) > h->work_bytes) return SEEDLM_E_INVALID;
   if ((int64_t)a.tiles * a.chunks >= (1LL << 30)) return SEEDLM_E_UNSUPPORTED;
   return SEEDLM_OK;
 }
 
 template <int C, int RW>
 void launch_main(const MfmaGroup& g, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_mfma_kernel<C, RW>), dim3((unsigned)grid), dim3(kThreads), 0, s, g);
+  hipEvent_t e0, e1;
+  main_launch_events(&e0, &e1);
+  hipExtLaunchKernelGGL((gemv_mfma_kernel<C, RW>), dim3((unsigned)grid), dim3(kThreads), 0, s, e0,
+                        e1, 0, g);
 }
 
 }  // namespace
 
+int64_t mfma_partial_floats(const seedlm_matrix* h, int batch) {
+  MfmaArgs a;
+  bool wide;
+  if (plan_mfma(h, nullptr, nullptr, nullptr, batch, a, wide) != SEEDLM_OK) return 0;
+  return a.chunks == 1 ? 0 : (int64_t)a.chunks * batch * h->Mp;
+}
+
 int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs,
-                           void* const* ys, int n, int batch, int xdt, int ydt, hipStream_t s,
-                           int phases) {
+                           void* const* ys, float* const* partials, int n, int batch, int xdt,
+                           int ydt, hipStream_t s, int phases) {
   if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
   if (batch < 1 || batch > kBatchPad) return SEEDLM_E_INVALID;
   if (n < 1 || n > kMaxMfmaGroup) return SEEDLM_E_INVALID;
@@ -378,8 +388,9 @@ int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs
   bool wide[kMaxMfmaGroup];
   for (int i = 0; i < n; ++i) {
     if (hs[i]->C != 8 && hs[i]->C != 12) return SEEDLM_E_UNSUPPORTED;
-    const int st = plan_mfma(hs[i], xs[i], ys[i], batch, args[i], wide[i]);
+    const int st = plan_mfma(hs[i], xs[i], ys[i], partials[i], batch, args[i], wide[i]);
     if (st != SEEDLM_OK) return st;
+    if (args[i].chunks > 1 && !partials[i]) return SEEDLM_E_INVALID;
   }
   if (phases & 1) {
     // One launch per (format, tiling) present.
@@ -426,11 +437,6 @@ int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs
     }
   }
   return SEEDLM_OK;
-}
-
-int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
-                     hipStream_t s) {
-  return launch_gemv_mfma_group(&h, &x, &y, 1, batch, xdt, ydt, s, 3);
 }
 
 }  // namespace seedlm

@@ -154,17 +154,16 @@ int seedlm_pack(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps,
   h->nwords = L.nwords;
   h->bytes = L.bytes;
   h->exp_off = L.exp_off;
-  // Partials of the split reduction: one float per (batch column, panel, row).
-  h->work_bytes = (size_t)SEEDLM_MAX_BATCH * L.np * L.Mp * sizeof(float);
 
   int rc = SEEDLM_OK;
   if (hipGetDevice(&h->device) != hipSuccess) rc = SEEDLM_E_DEVICE;
   if (rc == SEEDLM_OK && hipMalloc(&h->d_buf, L.bytes) != hipSuccess) rc = SEEDLM_E_NOMEM;
-  if (rc == SEEDLM_OK && hipMalloc((void**)&h->d_work, h->work_bytes) != hipSuccess)
-    rc = SEEDLM_E_NOMEM;
   if (rc == SEEDLM_OK && hipMemcpy(h->d_buf, host, L.bytes, hipMemcpyHostToDevice) != hipSuccess)
     rc = SEEDLM_E_DEVICE;
   hipHostFree(host);
+  // The device's 2^16-entry extension table (TABLE variant) is built here, once
+  // per device, so that no gemv call allocates or synchronises for it.
+  if (rc == SEEDLM_OK) rc = ensure_ext_table(h->device);
   if (rc != SEEDLM_OK) {
     seedlm_destroy(h);
     return rc;
@@ -177,8 +176,6 @@ int seedlm_destroy(seedlm_handle h) {
   if (!h) return SEEDLM_OK;
   int rc = SEEDLM_OK;
   if (h->d_buf && hipFree(h->d_buf) != hipSuccess) rc = SEEDLM_E_DEVICE;
-  if (h->d_work && hipFree(h->d_work) != hipSuccess) rc = SEEDLM_E_DEVICE;
-  if (h->d_ext_table && hipFree(h->d_ext_table) != hipSuccess) rc = SEEDLM_E_DEVICE;
   delete h;
   return rc;
 }

@@ -2,11 +2,13 @@
 // HIP kernels of libseedlm.  Not part of the public ABI (see include/seedlm.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/seedlm.h"
+#include "../../include/seedlm_bench.h"
 
 namespace seedlm {
 
@@ -19,7 +21,8 @@ constexpr uint32_t kPadWord = 0x00000001u;  // seed 1, t = 0, g = 0
 
 }  // namespace seedlm
 
-// The handle.  Immutable after seedlm_pack except for the workspace contents.
+// The handle.  Immutable after seedlm_pack: it owns the packed buffer and
+// nothing else, so calls that share it may run concurrently.
 struct seedlm_matrix {
   int64_t rows = 0, cols = 0;
   int C = 0, P = 0, K = 0;
@@ -32,9 +35,6 @@ struct seedlm_matrix {
   size_t exp_off = 0;   // byte offset of the exponent nibble array (P == 4)
   int device = 0;
   void* d_buf = nullptr;      // packed buffer (device)
-  float* d_work = nullptr;    // split-reduction partials (device)
-  size_t work_bytes = 0;
-  uint32_t* d_ext_table = nullptr;  // 2^16-entry extension table (variant TABLE)
 };
 
 // An encoder: the per-seed table of one format on one device.
@@ -80,25 +80,32 @@ __host__ __device__ inline int exp_nibble(int64_t r, int64_t b) {
 }
 
 // Launch wrappers implemented in the .hip files.  All return a status code.
+//
+// The batch-1 table-lookup kernels and the matrix-core kernel split a matrix's
+// reduction over workgroups and write fp32 partials, which a second launch adds
+// in a fixed order.  The partials live in caller-side scratch, not in the
+// handle: *_partial_floats gives the floats one matrix needs, and the group
+// launches take one partial pointer per matrix (`partials`, device memory).
 int launch_decode(const seedlm_matrix* h, float* W, hipStream_t s);
 int launch_gemv_simple(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt,
                        int ydt, hipStream_t s);
-int launch_gemv_lut(const seedlm_matrix* h, const void* x, void* y, int xdt, int ydt,
-                    bool global_table, hipStream_t s);
+int64_t lut_partial_floats(const seedlm_matrix* h);    // 4-bit, batch 1
+int64_t lut12_partial_floats(const seedlm_matrix* h);  // 3-bit, batch 1
+int64_t mfma_partial_floats(const seedlm_matrix* h, int batch);  // 0 when unsplit
 // Up to 8 batch-1 4-bit matrices in one main launch (phases & 1: panel
-// partials into the handles' workspaces) and one reduce launch (phases & 2: y).
+// partials) and one reduce launch (phases & 2: y).  ext_table: NULL for the
+// GF(2) byte tables in LDS, or the 2^16-entry table of extension bits.
 int launch_gemv_lut_group(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys,
-                          int n, int xdt, int ydt, bool global_table, hipStream_t s, int phases);
-// Matrix-core path (fp16 x and y only; E_UNSUPPORTED otherwise).
+                          float* const* partials, int n, int xdt, int ydt,
+                          const uint32_t* ext_table, hipStream_t s, int phases);
 int launch_gemv_lut12_group(const seedlm_matrix* const* hs, const void* const* xs,
-                            void* const* ys, int n, int xdt, int ydt, hipStream_t s, int phases);
-int launch_gemv_mfma(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
-                     hipStream_t s);
+                            void* const* ys, float* const* partials, int n, int xdt, int ydt,
+                            hipStream_t s, int phases);
 // Up to 8 matrices at batch > 1 (fp16): phases & 1 the decode-GEMM launches
 // (one per format and tiling present), phases & 2 one reduction launch.
 int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs,
-                           void* const* ys, int n, int batch, int xdt, int ydt, hipStream_t s,
-                           int phases);
+                           void* const* ys, float* const* partials, int n, int batch, int xdt,
+                           int ydt, hipStream_t s, int phases);
 // Prefill GEMM (both packed formats, fp16 X and Y; E_UNSUPPORTED otherwise).
 int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
                 hipStream_t s);
@@ -112,7 +119,10 @@ int launch_gemm_decoded(const seedlm_matrix* h, const void* x, void* y, int64_t 
                         int ydt, void* ws, size_t ws_bytes, hipStream_t s);
 int launch_fp16_gemv(const void* W, const void* x, void* y, int64_t rows, int64_t cols,
                      int batch, hipStream_t s);
-int build_ext_table(seedlm_matrix* h);
+// The 2^16-entry table of extension bits (TABLE variant), one per device: built
+// by the first seedlm_pack on a device; NULL before that.
+int ensure_ext_table(int device);
+const uint32_t* ext_table(int device);
 // Seed search: per-seed QR table (bytes for format C) and the search itself.
 bool encoder_format_supported(int C, int P, int K, int Q);
 size_t encoder_table_bytes(int C, int P, int K, int Q);
@@ -123,6 +133,14 @@ int launch_encode(int C, int P, int K, int Q, const void* table, const void* W, 
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
+
+// Timing of the main (decode-GEMV) kernels of one gemv call, for measurement
+// only (seedlm_bench_time_next_call).  While a call launches its main kernels,
+// main_launch_events() hands out the caller's events: the start event to the
+// first main launch (recorded when that kernel starts), the stop event to every
+// main launch (the last record wins, at the end of the last kernel).  Both are
+// null when no timing was asked for.  Per host thread.
+void main_launch_events(hipEvent_t* start, hipEvent_t* stop);
 
 }  // namespace seedlm
 

@@ -19,9 +19,12 @@ def _lib():
 
 def test_library_exports_every_declared_symbol():
     S = _lib()
-    header = open(os.path.join(ROOT, "include", "seedlm.h")).read()
-    names = re.findall(r"SEEDLM_API\s+[\w\s\*]+?\b(seedlm_\w+)\s*\(", header)
-    assert len(names) >= 10
+    names = []
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            header = open(os.path.join(ROOT, "include", h)).read()
+            names += re.findall(r"SEEDLM_API\s+[\w\s\*]+?\b(seedlm_\w+)\s*\(", header)
+    assert len(names) >= 10 and len(names) == len(set(names))
     L = S.lib()
     for n in names:
         assert hasattr(L, n), n
