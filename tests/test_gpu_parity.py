@@ -473,3 +473,37 @@ def test_gemv_many_more_than_one_group(batch):
     for y, y1, W_ref, x in zip(ys, single, refs, xs):
         assert O.normwise_error(y.float().cpu().numpy(), O.gemv(W_ref, x)) <= TOL["f16"]
         assert torch.equal(y, y1)
+
+
+def test_bench_timing_events_span_the_main_kernels():
+    # seedlm_bench_time_next_call: the next call's main kernels record the two
+    # events; the interval lies inside the call's own bracket, and the results
+    # are those of an untimed call.
+    S = _S()
+    dev = _dev()
+    rng = np.random.default_rng(61)
+    shapes = [(8, 3, 4096, 4096), (8, 3, 1024, 4096)]
+    mats, xs = [], []
+    for C, P, rows, cols in shapes:
+        s, c, e = _random_records(rng, rows, cols, C, P, (-12, -6))
+        mats.append(_pack(s, c, e, rows, cols, C, P))
+        xs.append(torch.from_numpy(rng.standard_normal((1, cols)).astype(np.float16)).to(dev))
+    ref = [torch.empty((1, m.rows), dtype=torch.float16, device=dev) for m in mats]
+    S.seedlm_gemv_many(mats, xs, ref)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    stream = torch.cuda.current_stream()
+    for e in ev:
+        e.record(stream)
+    torch.cuda.synchronize()
+    ys = [torch.empty_like(y) for y in ref]
+    ev[0].record(stream)
+    S.seedlm_bench_time_next_call(ev[1], ev[2])
+    S.seedlm_gemv_many(mats, xs, ys)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    kern, whole = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    _say(f"main kernel {kern * 1e3:.1f} us of a {whole * 1e3:.1f} us call")
+    assert 0 < kern < whole
+    assert all(torch.equal(a, b) for a, b in zip(ys, ref))
+    with pytest.raises(S.SeedLMError):
+        S.seedlm_bench_time_next_call(ev[1], None)
