@@ -67,6 +67,7 @@ extern "C" {
 #define SEEDLM_E_UNSUPPORTED (-2) /* (C, P, K) or dtype combination not supported  */
 #define SEEDLM_E_NOMEM (-3)       /* host or device allocation failed              */
 #define SEEDLM_E_DEVICE (-4)      /* a HIP runtime call failed                     */
+#define SEEDLM_E_SCRATCH_LIMIT (-5) /* needs more than the no-alloc scratch maximum */
 
 /* Element types for activations and outputs. */
 #define SEEDLM_F32 0
@@ -177,6 +178,27 @@ SEEDLM_API int seedlm_gemv_many_begin(const seedlm_handle* handles, const void* 
 SEEDLM_API int seedlm_gemv_many_end(const seedlm_handle* handles, const void* const* x,
                                     void* const* y, int n, int batch, int x_dtype, int y_dtype,
                                     void* stream);
+
+/*
+ * seedlm_gemv_many_noalloc -- seedlm_gemv_many for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels, results and arguments,
+ * with the partials in a fixed scratch array of SEEDLM_NOALLOC_SCRATCH_BYTES
+ * that every device the library runs on holds until the process ends (its
+ * device address is looked up once per device, on the first call there).  No
+ * hipMalloc, hipFree or other allocating call is made.  The array is shared by
+ * every call on a device and keeps the last call's contents: calls that
+ * overlap in time on one device race (serialise them, e.g. on one stream).
+ * Nothing in it needs clearing between calls.  A call whose partials exceed
+ * the array (seedlm_gemv_scratch_bytes) returns SEEDLM_E_SCRATCH_LIMIT before
+ * launching anything: every batch-1 call on a Llama-3-70B layer fits (13.4 MB),
+ * and its batch-8 call (41 MB).
+ * Errors: as seedlm_gemv_many, and SEEDLM_E_SCRATCH_LIMIT.
+ */
+#define SEEDLM_NOALLOC_SCRATCH_BYTES (64u << 20)
+SEEDLM_API int seedlm_gemv_many_noalloc(const seedlm_handle* handles, const void* const* x,
+                                        void* const* y, int n, int batch, int x_dtype,
+                                        int y_dtype, void* stream);
 
 /*
  * seedlm_gemv_scratch_bytes -- the scratch bytes seedlm_gemv_many(handles, n,

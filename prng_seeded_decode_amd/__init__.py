@@ -9,6 +9,8 @@ from ._binding import (  # noqa: F401
     E_DEVICE,
     E_INVALID,
     E_NOMEM,
+    E_SCRATCH_LIMIT,
+    NOALLOC_SCRATCH_BYTES,
     E_UNSUPPORTED,
     F16,
     F32,
@@ -35,6 +37,7 @@ from ._binding import (  # noqa: F401
     seedlm_gemm_decoded_bytes,
     seedlm_gemv,
     seedlm_gemv_many,
+    seedlm_gemv_many_noalloc,
     seedlm_gemv_scratch_bytes,
     seedlm_pack,
     seedlm_pack_host,

@@ -18,6 +18,8 @@ E_INVALID = -1
 E_UNSUPPORTED = -2
 E_NOMEM = -3
 E_DEVICE = -4
+E_SCRATCH_LIMIT = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 F32 = 0
 F16 = 1
 MAX_BATCH = 16
@@ -35,6 +37,7 @@ EXPORTED = (
     "seedlm_gemv_many",
     "seedlm_gemv_many_begin",
     "seedlm_gemv_many_end",
+    "seedlm_gemv_many_noalloc",
     "seedlm_gemv_scratch_bytes",
     "seedlm_scratch_release",
     "seedlm_decode",
@@ -94,6 +97,7 @@ def lib() -> ctypes.CDLL:
     L.seedlm_gemv_many.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
     L.seedlm_gemv_many_begin.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
     L.seedlm_gemv_many_end.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    L.seedlm_gemv_many_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
     L.seedlm_gemv_scratch_bytes.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
     L.seedlm_scratch_release.argtypes = []
     L.seedlm_decode.argtypes = [vp, vp, vp]
@@ -267,6 +271,14 @@ def seedlm_gemv_many(mats, xs, ys, batch=1, stream=None, phase="all"):
     fn = {"all": lib().seedlm_gemv_many, "begin": lib().seedlm_gemv_many_begin,
           "end": lib().seedlm_gemv_many_end}[phase]
     _check(fn(*_many_args(mats, xs, ys, batch), _stream_ptr(stream)), "seedlm_gemv_many")
+    return ys
+
+
+def seedlm_gemv_many_noalloc(mats, xs, ys, batch=1, stream=None):
+    """seedlm_gemv_many with the partials in the library's fixed device scratch
+    (no allocation; calls that overlap on one device race)."""
+    _check(lib().seedlm_gemv_many_noalloc(*_many_args(mats, xs, ys, batch), _stream_ptr(stream)),
+           "seedlm_gemv_many_noalloc")
     return ys
 
 

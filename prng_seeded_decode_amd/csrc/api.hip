@@ -106,8 +106,10 @@ struct Group {
 // with fp16 x and y up to 8 of any format (the matrix-core kernel, which
 // launches per format itself), otherwise one matrix at a time through the
 // exact per-lane kernel.  A variant other than AUTO applies to a single matrix.
-int make_groups(const seedlm_handle* hs, int n, int batch, int xdt, int ydt, int variant,
-                std::vector<Group>& out) {
+// next_group gives the group that starts at matrix i (no heap allocation, so
+// the no-alloc entry point can use it too).
+int next_group(const seedlm_handle* hs, int n, int batch, int xdt, int ydt, int variant, int i,
+               Group* g) {
   const bool f16 = xdt == SEEDLM_F16 && ydt == SEEDLM_F16;
   if (variant != SEEDLM_VARIANT_AUTO) {
     if (n != 1) return SEEDLM_E_INVALID;
@@ -115,40 +117,36 @@ int make_groups(const seedlm_handle* hs, int n, int batch, int xdt, int ydt, int
     switch (variant) {
       case SEEDLM_VARIANT_LUT:
         if (batch != 1) return SEEDLM_E_UNSUPPORTED;
-        out.push_back({0, 1, C == 8 ? kLut8 : kLut12});
+        *g = {0, 1, C == 8 ? kLut8 : kLut12};
         return SEEDLM_OK;
       case SEEDLM_VARIANT_TABLE:
         if (batch != 1 || C != 8) return SEEDLM_E_UNSUPPORTED;
-        out.push_back({0, 1, kTable});
+        *g = {0, 1, kTable};
         return SEEDLM_OK;
       case SEEDLM_VARIANT_SIMPLE:
-        out.push_back({0, 1, kSimple});
+        *g = {0, 1, kSimple};
         return SEEDLM_OK;
       case SEEDLM_VARIANT_MFMA:
         if (!f16) return SEEDLM_E_UNSUPPORTED;
-        out.push_back({0, 1, kMfma});
+        *g = {0, 1, kMfma};
         return SEEDLM_OK;
       default:
         return SEEDLM_E_UNSUPPORTED;
     }
   }
-  int i = 0;
-  while (i < n) {
-    const int C = hs[i]->C;
-    int k = 0;
-    Kind kind = kSimple;
-    if (batch == 1) {
-      kind = C == 8 ? kLut8 : kLut12;
-      while (i + k < n && k < 8 && hs[i + k]->C == C) ++k;
-    } else if (f16) {
-      kind = kMfma;
-      while (i + k < n && k < 8) ++k;
-    } else {
-      k = 1;
-    }
-    out.push_back({i, k, kind});
-    i += k;
+  const int C = hs[i]->C;
+  int k = 0;
+  Kind kind = kSimple;
+  if (batch == 1) {
+    kind = C == 8 ? kLut8 : kLut12;
+    while (i + k < n && k < 8 && hs[i + k]->C == C) ++k;
+  } else if (f16) {
+    kind = kMfma;
+    while (i + k < n && k < 8) ++k;
+  } else {
+    k = 1;
   }
+  *g = {i, k, kind};
   return SEEDLM_OK;
 }
 
@@ -166,12 +164,17 @@ int64_t partial_floats(Kind kind, const seedlm_matrix* h, int batch) {
   return (f + kScratchAlign - 1) / kScratchAlign * kScratchAlign;
 }
 
-int64_t total_partial_floats(const seedlm_handle* hs, const std::vector<Group>& groups,
-                             int batch) {
-  int64_t total = 0;
-  for (const Group& g : groups)
-    for (int j = 0; j < g.count; ++j) total += partial_floats(g.kind, hs[g.begin + j], batch);
-  return total;
+// Scratch floats of a whole call (the matrices' ranges one after another).
+int total_partial_floats(const seedlm_handle* hs, int n, int batch, int xdt, int ydt,
+                         int variant, int64_t* total) {
+  *total = 0;
+  Group g;
+  for (int i = 0; i < n; i += g.count) {
+    const int st = next_group(hs, n, batch, xdt, ydt, variant, i, &g);
+    if (st != SEEDLM_OK) return st;
+    for (int j = 0; j < g.count; ++j) *total += partial_floats(g.kind, hs[g.begin + j], batch);
+  }
+  return SEEDLM_OK;
 }
 
 int check_call(const seedlm_handle* hs, const void* const* x, void* const* y, int n, int batch,
@@ -188,8 +191,35 @@ int check_call(const seedlm_handle* hs, const void* const* x, void* const* y, in
   return SEEDLM_OK;
 }
 
-// Where a call's partials go.
-enum ScratchSource { kStreamScratch };
+// Where a call's partials go: the library's per-stream scratch (allocated on
+// demand), or the static scratch of the no-alloc entry point.
+enum ScratchSource { kStreamScratch, kStaticScratch };
+
+// ---- static scratch of seedlm_gemv_many_noalloc ----
+//
+// A file-scope device array: every device the library runs on holds its own
+// copy (kStaticScratchBytes) until the process ends.  In host code `scratch` is
+// only a stand-in for the symbol, never a device address: its address on a
+// device comes from hipGetSymbolAddress, taken once per device with that device
+// current and kept in g_static_ptr; kernels get that pointer.  The main kernels
+// write every partial the reductions read, so nothing needs clearing between
+// calls; calls that overlap on one device share the array and race.
+constexpr size_t kStaticScratchBytes = SEEDLM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {nullptr};
+
+int static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return SEEDLM_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SEEDLM_E_DEVICE;
+    g_static_ptr[dev] = p;
+  }
+  *out = g_static_ptr[dev];
+  return SEEDLM_OK;
+}
 
 // The body of every gemv entry point: phases & 1 runs the main kernels, phases
 // & 2 the reductions of the split ones.  The exact per-lane kernel has no
@@ -208,20 +238,27 @@ int run_gemv(const seedlm_handle* hs, const void* const* x, void* const* y, int 
   } active_events(phases & 1);
   int st = check_call(hs, x, y, n, batch, xdt, ydt);
   if (st != SEEDLM_OK || n == 0) return st;
-  std::vector<Group> groups;
-  st = make_groups(hs, n, batch, xdt, ydt, variant, groups);
+  int64_t total = 0;
+  st = total_partial_floats(hs, n, batch, xdt, ydt, variant, &total);
   if (st != SEEDLM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t total = total_partial_floats(hs, groups, batch);
   float* base = nullptr;
-  if (total > 0 && src == kStreamScratch) {
+  if (total > 0) {
     void* p = nullptr;
-    st = stream_scratch(hs[0]->device, s, (size_t)total * sizeof(float), &p);
+    if (src == kStreamScratch) {
+      st = stream_scratch(hs[0]->device, s, (size_t)total * sizeof(float), &p);
+    } else {
+      if ((size_t)total * sizeof(float) > kStaticScratchBytes) return SEEDLM_E_SCRATCH_LIMIT;
+      st = static_scratch(hs[0]->device, &p);
+    }
     if (st != SEEDLM_OK) return st;
     base = static_cast<float*>(p);
   }
   int64_t off = 0;
-  for (const Group& g : groups) {
+  Group g;
+  for (int i = 0; i < n; i += g.count) {
+    st = next_group(hs, n, batch, xdt, ydt, variant, i, &g);
+    if (st != SEEDLM_OK) return st;
     const seedlm_matrix* gh[8];
     float* parts[8];
     for (int j = 0; j < g.count; ++j) {
@@ -314,6 +351,12 @@ int seedlm_gemv_many(const seedlm_handle* handles, const void* const* x, void* c
                   kStreamScratch);
 }
 
+int seedlm_gemv_many_noalloc(const seedlm_handle* handles, const void* const* x, void* const* y,
+                             int n, int batch, int x_dtype, int y_dtype, void* stream) {
+  return run_gemv(handles, x, y, n, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, stream, 3,
+                  kStaticScratch);
+}
+
 int seedlm_gemv_many_begin(const seedlm_handle* handles, const void* const* x, void* const* y,
                            int n, int batch, int x_dtype, int y_dtype, void* stream) {
   return run_gemv(handles, x, y, n, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, stream, 1,
@@ -333,10 +376,11 @@ int seedlm_gemv_scratch_bytes(const seedlm_handle* handles, int n, int batch, in
   if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return SEEDLM_E_UNSUPPORTED;
   for (int i = 0; i < n; ++i)
     if (!handles[i]) return SEEDLM_E_INVALID;
-  std::vector<Group> groups;
-  const int st = make_groups(handles, n, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, groups);
+  int64_t total = 0;
+  const int st =
+      total_partial_floats(handles, n, batch, x_dtype, y_dtype, SEEDLM_VARIANT_AUTO, &total);
   if (st != SEEDLM_OK) return st;
-  *bytes = (size_t)total_partial_floats(handles, groups, batch) * sizeof(float);
+  *bytes = (size_t)total * sizeof(float);
   return SEEDLM_OK;
 }
 

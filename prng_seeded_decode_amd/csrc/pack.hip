@@ -100,6 +100,7 @@ const char* seedlm_status_string(int status) {
     case SEEDLM_E_UNSUPPORTED: return "unsupported format or dtype";
     case SEEDLM_E_NOMEM: return "out of memory";
     case SEEDLM_E_DEVICE: return "HIP runtime error";
+    case SEEDLM_E_SCRATCH_LIMIT: return "the call needs more scratch than the no-alloc maximum";
     default: return "unknown status";
   }
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     S = _lib()
-    for code in (S.OK, S.E_INVALID, S.E_UNSUPPORTED, S.E_NOMEM, S.E_DEVICE):
+    for code in (S.OK, S.E_INVALID, S.E_UNSUPPORTED, S.E_NOMEM, S.E_DEVICE, S.E_SCRATCH_LIMIT):
         assert S.status_string(code) not in ("", "unknown status")
     assert S.status_string(12345) == "unknown status"
 
