@@ -16,31 +16,40 @@
  *     the rebuttal on shared exponents.
  *
  * Format fixed by this library (the pages leave these open):
- *   LFSR      16-bit Fibonacci, right shift: z' = (z >> 1) | (f << 15) with
- *             f = bit0 ^ bit2 ^ bit3 ^ bit5 of z (x^16 + x^5 + x^3 + x^2 + 1,
- *             period 65535).  The seed is the first state, z_0 = s, s != 0.
- *   values    v_n = (z_n - 2^15) / 2^15.
+ *   LFSR      K-bit Fibonacci, right shift: z' = (z >> 1) | (f << (K-1)); for
+ *             K = 16, f = bit0 ^ bit2 ^ bit3 ^ bit5 of z (x^16 + x^5 + x^3 +
+ *             x^2 + 1); for K = 20, f = bit0 ^ bit3 (x^20 + x^3 + 1); both of
+ *             period 2^K - 1.  The seed is the first state, z_0 = s, s != 0.
+ *   values    v_n = (z_n - 2^(K-1)) / 2^(K-1).
  *   U(s)      column-major: U[i][j] = v_{j*C + i}, i < C, j < P.
- *   block     w_i = 2^e * sum_j U[i][j] * t_j, t_j in [-8, 7], e in [-15, 0].
+ *   block     w_i = 2^e * sum_j U[i][j] * t_j, t_j Q-bit two's complement
+ *             ([-8, 7] for Q = 4), e in [-15, 0].
  *   blocks    lie along a row: block b of row r holds columns b*C .. b*C+C-1;
  *             nb = ceil(cols / C); the last block keeps its first
  *             cols - (nb-1)*C weights.
- *   word      uint32 per block: bits 0..15 seed, 16..19 t0, 20..23 t1,
- *             24..27 t2 (two's-complement nibbles);
- *             (C,P)=(8,3):  bits 28..31 g = e + 15;
- *             (C,P)=(12,4): bits 28..31 t3, and g sits in a nibble array.
+ *   formats   (C, P, K, Q): (8, 3, 16, 4) 4 bits per weight and (12, 4, 16, 4)
+ *             3 bits per weight, the pages' formats; (8, 4, 16, 3) 4 bits and
+ *             (12, 3, 20, 4) 3 bits, which spend the same bits on a fourth
+ *             latent column with 3-bit coefficients or on a 20-bit seed (the
+ *             knobs the pages name below 3 bits: paperhub.cn, answer on
+ *             1.5-2.5 bits per weight).  Q follows from (C, P, K).
+ *   word      uint32 per block: bits 0..K-1 seed, bits K+Q*j .. K+Q*j+Q-1 t_j;
+ *             C = 8: bits 28..31 g = e + 15; C = 12: the word is full and g
+ *             sits in a nibble array.
  *   panels    rows are padded to Mp = 8*ceil(rows/8); blocks are grouped in
- *             panels of 32: panel p holds blocks 32p .. 32p+Wp-1,
- *             Wp = min(32, nb-32p), stored Wp' = 4*ceil(Wp/4) slots wide.
- *             Padding (rows >= rows, slots >= Wp) holds pad words 0x00000001
- *             (seed 1, t = 0, g = 0).  Panel p starts at word p*Mp*32 and stores
- *             its Mp rows one after another, Wp' words each; slot q of row r
- *             sits at 4*(q/4) + ((q-r) mod 4) of the row (groups of four slots
- *             rotated by the row index).  For (12,4) the exponent of (r, b) is
- *             nibble ((q-r) mod 4) of uint16 number p*Mp*8 + r*(Wp'/4) + q/4
- *             of an array starting at byte align256(4 * total words).
- *   Supported (C, P, K): (8, 3, 16) -- 4 bits per weight; (12, 4, 16) -- 3 bits
- *   per weight (36 bits per 12-weight block).
+ *             panels of PB = 32 (C = 8) or PB = 16 (C = 12) blocks: panel p
+ *             holds blocks PB*p .. PB*p+Wp-1, Wp = min(PB, nb-PB*p), stored
+ *             Wp' = 4*ceil(Wp/4) slots wide.  Padding (rows >= rows, slots
+ *             >= Wp) holds pad words 0x00000001 (seed 1, t = 0, g = 0).  Panel
+ *             p starts at word p*Mp*PB and stores its Mp rows one after
+ *             another, Wp' words each; slot q of row r sits at
+ *             4*(q/4) + ((q-r) mod 4) of the row (groups of four slots rotated
+ *             by the row index).  For C = 12 the exponent of (r, b) is nibble
+ *             ((q-r) mod 4) of uint16 number p*Mp*(PB/4) + r*(Wp'/4) + q/4 of
+ *             an array starting at byte align256(4 * total words).
+ *   Kernels   every call takes every format; the batch-1 table-lookup and
+ *             matrix-core kernels run the pages' two formats, the others run
+ *             the exact per-lane kernel (seedlm_gemv) and seedlm_decode.
  *
  * Conventions: every call returns a status (0 = SEEDLM_OK, negative = error);
  * no C++ exception crosses this boundary.  "device" pointers are HIP device
@@ -85,12 +94,13 @@ typedef struct seedlm_info_t {
   int64_t blocks_per_row;   /* nb = ceil(N / C) */
   int64_t stored_blocks_per_row; /* nb with the last panel padded to 4 slots */
   int64_t compressed_bytes; /* size of the packed buffer, padding included */
+  int32_t Q;                /* coefficient width in bits */
 } seedlm_info_t;
 
 /*
  * seedlm_pack_host -- write the packed layout into host memory (no GPU use).
- *   seeds  host uint16 [rows][nb], each in [1, 65535]
- *   coeffs host int8   [rows][nb][P], each in [-8, 7]
+ *   seeds  host uint16 [rows][nb] (uint32 for K = 20), each in [1, 2^K - 1]
+ *   coeffs host int8   [rows][nb][P], each Q-bit: in [-8, 7], or [-4, 3] for Q = 3
  *   exps   host int8   [rows][nb], each in [-15, 0]
  *   dst    host buffer of *bytes bytes, or NULL to query the size.
  * On entry *bytes is the capacity of dst; on return it is the layout size.
@@ -99,7 +109,7 @@ typedef struct seedlm_info_t {
  * Source: the per-block record {seed, coefficients, shared exponent} of the
  * pages (atlas.scime.ai "Approach"; paperhub.cn rebuttal on shared exponents).
  */
-SEEDLM_API int seedlm_pack_host(const uint16_t* seeds, const int8_t* coeffs,
+SEEDLM_API int seedlm_pack_host(const void* seeds, const int8_t* coeffs,
                                 const int8_t* exps, int64_t rows, int64_t cols,
                                 int C, int P, int K, void* dst, size_t* bytes);
 
@@ -114,7 +124,7 @@ SEEDLM_API int seedlm_pack_host(const uint16_t* seeds, const int8_t* coeffs,
  * Errors: as seedlm_pack_host, plus SEEDLM_E_NOMEM and SEEDLM_E_DEVICE.
  * Source: as seedlm_pack_host.
  */
-SEEDLM_API int seedlm_pack(const uint16_t* seeds, const int8_t* coeffs,
+SEEDLM_API int seedlm_pack(const void* seeds, const int8_t* coeffs,
                            const int8_t* exps, int64_t rows, int64_t cols,
                            int C, int P, int K, seedlm_handle* out);
 

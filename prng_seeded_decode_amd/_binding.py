@@ -73,6 +73,7 @@ class _Info(ctypes.Structure):
         ("blocks_per_row", ctypes.c_int64),
         ("stored_blocks_per_row", ctypes.c_int64),
         ("compressed_bytes", ctypes.c_int64),
+        ("Q", ctypes.c_int32),
     ]
 
 
@@ -131,9 +132,9 @@ def _check(status: int, what: str):
         raise SeedLMError(status, what)
 
 
-def _records(seeds, coeffs, exps, rows, cols, C, P):
+def _records(seeds, coeffs, exps, rows, cols, C, P, K=16):
     nb = -(-cols // C)
-    seeds = np.ascontiguousarray(seeds, dtype=np.uint16)
+    seeds = np.ascontiguousarray(seeds, dtype=np.uint16 if K <= 16 else np.uint32)
     coeffs = np.ascontiguousarray(coeffs, dtype=np.int8)
     exps = np.ascontiguousarray(exps, dtype=np.int8)
     if seeds.shape != (rows, nb) or coeffs.shape != (rows, nb, P) or exps.shape != (rows, nb):
@@ -147,7 +148,7 @@ def _ptr(a: np.ndarray):
 
 def seedlm_pack_host(seeds, coeffs, exps, rows, cols, C, P, K=16) -> bytes:
     """Packed layout written on the host (no GPU involved)."""
-    seeds, coeffs, exps = _records(seeds, coeffs, exps, rows, cols, C, P)
+    seeds, coeffs, exps = _records(seeds, coeffs, exps, rows, cols, C, P, K)
     n = ctypes.c_size_t(0)
     _check(lib().seedlm_pack_host(_ptr(seeds), _ptr(coeffs), _ptr(exps), rows, cols, C, P, K,
                                   None, ctypes.byref(n)), "seedlm_pack_host")
@@ -160,7 +161,7 @@ def seedlm_pack_host(seeds, coeffs, exps, rows, cols, C, P, K=16) -> bytes:
 
 def pack_host_status(seeds, coeffs, exps, rows, cols, C, P, K=16) -> int:
     """Raw status of seedlm_pack_host on arbitrary arrays (for error-path tests)."""
-    seeds = np.ascontiguousarray(seeds, dtype=np.uint16)
+    seeds = np.ascontiguousarray(seeds, dtype=np.uint16 if K <= 16 else np.uint32)
     coeffs = np.ascontiguousarray(coeffs, dtype=np.int8)
     exps = np.ascontiguousarray(exps, dtype=np.int8)
     n = ctypes.c_size_t(0)
@@ -197,7 +198,7 @@ class SeedLMMatrix:
         _check(lib().seedlm_info(self._h, ctypes.byref(info)), "seedlm_info")
         self.rows = info.rows
         self.cols = info.cols
-        self.C, self.P, self.K = info.C, info.P, info.K
+        self.C, self.P, self.K, self.Q = info.C, info.P, info.K, info.Q
         self.blocks_per_row = info.blocks_per_row
         self.stored_blocks_per_row = info.stored_blocks_per_row
         self.compressed_bytes = info.compressed_bytes
@@ -221,8 +222,9 @@ class SeedLMMatrix:
 
 
 def seedlm_pack(seeds, coeffs, exps, rows, cols, C, P, K=16) -> SeedLMMatrix:
-    """Validate, pack and upload records; returns a SeedLMMatrix."""
-    seeds, coeffs, exps = _records(seeds, coeffs, exps, rows, cols, C, P)
+    """Validate, pack and upload records; returns a SeedLMMatrix.  Seeds are
+    uint16 for K = 16 and uint32 for K = 20."""
+    seeds, coeffs, exps = _records(seeds, coeffs, exps, rows, cols, C, P, K)
     h = ctypes.c_void_p()
     _check(lib().seedlm_pack(_ptr(seeds), _ptr(coeffs), _ptr(exps), rows, cols, C, P, K,
                              ctypes.byref(h)), "seedlm_pack")

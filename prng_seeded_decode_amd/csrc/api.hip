@@ -111,38 +111,41 @@ struct Group {
 int next_group(const seedlm_handle* hs, int n, int batch, int xdt, int ydt, int variant, int i,
                Group* g) {
   const bool f16 = xdt == SEEDLM_F16 && ydt == SEEDLM_F16;
+  // The table-lookup and matrix-core kernels take the pages' two formats.
+  auto fast = [&](int m) { return hs[m]->is_4bit() || hs[m]->is_3bit(); };
   if (variant != SEEDLM_VARIANT_AUTO) {
     if (n != 1) return SEEDLM_E_INVALID;
-    const int C = hs[0]->C;
     switch (variant) {
       case SEEDLM_VARIANT_LUT:
-        if (batch != 1) return SEEDLM_E_UNSUPPORTED;
-        *g = {0, 1, C == 8 ? kLut8 : kLut12};
+        if (batch != 1 || !fast(0)) return SEEDLM_E_UNSUPPORTED;
+        *g = {0, 1, hs[0]->is_4bit() ? kLut8 : kLut12};
         return SEEDLM_OK;
       case SEEDLM_VARIANT_TABLE:
-        if (batch != 1 || C != 8) return SEEDLM_E_UNSUPPORTED;
+        if (batch != 1 || !hs[0]->is_4bit()) return SEEDLM_E_UNSUPPORTED;
         *g = {0, 1, kTable};
         return SEEDLM_OK;
       case SEEDLM_VARIANT_SIMPLE:
         *g = {0, 1, kSimple};
         return SEEDLM_OK;
       case SEEDLM_VARIANT_MFMA:
-        if (!f16) return SEEDLM_E_UNSUPPORTED;
+        if (!f16 || !fast(0)) return SEEDLM_E_UNSUPPORTED;
         *g = {0, 1, kMfma};
         return SEEDLM_OK;
       default:
         return SEEDLM_E_UNSUPPORTED;
     }
   }
-  const int C = hs[i]->C;
   int k = 0;
   Kind kind = kSimple;
-  if (batch == 1) {
-    kind = C == 8 ? kLut8 : kLut12;
-    while (i + k < n && k < 8 && hs[i + k]->C == C) ++k;
+  if (!fast(i)) {
+    k = 1;
+  } else if (batch == 1) {
+    const bool four = hs[i]->is_4bit();
+    kind = four ? kLut8 : kLut12;
+    while (i + k < n && k < 8 && fast(i + k) && hs[i + k]->is_4bit() == four) ++k;
   } else if (f16) {
     kind = kMfma;
-    while (i + k < n && k < 8) ++k;
+    while (i + k < n && k < 8 && fast(i + k)) ++k;
   } else {
     k = 1;
   }

@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
   auto load_w = [&](int ks) -> uint4 {
     const int b0 = ks * 4;  // first block of the group
     const int p = b0 / kPanelBlocks;
-    const int Wps = (int)panel_stored_width(p, a.nb);
+    const int Wps = (int)panel_stored_width(p, a.nb, kPanelBlocks);
     const int q0 = b0 - p * kPanelBlocks;
     // zero words decode to t = 0
     const uint32_t off = (row < a.Mp && q0 < Wps)
@@ -335,15 +335,15 @@ __global__ void __launch_bounds__(2 * ROWS, 1) gemm_c12_kernel(const Gemm12Args 
     uint32_t e;  // the group's exponent nibbles
   };
   auto load_w = [&](int ks) -> Group {
+    constexpr int PB = panel_blocks(12);
     const int b0 = ks * 4;
-    const int p = b0 / kPanelBlocks;
-    const int Wps = (int)panel_stored_width(p, a.nb);
-    const int q0 = b0 - p * kPanelBlocks;
+    const int p = b0 / PB;
+    const int Wps = (int)panel_stored_width(p, a.nb, PB);
+    const int q0 = b0 - p * PB;
     const bool ok = row < a.Mp && q0 < Wps;
-    const uint32_t off = ok ? (uint32_t)((p * a.Mp * kPanelBlocks + row * Wps + q0) * 4)
-                            : 0x80000000u;
+    const uint32_t off = ok ? (uint32_t)((p * a.Mp * PB + row * Wps + q0) * 4) : 0x80000000u;
     const uint32_t eoff =
-        ok ? a.exp_off + (uint32_t)((p * a.Mp * (kPanelBlocks / 4) + row * (Wps / 4) + q0 / 4) * 2)
+        ok ? a.exp_off + (uint32_t)((p * a.Mp * (PB / 4) + row * (Wps / 4) + q0 / 4) * 2)
            : 0x80000000u;
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0);
     Group g;
@@ -540,6 +540,7 @@ int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, in
   if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
   // token tiles go on grid.y, which holds at most 65535 workgroups
   if ((ntok + 255) / 256 > 65535) return SEEDLM_E_UNSUPPORTED;
+  if (!h->is_4bit() && !h->is_3bit()) return SEEDLM_E_UNSUPPORTED;
   if (h->C == 12) {
     if (h->cols % 8 != 0 || (uintptr_t)x % 16 != 0) return SEEDLM_E_UNSUPPORTED;
     if (h->bytes >= (1ULL << 31) || ntok * h->cols * 2 >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;

@@ -51,19 +51,21 @@ __global__ void __launch_bounds__(kDecThreads) decode_f16_kernel(
     else T1[u] = ext_bits<Ext>(u << 8);
   }
   __syncthreads();
+  constexpr int PB = panel_blocks(C);
+  constexpr int kLogPB = PB == 32 ? 5 : 4;
   const int p = blockIdx.y;
-  const int Wps = (int)panel_stored_width(p, nb);
-  const uint32_t* pw = buf + (int64_t)p * Mp * kPanelBlocks;
+  const int Wps = (int)panel_stored_width(p, nb, PB);
+  const uint32_t* pw = buf + (int64_t)p * Mp * PB;
   const uint16_t* ex = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(buf) +
                                                          exp_off) +
-                       (int64_t)p * Mp * (kPanelBlocks / 4);
+                       (int64_t)p * Mp * (PB / 4);
   const int n = Mp * Wps;
   const int stride = gridDim.x * kDecThreads;
   auto one = [&](int j, uint32_t w, uint32_t e) {
-    const int r = Wps == kPanelBlocks ? j >> 5 : j / Wps;
+    const int r = Wps == PB ? j >> kLogPB : j / Wps;
     const int s = j - r * Wps;
     const int q = (s & ~3) | ((s + r) & 3);
-    const int b = p * kPanelBlocks + q;
+    const int b = p * PB + q;
     if (j >= n || r >= rows || b >= nb) return;
     _Float16* dst = Wd + (int64_t)r * cols + (int64_t)b * C;
     if constexpr (C == 8) {
@@ -91,7 +93,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_f16_kernel(
       w[u] = j < n ? pw[j] : 0u;
       e[u] = 0u;
       if constexpr (C == 12) {
-        const int r = Wps == kPanelBlocks ? j >> 5 : j / Wps;
+        const int r = Wps == PB ? j >> kLogPB : j / Wps;
         e[u] = j < n ? ex[r * (Wps / 4) + ((j - r * Wps) >> 2)] : 0u;
       }
     }
@@ -191,7 +193,8 @@ int launch_gemm_decoded(const seedlm_matrix* h, const void* x, void* y, int64_t 
   if (ws_bytes < decoded_bytes(h)) return SEEDLM_E_INVALID;
   if (h->rows >= (1LL << 31) || h->cols >= (1LL << 31) || ntok >= (1LL << 31))
     return SEEDLM_E_UNSUPPORTED;
-  if (h->Mp * kPanelBlocks >= (1LL << 31) || h->np >= 65536) return SEEDLM_E_UNSUPPORTED;
+  if (!h->is_4bit() && !h->is_3bit()) return SEEDLM_E_UNSUPPORTED;
+  if (h->Mp * h->pb >= (1LL << 31) || h->np >= 65536) return SEEDLM_E_UNSUPPORTED;
   // The GEMM handle is per device and binds to the current one when created.
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return SEEDLM_E_DEVICE;
@@ -224,7 +227,7 @@ int launch_gemm_decoded(const seedlm_matrix* h, const void* x, void* y, int64_t 
     found = B.plans.emplace(key, p).first;
   }
   // about eight workgroups per CU over all panels
-  const int64_t per_panel = (h->Mp * kPanelBlocks + kDecThreads - 1) / kDecThreads;
+  const int64_t per_panel = (h->Mp * h->pb + kDecThreads - 1) / kDecThreads;
   const int64_t gx = std::max<int64_t>(
       1, std::min<int64_t>(per_panel, (8LL * device_cu_count() + h->np - 1) / h->np));
   const dim3 grid((unsigned)gx, (unsigned)h->np);

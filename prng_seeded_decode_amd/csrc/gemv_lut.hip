@@ -244,7 +244,7 @@ __global__ void __launch_bounds__(kThreads, 1)
       pn = 0;
       ++mn;
     }
-    const int Wp = (int)panel_stored_width(p, M.nb);
+    const int Wp = (int)panel_stored_width(p, M.nb, kPanelBlocks);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)M.words, 0, (int)M.words_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t prsrc =
@@ -385,7 +385,7 @@ bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* con
   grp.n = n;
   for (int i = 0; i < n; ++i) {
     const seedlm_matrix* h = hs[i];
-    if (h->C != 8 || h->P != 3 || h->bytes >= 0x80000000ull) return false;
+    if (!h->is_4bit() || h->bytes >= 0x80000000ull) return false;
     if (h->Mp >= (1 << 28) || h->cols >= (1 << 30)) return false;
     if (h->np * h->Mp * 4 >= (1LL << 31)) return false;  // partial offsets are 32-bit
     LutMatrix& M = grp.m[i];

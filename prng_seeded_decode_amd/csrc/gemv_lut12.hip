@@ -19,8 +19,10 @@
 // distinct bytes.  The stream bits past the seed come from GF(2) byte tables,
 // ext(s) = T0[s & 255] ^ T1[s >> 8] (64-bit entries, kept as lo/hi words).
 //
-// The tables depend on x, so they are built per column unit: half a panel, 16
-// blocks = 192 columns.  LDS rows are indexed by a stream byte (256 B per row):
+// The tables depend on x, so they are built per column unit: one packed panel
+// of 16 blocks = 192 columns, whose rows are 64 contiguous bytes of words, so
+// a unit's loads fetch only its own bytes.  LDS rows are indexed by a stream
+// byte (256 B per row):
 //   region 0 row v = [H0 | H1 | H2 | H3]          (16 slots each)
 //   region 1 row v = [T0lo | T1lo | T0hi | T1hi]  (16 copies each)
 // One v_perm_b32 turns a byte and a per-lane constant into an address.
@@ -226,7 +228,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
     const LutMatrix& M = grp.m[mi];
     const int64_t Mp = M.Mp;
     const int slabs = M.slabs;
-    const int64_t ustart = M.item_begin + (int64_t)u * slabs;  // u: half (u & 1) of panel p
+    const int64_t ustart = M.item_begin + (int64_t)u * slabs;  // u: panel u
     const int64_t seg_end = ustart + slabs < end ? ustart + slabs : end;
     const int sb = (int)(seg_end - ustart);
     int mn = mi, un = u + 1;  // the next segment's unit
@@ -234,9 +236,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
       un = 0;
       ++mn;
     }
-    const int64_t p = u >> 1;
-    const int grp4 = 4 * (int)(u & 1) + g;  // this lane's slot group in the panel
-    const int Wp = (int)panel_stored_width(p, M.nb);
+    const int64_t p = u;   // a unit is one whole 16-block panel
+    const int grp4 = g;    // this lane's slot group in the panel
+    const int Wp = (int)panel_stored_width(p, M.nb, kSlots);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)M.words, 0, (int)M.words_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t prsrc =
@@ -245,10 +247,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
     // contribution); rows at or past Mp in the last slab read words of no row
     // of this unit (or zeros past the buffer) and store nothing.
     const bool gvalid = 4 * grp4 < Wp;
-    const uint32_t wbase = gvalid ? (uint32_t)(p * Mp * kPanelBlocks + rho * Wp + 4 * grp4) * 4u
+    const uint32_t wbase = gvalid ? (uint32_t)(p * Mp * kSlots + rho * Wp + 4 * grp4) * 4u
                                   : 0x80000000u;
     const uint32_t ebase =
-        gvalid ? M.exp_off + (uint32_t)(p * Mp * (kPanelBlocks / 4) + rho * (Wp / 4) + grp4) * 2u
+        gvalid ? M.exp_off + (uint32_t)(p * Mp * (kSlots / 4) + rho * (Wp / 4) + grp4) * 2u
                : 0x80000000u;
     const uint32_t wstride = (uint32_t)kRowsPerSlab * (uint32_t)Wp * 4u;
     const uint32_t estride = (uint32_t)kRowsPerSlab * (uint32_t)(Wp / 4) * 2u;
@@ -407,7 +409,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
   }
 }
 
-int64_t units_of(const seedlm_matrix* h) { return (h->nb + kSlots - 1) / kSlots; }
+static_assert(kSlots == panel_blocks(12), "a column unit is one packed panel");
+int64_t units_of(const seedlm_matrix* h) { return h->np; }
 
 bool fill_group12(const seedlm_matrix* const* hs, const void* const* xs, void* const* ys,
                   float* const* partials, int n, LutGroup& grp) {
@@ -416,7 +419,7 @@ bool fill_group12(const seedlm_matrix* const* hs, const void* const* xs, void* c
   grp.n = n;
   for (int i = 0; i < n; ++i) {
     const seedlm_matrix* h = hs[i];
-    if (h->C != 12 || h->P != 4 || h->bytes >= 0x80000000ull) return false;
+    if (!h->is_3bit() || h->bytes >= 0x80000000ull) return false;
     if (h->Mp >= (1 << 27) || h->cols >= (1 << 30)) return false;
     const int64_t units = units_of(h);
     if (units * h->Mp * 4 >= (1LL << 31)) return false;  // partial offsets are 32-bit

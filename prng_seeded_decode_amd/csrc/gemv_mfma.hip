@@ -177,28 +177,37 @@ gemv_mfma_kernel(const MfmaGroup grp) {
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr) acc[rr] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Load unit k = 2*rr + h of panel p: the 16-byte record group (slots
-  // 4g .. 4g+3, g = 4h + q) of row row0 + rho + 4*i16, and its exponent
-  // nibbles (3-bit).  Units are loaded two ahead into a 4-slot ring; the ring
-  // crosses panel boundaries, and loads past the last panel read zeros.
+  // Load unit k = 2*rr + h of the 32-block step p: the 16-byte record group
+  // (slots 4g .. 4g+3 of the step, g = 4h + q) of row row0 + rho + 4*i16, and
+  // its exponent nibbles (3-bit).  A 4-bit step is one packed panel; a 3-bit
+  // step is two packed 16-block panels, 2p and 2p + 1, and unit h reads group
+  // q of panel 2p + h.  Units are loaded two ahead into a 4-slot ring; the
+  // ring crosses step boundaries, and loads past the last step read zeros.
   auto unit_load = [&](int p, int k, v4u& wd, uint32_t& ev) {
     const int rho = rho_of(k >> 1), h = k & 1;
     const int r = row0 + rho + 4 * i16;
-    const int g = 4 * h + q;
-    const int Wp = (int)panel_stored_width(p, a.nb);
-    const bool ok = p < pb && r < a.Mp && 4 * g < Wp;
-    const uint32_t off =
-        ok ? (uint32_t)(((int64_t)p * Mp * kPanelBlocks + (int64_t)r * Wp + 4 * g) * 4)
-           : 0x80000000u;
-    wd = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
-    if constexpr (C == 12) {
-      const uint32_t eoff =
-          ok ? a.exp_off + (uint32_t)(((int64_t)p * Mp * (kPanelBlocks / 4) +
-                                       (int64_t)r * (Wp / 4) + g) * 2)
+    if constexpr (C == 8) {
+      const int g = 4 * h + q;
+      const int Wp = (int)panel_stored_width(p, a.nb, kPanelBlocks);
+      const bool ok = p < pb && r < a.Mp && 4 * g < Wp;
+      const uint32_t off =
+          ok ? (uint32_t)(((int64_t)p * Mp * kPanelBlocks + (int64_t)r * Wp + 4 * g) * 4)
              : 0x80000000u;
-      ev = __builtin_amdgcn_raw_buffer_load_b16(rsrc, eoff, 0, 0);
-    } else {
+      wd = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
       ev = 0u;
+    } else {
+      constexpr int PB = panel_blocks(12);
+      const int pp = 2 * p + h;  // packed panel; past the last one Wp <= 0
+      const int Wp = (int)panel_stored_width(pp, a.nb, PB);
+      const bool ok = p < pb && r < a.Mp && 4 * q < Wp;
+      const uint32_t off =
+          ok ? (uint32_t)(((int64_t)pp * Mp * PB + (int64_t)r * Wp + 4 * q) * 4) : 0x80000000u;
+      const uint32_t eoff =
+          ok ? a.exp_off +
+                   (uint32_t)(((int64_t)pp * Mp * (PB / 4) + (int64_t)r * (Wp / 4) + q) * 2)
+             : 0x80000000u;
+      wd = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+      ev = __builtin_amdgcn_raw_buffer_load_b16(rsrc, eoff, 0, 0);
     }
   };
   auto unit_compute = [&](const _Float16* xp, int k, const v4u wd, uint32_t ev) {
@@ -346,10 +355,10 @@ int plan_mfma(const seedlm_matrix* h, const void* x, void* y, float* partial, in
   a.cols = (int)h->cols;
   a.Mp = (int)h->Mp;
   a.nb = (int)h->nb;
-  a.np = (int)h->np;
+  a.np = (int)((h->nb + kPanelBlocks - 1) / kPanelBlocks);  // 32-block steps
   a.batch = batch;
   const int64_t want = 4LL * device_cu_count();
-  wide = ((h->Mp + kRowsPerTile - 1) / kRowsPerTile) * h->np >= want;
+  wide = ((h->Mp + kRowsPerTile - 1) / kRowsPerTile) * a.np >= want;
   const int tile_rows = wide ? kRowsPerTile : 64;
   a.tiles = (int)((h->Mp + tile_rows - 1) / tile_rows);
   int64_t chunks = (want + a.tiles - 1) / a.tiles;
@@ -387,7 +396,7 @@ int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs
   MfmaArgs args[kMaxMfmaGroup];
   bool wide[kMaxMfmaGroup];
   for (int i = 0; i < n; ++i) {
-    if (hs[i]->C != 8 && hs[i]->C != 12) return SEEDLM_E_UNSUPPORTED;
+    if (!hs[i]->is_4bit() && !hs[i]->is_3bit()) return SEEDLM_E_UNSUPPORTED;
     const int st = plan_mfma(hs[i], xs[i], ys[i], partials[i], batch, args[i], wide[i]);
     if (st != SEEDLM_OK) return st;
     if (args[i].chunks > 1 && !partials[i]) return SEEDLM_E_INVALID;

@@ -1,6 +1,6 @@
 // Reference-grade fused decode-GEMV: one wavefront per output row, each lane
 // rebuilds whole blocks (exact integer reconstruction, as in decode) and
-// multiplies them with x.  Any (C, P), batch 1..16, any dtype pair.  This is
+// multiplies them with x.  Every packed format, batch 1..16, any dtype pair.  This is
 // the correctness anchor for the faster kernels and the SIMPLE variant of the
 // A/B measurements.  SeedLM's inference step: fetch s and t, rebuild the
 // weights on the fly, use them to compute the activations (paperhub.cn
@@ -33,7 +33,7 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-template <int C, int P, int B, typename XT, typename YT>
+template <int C, int P, int K, int Q, int B, typename XT, typename YT>
 __global__ void __launch_bounds__(256) gemv_simple_kernel(const uint32_t* __restrict__ words,
                                                           const uint16_t* __restrict__ exps,
                                                           const XT* __restrict__ x,
@@ -46,19 +46,20 @@ __global__ void __launch_bounds__(256) gemv_simple_kernel(const uint32_t* __rest
   float acc[B];
 #pragma unroll
   for (int k = 0; k < B; ++k) acc[k] = 0.f;
+  constexpr int PB = panel_blocks(C);
   for (int64_t b = lane; b < nb; b += 64) {
-    const uint32_t w = words[word_index(r, b, Mp, nb)];
+    const uint32_t w = words[word_index(r, b, Mp, nb, PB)];
     int g;
-    if constexpr (P == 3) {
+    if constexpr (C == 8) {
       g = (int)(w >> 28);
     } else {
-      g = (exps[exp_index(r, b, Mp, nb)] >> (4 * exp_nibble(r, b))) & 0xF;
+      g = (exps[exp_index(r, b, Mp, nb, PB)] >> (4 * exp_nibble(r, b, PB))) & 0xF;
     }
-    const uint64_t stream = lfsr_stream<C * P + 15>(w);
+    const uint64_t stream = lfsr_stream_k<K, C * P + K - 1>(w);
     int t[P];
 #pragma unroll
-    for (int j = 0; j < P; ++j) t[j] = ((int)(w << (12 - 4 * j))) >> 28;
-    const float scale = __int_as_float((g - 30 + 127) << 23);
+    for (int j = 0; j < P; ++j) t[j] = ((int)(w << (32 - K - Q * (j + 1)))) >> (32 - Q);
+    const float scale = __int_as_float((g - 14 - K + 127) << 23);  // 2^(e - (K-1))
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const int64_t c = b * C + i;
@@ -66,8 +67,8 @@ __global__ void __launch_bounds__(256) gemv_simple_kernel(const uint32_t* __rest
       int I = 0;
 #pragma unroll
       for (int j = 0; j < P; ++j) {
-        const int z = (int)((stream >> (j * C + i)) & 0xFFFFu);
-        I += t[j] * (z - (int)kHalf);
+        const int z = (int)((stream >> (j * C + i)) & ((1u << K) - 1u));
+        I += t[j] * (z - (1 << (K - 1)));
       }
       const float wv = (float)I * scale;
 #pragma unroll
@@ -84,7 +85,7 @@ __global__ void __launch_bounds__(256) gemv_simple_kernel(const uint32_t* __rest
   }
 }
 
-template <int C, int P, typename XT, typename YT>
+template <int C, int P, int K, int Q, typename XT, typename YT>
 int launch_typed(const seedlm_matrix* h, const void* x, void* y, int batch, hipStream_t s) {
   const int waves = 4;
   const int64_t grid = (h->rows + waves - 1) / waves;
@@ -94,32 +95,38 @@ int launch_typed(const seedlm_matrix* h, const void* x, void* y, int batch, hipS
   const XT* xp = static_cast<const XT*>(x);
   YT* yp = static_cast<YT*>(y);
   if (batch == 1)
-    hipLaunchKernelGGL((gemv_simple_kernel<C, P, 1, XT, YT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((gemv_simple_kernel<C, P, K, Q, 1, XT, YT>), dim3((unsigned)grid),
                        dim3(64 * waves), 0, s, words, exps, xp, yp, h->rows, h->cols, h->nb,
                        h->Mp, batch);
   else
-    hipLaunchKernelGGL((gemv_simple_kernel<C, P, SEEDLM_MAX_BATCH, XT, YT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((gemv_simple_kernel<C, P, K, Q, SEEDLM_MAX_BATCH, XT, YT>),
+                       dim3((unsigned)grid),
                        dim3(64 * waves), 0, s, words, exps, xp, yp, h->rows, h->cols, h->nb,
                        h->Mp, batch);
   SEEDLM_HIP_CHECK(hipGetLastError());
   return SEEDLM_OK;
 }
 
-template <int C, int P>
+template <int C, int P, int K, int Q>
 int launch_cp(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt, int ydt,
               hipStream_t s) {
-  if (xdt == SEEDLM_F32 && ydt == SEEDLM_F32) return launch_typed<C, P, float, float>(h, x, y, batch, s);
-  if (xdt == SEEDLM_F32 && ydt == SEEDLM_F16) return launch_typed<C, P, float, __half>(h, x, y, batch, s);
-  if (xdt == SEEDLM_F16 && ydt == SEEDLM_F32) return launch_typed<C, P, __half, float>(h, x, y, batch, s);
-  return launch_typed<C, P, __half, __half>(h, x, y, batch, s);
+  if (xdt == SEEDLM_F32 && ydt == SEEDLM_F32)
+    return launch_typed<C, P, K, Q, float, float>(h, x, y, batch, s);
+  if (xdt == SEEDLM_F32 && ydt == SEEDLM_F16)
+    return launch_typed<C, P, K, Q, float, __half>(h, x, y, batch, s);
+  if (xdt == SEEDLM_F16 && ydt == SEEDLM_F32)
+    return launch_typed<C, P, K, Q, __half, float>(h, x, y, batch, s);
+  return launch_typed<C, P, K, Q, __half, __half>(h, x, y, batch, s);
 }
 
 }  // namespace
 
 int launch_gemv_simple(const seedlm_matrix* h, const void* x, void* y, int batch, int xdt,
                        int ydt, hipStream_t s) {
-  if (h->C == 8) return launch_cp<8, 3>(h, x, y, batch, xdt, ydt, s);
-  return launch_cp<12, 4>(h, x, y, batch, xdt, ydt, s);
+  if (h->is_4bit()) return launch_cp<8, 3, 16, 4>(h, x, y, batch, xdt, ydt, s);
+  if (h->is_3bit()) return launch_cp<12, 4, 16, 4>(h, x, y, batch, xdt, ydt, s);
+  if (h->C == 8) return launch_cp<8, 4, 16, 3>(h, x, y, batch, xdt, ydt, s);
+  return launch_cp<12, 3, 20, 4>(h, x, y, batch, xdt, ydt, s);
 }
 
 }  // namespace seedlm

@@ -3,8 +3,8 @@
 // group of matrices, the host-side work split, the deterministic panel
 // reduction and a few device helpers.
 //
-// Both kernels cut every matrix into column units (a panel of 32 blocks for
-// C = 8, half a panel for C = 12), build per-unit lookup tables of x in LDS and
+// Both kernels cut every matrix into column units (a packed panel: 32 blocks
+// for C = 8, 16 blocks for C = 12), build per-unit lookup tables of x in LDS and
 // stream the unit's rows past them, writing one fp32 partial per (unit, row).
 // reduce_panels_kernel then adds the partials of each row in a fixed order.
 #pragma once

@@ -1,9 +1,10 @@
 // Host packer and handle management of libseedlm.
 //
 // The packed buffer holds one 32-bit word per block {seed, coefficients,
-// biased shared exponent} (4-bit format) or {seed, coefficients} plus a nibble
-// array of exponents (3-bit format), grouped into 32-block panels whose rows
-// hold groups of four slots rotated by the row index.  The record itself is the pages' {seed s, coefficients t, shared
+// biased shared exponent} (C = 8 formats) or {seed, coefficients} plus a nibble
+// array of exponents (C = 12 formats), grouped into panels of 32 (C = 8) or 16
+// (C = 12) blocks whose rows hold groups of four slots rotated by the row
+// index.  The record itself is the pages' {seed s, coefficients t, shared
 // exponent} (atlas.scime.ai "Approach"; paperhub.cn rebuttal on shared
 // exponents); the bit positions and the panel order are this library's.
 #include <stdlib.h>
@@ -18,23 +19,22 @@ using namespace seedlm;
 
 namespace {
 
-bool supported(int C, int P, int K) {
-  return K == 16 && ((C == 8 && P == 3) || (C == 12 && P == 4));
-}
-
 struct Layout {
+  int Q, PB;
   int64_t nb, nbs, np, Mp, nwords;
   size_t exp_off, bytes;
 };
 
-Layout make_layout(int64_t rows, int64_t cols, int C, int P) {
+Layout make_layout(int64_t rows, int64_t cols, int C, int P, int K) {
   Layout L;
+  L.Q = packed_q(C, P, K);
+  L.PB = panel_blocks(C);
   L.nb = (cols + C - 1) / C;
-  L.np = (L.nb + kPanelBlocks - 1) / kPanelBlocks;
-  L.nbs = (L.np - 1) * kPanelBlocks + panel_stored_width(L.np - 1, L.nb);
+  L.np = (L.nb + L.PB - 1) / L.PB;
+  L.nbs = (L.np - 1) * L.PB + panel_stored_width(L.np - 1, L.nb, L.PB);
   L.Mp = padded_rows(rows);
   L.nwords = L.Mp * L.nbs;
-  if (P == 3) {
+  if (C == 8) {
     L.exp_off = 0;
     L.bytes = (size_t)L.nwords * 4;
   } else {
@@ -44,47 +44,56 @@ Layout make_layout(int64_t rows, int64_t cols, int C, int P) {
   return L;
 }
 
-int validate(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps, int64_t rows,
+// Seed k of the record arrays: uint16 for K <= 16, uint32 above.
+uint32_t seed_at(const void* seeds, int K, int64_t k) {
+  return K <= 16 ? static_cast<const uint16_t*>(seeds)[k] : static_cast<const uint32_t*>(seeds)[k];
+}
+
+int validate(const void* seeds, const int8_t* coeffs, const int8_t* exps, int64_t rows,
              int64_t cols, int C, int P, int K) {
   if (!seeds || !coeffs || !exps) return SEEDLM_E_INVALID;
   if (rows <= 0 || cols <= 0) return SEEDLM_E_INVALID;
-  if (!supported(C, P, K)) return SEEDLM_E_UNSUPPORTED;
+  const int Q = packed_q(C, P, K);
+  if (Q == 0) return SEEDLM_E_UNSUPPORTED;
   // Keep every index of the layout (and of the kernels' 32-bit row math) in range.
   if (rows > (1LL << 30) || cols > (1LL << 30)) return SEEDLM_E_INVALID;
   const int64_t nb = (cols + C - 1) / C;
   const int64_t n = rows * nb;
   for (int64_t k = 0; k < n; ++k) {
-    if (seeds[k] == 0) return SEEDLM_E_INVALID;
+    const uint32_t s = seed_at(seeds, K, k);
+    if (s == 0 || s >= (1u << K)) return SEEDLM_E_INVALID;
     if (exps[k] < -15 || exps[k] > 0) return SEEDLM_E_INVALID;
   }
+  const int lo = -(1 << (Q - 1)), hi = (1 << (Q - 1)) - 1;
   for (int64_t k = 0; k < n * P; ++k)
-    if (coeffs[k] < -8 || coeffs[k] > 7) return SEEDLM_E_INVALID;
+    if (coeffs[k] < lo || coeffs[k] > hi) return SEEDLM_E_INVALID;
   return SEEDLM_OK;
 }
 
-void write_layout(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps, int64_t rows,
-                  int C, int P, const Layout& L, uint8_t* dst) {
-  (void)C;
+void write_layout(const void* seeds, const int8_t* coeffs, const int8_t* exps, int64_t rows,
+                  int C, int P, int K, const Layout& L, uint8_t* dst) {
   uint32_t* words = reinterpret_cast<uint32_t*>(dst);
   for (int64_t k = 0; k < L.nwords; ++k) words[k] = kPadWord;
   uint16_t* ex = nullptr;
-  if (P == 4) {
+  if (C == 12) {
     memset(dst + (size_t)L.nwords * 4, 0, L.exp_off - (size_t)L.nwords * 4);
     ex = reinterpret_cast<uint16_t*>(dst + L.exp_off);
     memset(ex, 0, L.bytes - L.exp_off);
   }
+  const uint32_t qmask = (1u << L.Q) - 1;
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t b = 0; b < L.nb; ++b) {
       const int64_t k = r * L.nb + b;
-      uint32_t w = seeds[k];
-      for (int j = 0; j < P; ++j) w |= (uint32_t)(coeffs[k * P + j] & 0xF) << (16 + 4 * j);
+      uint32_t w = seed_at(seeds, K, k);
+      for (int j = 0; j < P; ++j)
+        w |= ((uint32_t)coeffs[k * P + j] & qmask) << (K + L.Q * j);
       const uint32_t g = (uint32_t)(exps[k] + 15);
-      if (P == 3) {
+      if (C == 8) {
         w |= g << 28;
       } else {
-        ex[exp_index(r, b, L.Mp, L.nb)] |= (uint16_t)(g << (4 * exp_nibble(r, b)));
+        ex[exp_index(r, b, L.Mp, L.nb, L.PB)] |= (uint16_t)(g << (4 * exp_nibble(r, b, L.PB)));
       }
-      words[word_index(r, b, L.Mp, L.nb)] = w;
+      words[word_index(r, b, L.Mp, L.nb, L.PB)] = w;
     }
   }
 }
@@ -105,13 +114,13 @@ const char* seedlm_status_string(int status) {
   }
 }
 
-int seedlm_pack_host(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps,
+int seedlm_pack_host(const void* seeds, const int8_t* coeffs, const int8_t* exps,
                      int64_t rows, int64_t cols, int C, int P, int K, void* dst,
                      size_t* bytes) {
   if (!bytes) return SEEDLM_E_INVALID;
   int st = validate(seeds, coeffs, exps, rows, cols, C, P, K);
   if (st != SEEDLM_OK) return st;
-  const Layout L = make_layout(rows, cols, C, P);
+  const Layout L = make_layout(rows, cols, C, P, K);
   if (!dst) {
     *bytes = L.bytes;
     return SEEDLM_OK;
@@ -120,23 +129,23 @@ int seedlm_pack_host(const uint16_t* seeds, const int8_t* coeffs, const int8_t* 
     *bytes = L.bytes;
     return SEEDLM_E_INVALID;
   }
-  write_layout(seeds, coeffs, exps, rows, C, P, L, static_cast<uint8_t*>(dst));
+  write_layout(seeds, coeffs, exps, rows, C, P, K, L, static_cast<uint8_t*>(dst));
   *bytes = L.bytes;
   return SEEDLM_OK;
 }
 
-int seedlm_pack(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps, int64_t rows,
+int seedlm_pack(const void* seeds, const int8_t* coeffs, const int8_t* exps, int64_t rows,
                 int64_t cols, int C, int P, int K, seedlm_handle* out) {
   if (!out) return SEEDLM_E_INVALID;
   *out = nullptr;
   int st = validate(seeds, coeffs, exps, rows, cols, C, P, K);
   if (st != SEEDLM_OK) return st;
-  const Layout L = make_layout(rows, cols, C, P);
+  const Layout L = make_layout(rows, cols, C, P, K);
 
   uint8_t* host = nullptr;
   if (hipHostMalloc((void**)&host, L.bytes, hipHostMallocDefault) != hipSuccess)
     return SEEDLM_E_NOMEM;
-  write_layout(seeds, coeffs, exps, rows, C, P, L, host);
+  write_layout(seeds, coeffs, exps, rows, C, P, K, L, host);
 
   seedlm_matrix* h = new (std::nothrow) seedlm_matrix();
   if (!h) {
@@ -148,6 +157,8 @@ int seedlm_pack(const uint16_t* seeds, const int8_t* coeffs, const int8_t* exps,
   h->C = C;
   h->P = P;
   h->K = K;
+  h->Q = L.Q;
+  h->pb = L.PB;
   h->nb = L.nb;
   h->nbs = L.nbs;
   h->np = L.np;
@@ -191,6 +202,7 @@ int seedlm_info(seedlm_handle h, seedlm_info_t* info) {
   info->blocks_per_row = h->nb;
   info->stored_blocks_per_row = h->nbs;
   info->compressed_bytes = (int64_t)h->bytes;
+  info->Q = h->Q;
   return SEEDLM_OK;
 }
 

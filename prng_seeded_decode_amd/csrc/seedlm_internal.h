@@ -13,11 +13,26 @@
 namespace seedlm {
 
 // Packed layout constants (documented in include/seedlm.h).
-constexpr int kPanelBlocks = 32;  // blocks per panel
+constexpr int kPanelBlocks = 32;  // blocks per panel of the C = 8 formats
 constexpr int kGroup = 4;         // slots per rotated group (one 16-byte load)
-constexpr int kStateBits = 16;    // K
+constexpr int kStateBits = 16;    // K of the two formats the fast kernels take
 constexpr uint32_t kHalf = 1u << (kStateBits - 1);
 constexpr uint32_t kPadWord = 0x00000001u;  // seed 1, t = 0, g = 0
+
+// Blocks per panel: a panel row is 128 bytes of words for C = 8 and 64 bytes
+// for C = 12, so that the batch-1 kernels' column unit (32 and 16 blocks) reads
+// whole contiguous rows.
+__host__ __device__ constexpr int panel_blocks(int C) { return C == 8 ? 32 : 16; }
+
+// The packed formats (C, P, K) and their coefficient width Q: the word holds
+// the seed in bits 0..K-1 and t_j in bits K+Q*j .. K+Q*j+Q-1; C = 8 formats
+// keep g in bits 28..31, C = 12 formats in a nibble array.  0 = unsupported.
+__host__ __device__ constexpr int packed_q(int C, int P, int K) {
+  return (C == 8 && P == 3 && K == 16) || (C == 12 && P == 4 && K == 16) ||
+                 (C == 12 && P == 3 && K == 20)
+             ? 4
+             : (C == 8 && P == 4 && K == 16 ? 3 : 0);
+}
 
 }  // namespace seedlm
 
@@ -25,16 +40,21 @@ constexpr uint32_t kPadWord = 0x00000001u;  // seed 1, t = 0, g = 0
 // nothing else, so calls that share it may run concurrently.
 struct seedlm_matrix {
   int64_t rows = 0, cols = 0;
-  int C = 0, P = 0, K = 0;
+  int C = 0, P = 0, K = 0, Q = 0;
+  int pb = 0;           // blocks per panel (panel_blocks(C))
   int64_t nb = 0;       // blocks per row
   int64_t nbs = 0;      // stored blocks per row (last panel padded to 4 slots)
-  int64_t np = 0;       // panels per row: ceil(nb / 32)
+  int64_t np = 0;       // panels per row: ceil(nb / pb)
   int64_t Mp = 0;       // rows padded to a multiple of 8
   int64_t nwords = 0;   // Mp * nbs
   size_t bytes = 0;     // packed buffer size
-  size_t exp_off = 0;   // byte offset of the exponent nibble array (P == 4)
+  size_t exp_off = 0;   // byte offset of the exponent nibble array (C == 12)
   int device = 0;
   void* d_buf = nullptr;      // packed buffer (device)
+  // The pages' formats, which the table-lookup and matrix-core kernels take;
+  // the other packed formats run the exact per-lane kernel.
+  bool is_4bit() const { return C == 8 && P == 3 && K == 16; }
+  bool is_3bit() const { return C == 12 && P == 4 && K == 16; }
 };
 
 // An encoder: the per-seed table of one format on one device.
@@ -47,36 +67,38 @@ struct seedlm_encoder {
 
 namespace seedlm {
 
-// Layout helpers (host and device).  Rows are padded to Mp = 8*ceil(rows/8).
-// Panel p holds blocks 32p .. 32p+Wp-1; its stored width is Wp rounded up to a
-// multiple of 4.  Panel p starts at word p*Mp*32 and stores its Mp rows one
-// after another; inside a row, slot q sits at 4*(q/4) + ((q - r) mod 4), so the
-// four words of one 16-byte load hold the group's slots rotated by the row.
-__host__ __device__ inline int64_t panel_width(int64_t p, int64_t nb) {
-  int64_t w = nb - (int64_t)kPanelBlocks * p;
-  return w < kPanelBlocks ? w : kPanelBlocks;
+// Layout helpers (host and device), PB = blocks per panel.  Rows are padded to
+// Mp = 8*ceil(rows/8).  Panel p holds blocks PB*p .. PB*p+Wp-1; its stored
+// width is Wp rounded up to a multiple of 4.  Panel p starts at word p*Mp*PB
+// and stores its Mp rows one after another; inside a row, slot q sits at
+// 4*(q/4) + ((q - r) mod 4), so the four words of one 16-byte load hold the
+// group's slots rotated by the row.
+__host__ __device__ inline int64_t panel_width(int64_t p, int64_t nb, int PB) {
+  int64_t w = nb - (int64_t)PB * p;
+  return w < PB ? w : PB;
 }
 
-__host__ __device__ inline int64_t panel_stored_width(int64_t p, int64_t nb) {
-  return (panel_width(p, nb) + kGroup - 1) / kGroup * kGroup;
+__host__ __device__ inline int64_t panel_stored_width(int64_t p, int64_t nb, int PB) {
+  return (panel_width(p, nb, PB) + kGroup - 1) / kGroup * kGroup;
 }
 
 __host__ __device__ inline int64_t padded_rows(int64_t rows) { return (rows + 7) / 8 * 8; }
 
-__host__ __device__ inline int64_t word_index(int64_t r, int64_t b, int64_t Mp, int64_t nb) {
-  const int64_t p = b / kPanelBlocks, q = b % kPanelBlocks;
-  return p * Mp * kPanelBlocks + r * panel_stored_width(p, nb) + (q & ~(int64_t)3) +
-         ((q - r) & 3);
+__host__ __device__ inline int64_t word_index(int64_t r, int64_t b, int64_t Mp, int64_t nb,
+                                              int PB) {
+  const int64_t p = b / PB, q = b % PB;
+  return p * Mp * PB + r * panel_stored_width(p, nb, PB) + (q & ~(int64_t)3) + ((q - r) & 3);
 }
 
 // Index of the uint16 that holds the exponent nibbles of (r, b)'s group, and the
-// nibble number inside it (3-bit format).
-__host__ __device__ inline int64_t exp_index(int64_t r, int64_t b, int64_t Mp, int64_t nb) {
-  const int64_t p = b / kPanelBlocks, q = b % kPanelBlocks;
-  return p * Mp * (kPanelBlocks / kGroup) + r * (panel_stored_width(p, nb) / kGroup) + q / kGroup;
+// nibble number inside it (C = 12 formats).
+__host__ __device__ inline int64_t exp_index(int64_t r, int64_t b, int64_t Mp, int64_t nb,
+                                             int PB) {
+  const int64_t p = b / PB, q = b % PB;
+  return p * Mp * (PB / kGroup) + r * (panel_stored_width(p, nb, PB) / kGroup) + q / kGroup;
 }
-__host__ __device__ inline int exp_nibble(int64_t r, int64_t b) {
-  return (int)(((b % kPanelBlocks) - r) & 3);
+__host__ __device__ inline int exp_nibble(int64_t r, int64_t b, int PB) {
+  return (int)(((b % PB) - r) & 3);
 }
 
 // Launch wrappers implemented in the .hip files.  All return a status code.

@@ -1,11 +1,11 @@
 """GPU parity of the batch-1 3-bit table-lookup kernel (C=12, P=4) against the
 CPU oracle, through the C ABI.
 
-The kernel works on column units of 16 blocks (half a packed panel) and on
+The kernel works on column units of 16 blocks (one packed 3-bit panel) and on
 16-row slabs, so the edge cases here are: a last slab holding only 8 rows
-(Mp = 8 mod 16), last panels whose stored width ends inside either half or
-exactly at a half, a single block, the extreme exponents and coefficients, and
-several matrices in one grouped launch.  Bars as in the other GPU parity tests
+(Mp = 8 mod 16), last panels of every stored width class (1, 4, 15, 16 blocks
+and the steps between), a single block, the extreme exponents and
+coefficients, and several matrices in one grouped launch.  Bars as in the other GPU parity tests
 (normwise error against the float64 oracle): 2e-3 for fp16 output, 1e-5 for
 fp32 output; repeated calls must agree bit for bit.
 """
@@ -57,9 +57,9 @@ def _gemv(m, x_np, ydt, variant=LUT):
     return y.float().cpu().numpy()
 
 
-# (rows, nb): rows 40 and 24 leave an 8-row last slab; nb mod 32 = 1, 4, 15, 16,
-# 17, 20, 31 and 0 put the last panel's stored width inside the first half, at
-# the half, inside the second half and at the full panel.
+# (rows, nb): rows 40 and 24 leave an 8-row last slab; nb mod 16 = 1, 4, 15, 0,
+# 1, 4, 15 and 0 give last panels of 1 block (stored 4 wide), 4, 15 (stored 16)
+# and a full 16.
 SHAPES = [(40, 33), (24, 36), (16, 47), (8, 48), (56, 49), (72, 52), (33, 63), (48, 64),
           (1, 1), (129, 342), (200, 96)]
 

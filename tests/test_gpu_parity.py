@@ -507,3 +507,102 @@ def test_bench_timing_events_span_the_main_kernels():
     assert all(torch.equal(a, b) for a, b in zip(ys, ref))
     with pytest.raises(S.SeedLMError):
         S.seedlm_bench_time_next_call(ev[1], None)
+
+
+# The two packed formats beside the pages' ones: (8, 4, 16) with 3-bit
+# coefficients and (12, 3, 20) with a 20-bit seed.  seedlm_decode must be
+# bit-exact and seedlm_gemv (the exact per-lane kernel for these formats) meet
+# the same bars, at ragged shapes, several batch sizes and every dtype pair.
+OTHER_FORMATS = [
+    # (C, P, K, rows, cols, batch, xdt, ydt)
+    (8, 4, 16, 37, 8 * 45 + 5, 1, "f16", "f16"),
+    (8, 4, 16, 300, 8 * 70, 3, "f32", "f32"),
+    (8, 4, 16, 64, 1000, 8, "f16", "f32"),
+    (12, 3, 20, 30, 12 * 70 + 7, 1, "f16", "f16"),
+    (12, 3, 20, 129, 4096, 2, "f32", "f32"),
+    (12, 3, 20, 70, 12 * 40 + 4, 16, "f16", "f16"),
+    (12, 3, 20, 1, 5, 1, "f32", "f16"),
+]
+
+
+def _records_k(rng, rows, cols, C, P, K, Q, erange=(-15, 0)):
+    nb = math.ceil(cols / C)
+    s = rng.integers(1, 1 << K, (rows, nb)).astype(np.uint16 if K <= 16 else np.uint32)
+    c = rng.integers(-(1 << (Q - 1)), 1 << (Q - 1), (rows, nb, P)).astype(np.int8)
+    e = rng.integers(erange[0], erange[1] + 1, (rows, nb)).astype(np.int8)
+    return s, c, e
+
+
+@pytest.mark.parametrize("C,P,K,rows,cols,batch,xdt,ydt", OTHER_FORMATS,
+                         ids=[f"C{c[0]}P{c[1]}K{c[2]}_{c[3]}x{c[4]}_b{c[5]}_{c[6]}{c[7]}"
+                              for c in OTHER_FORMATS])
+def test_other_packed_formats_decode_and_gemv(C, P, K, rows, cols, batch, xdt, ydt):
+    S = _S()
+    Q = O.PACKED_FORMATS[(C, P, K)]
+    rng = np.random.default_rng(rows * 31 + cols + K)
+    s, c, e = _records_k(rng, rows, cols, C, P, K, Q)
+    m = S.seedlm_pack(s, c, e, rows, cols, C, P, K)
+    assert (m.C, m.P, m.K, m.Q) == (C, P, K, Q)
+    W_ref = O.decode_rows(s, c, e, cols, C, P, K=K)
+    _say(f"decode C={C} P={P} K={K} {rows}x{cols}")
+    W = _decode_gpu(m, rows, cols).cpu().numpy()
+    assert np.array_equal(W, W_ref.astype(np.float32)), "decode must be bit-exact"
+    x = rng.standard_normal((batch, cols)).astype(np.float16 if xdt == "f16" else np.float32)
+    _say(f"gemv C={C} P={P} K={K} batch={batch} {xdt}->{ydt}")
+    y = _gemv_gpu(m, x, ydt)
+    assert O.normwise_error(y, O.gemv(W_ref, x)) <= TOL[ydt]
+    # the fast kernels take only the pages' formats
+    for variant in (1, 4):
+        with pytest.raises(S.SeedLMError) as err:
+            _gemv_gpu(m, x, ydt, variant=variant)
+        assert err.value.status == S.E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gemv_many_over_all_packed_formats(batch):
+    # One call over matrices of all four formats: the pages' formats go through
+    # their grouped kernels, the others through the exact kernel, and every
+    # output equals a single call's and meets the oracle's bar.
+    S = _S()
+    dev = _dev()
+    rng = np.random.default_rng(808 + batch)
+    shapes = [(8, 3, 16, 300, 1000), (8, 4, 16, 200, 8 * 50 + 3), (12, 4, 16, 50, 600),
+              (12, 3, 20, 90, 12 * 30 + 5), (8, 3, 16, 1000, 256), (12, 3, 20, 8, 48)]
+    mats, refs, xs = [], [], []
+    for C, P, K, rows, cols in shapes:
+        Q = O.PACKED_FORMATS[(C, P, K)]
+        s, c, e = _records_k(rng, rows, cols, C, P, K, Q)
+        mats.append(S.seedlm_pack(s, c, e, rows, cols, C, P, K))
+        refs.append(O.decode_rows(s, c, e, cols, C, P, K=K))
+        xs.append(rng.standard_normal((batch, cols)).astype(np.float16))
+    xd = [torch.from_numpy(x).to(dev) for x in xs]
+    ys = [torch.empty((batch, m.rows), dtype=torch.float16, device=dev) for m in mats]
+    _say(f"gemv_many over four formats, batch {batch}")
+    S.seedlm_gemv_many(mats, xd, ys, batch=batch)
+    single = [torch.empty_like(y) for y in ys]
+    for m, x, y in zip(mats, xd, single):
+        S.seedlm_gemv(m, x, y, batch=batch)
+    torch.cuda.synchronize()
+    for y, y1, W_ref, x in zip(ys, single, refs, xs):
+        assert torch.equal(y, y1)
+        assert O.normwise_error(y.float().cpu().numpy(), O.gemv(W_ref, x)) <= TOL["f16"]
+
+
+def test_prefill_paths_reject_the_other_formats():
+    S = _S()
+    dev = _dev()
+    rng = np.random.default_rng(5)
+    for C, P, K in ((8, 4, 16), (12, 3, 20)):
+        Q = O.PACKED_FORMATS[(C, P, K)]
+        rows, cols = 64, C * 32
+        s, c, e = _records_k(rng, rows, cols, C, P, K, Q)
+        m = S.seedlm_pack(s, c, e, rows, cols, C, P, K)
+        X = torch.zeros((32, cols), dtype=torch.float16, device=dev)
+        Y = torch.empty((32, rows), dtype=torch.float16, device=dev)
+        with pytest.raises(S.SeedLMError) as err:
+            S.seedlm_gemm(m, X, Y)
+        assert err.value.status == S.E_UNSUPPORTED
+        ws = torch.empty((S.seedlm_gemm_decoded_bytes(m) // 2,), dtype=torch.float16, device=dev)
+        with pytest.raises(S.SeedLMError) as err:
+            S.seedlm_gemm_decoded(m, X, Y, ws)
+        assert err.value.status == S.E_UNSUPPORTED

@@ -38,21 +38,24 @@ def test_status_strings():
     assert S.status_string(12345) == "unknown status"
 
 
-@pytest.mark.parametrize("C,P,rows,cols", [
-    (8, 3, 1, 1), (8, 3, 5, 320), (8, 3, 9, 8 * 77 + 3), (12, 4, 6, 401), (12, 4, 4, 12 * 64),
+@pytest.mark.parametrize("C,P,K,rows,cols", [
+    (8, 3, 16, 1, 1), (8, 3, 16, 5, 320), (8, 3, 16, 9, 8 * 77 + 3), (12, 4, 16, 6, 401),
+    (12, 4, 16, 4, 12 * 64), (12, 4, 16, 3, 12 * 37 + 5), (8, 4, 16, 7, 8 * 45 + 1),
+    (12, 3, 20, 5, 12 * 35 + 7),
 ])
-def test_host_packer_matches_oracle_writer_and_reader(C, P, rows, cols):
+def test_host_packer_matches_oracle_writer_and_reader(C, P, K, rows, cols):
     S = _lib()
     from oracle import seedlm_oracle as O
 
     rng = np.random.default_rng(rows * 1000 + cols)
     nb = -(-cols // C)
-    s = rng.integers(1, 65536, (rows, nb)).astype(np.uint16)
-    c = rng.integers(-8, 8, (rows, nb, P)).astype(np.int8)
+    Q = O.PACKED_FORMATS[(C, P, K)]
+    s = rng.integers(1, 1 << K, (rows, nb)).astype(np.uint16 if K <= 16 else np.uint32)
+    c = rng.integers(-(1 << (Q - 1)), 1 << (Q - 1), (rows, nb, P)).astype(np.int8)
     e = rng.integers(-15, 1, (rows, nb)).astype(np.int8)
-    buf = S.seedlm_pack_host(s, c, e, rows, cols, C, P)
-    assert buf == O.write_packed(s, c, e, rows, cols, C, P)
-    s2, c2, e2 = O.read_packed(buf, rows, cols, C, P)
+    buf = S.seedlm_pack_host(s, c, e, rows, cols, C, P, K)
+    assert buf == O.write_packed(s, c, e, rows, cols, C, P, K=K)
+    s2, c2, e2 = O.read_packed(buf, rows, cols, C, P, K=K)
     assert (s2 == s).all() and (c2 == c).all() and (e2 == e).all()
 
 
@@ -76,8 +79,22 @@ def test_host_packer_rejects_bad_records():
     assert S.pack_host_status(s, c, e, 0, cols, 8, 3) == S.E_INVALID
     assert S.pack_host_status(s, c, e, rows, 0, 8, 3) == S.E_INVALID
     assert S.pack_host_status(s, c, e, rows, cols, 8, 3, K=12) == S.E_UNSUPPORTED
-    assert S.pack_host_status(s, c, e, rows, cols, 8, 4) == S.E_UNSUPPORTED
     assert S.pack_host_status(s, c, e, rows, cols, 16, 3) == S.E_UNSUPPORTED
+    assert S.pack_host_status(s, c, e, rows, cols, 12, 3, K=16) == S.E_UNSUPPORTED
+    # (8, 4, 16) takes 3-bit coefficients: [-4, 3]
+    c4 = np.zeros((rows, 3, 4), np.int8)
+    c4[1, 1] = (3, -4, 0, 1)
+    assert S.pack_host_status(s, c4, e, rows, cols, 8, 4) == S.OK
+    bad = c4.copy(); bad[2, 2, 3] = 4
+    assert S.pack_host_status(s, bad, e, rows, cols, 8, 4) == S.E_INVALID
+    bad = c4.copy(); bad[0, 0, 0] = -5
+    assert S.pack_host_status(s, bad, e, rows, cols, 8, 4) == S.E_INVALID
+    # (12, 3, 20) takes 20-bit seeds: [1, 2^20 - 1]
+    s20 = np.full((rows, 2), (1 << 20) - 1, np.uint32)
+    c3, e2 = np.zeros((rows, 2, 3), np.int8), np.zeros((rows, 2), np.int8)
+    assert S.pack_host_status(s20, c3, e2, rows, cols, 12, 3, K=20) == S.OK
+    bad = s20.copy(); bad[1, 1] = 1 << 20
+    assert S.pack_host_status(bad, c3, e2, rows, cols, 12, 3, K=20) == S.E_INVALID
     # null pointers and a too-small destination
     L = S.lib()
     n = ctypes.c_size_t(0)

@@ -83,16 +83,67 @@ def test_exponent_positions_worked_by_hand_3bit():
     assert ((v >> 8) & 0xF) == 0
 
 
-@pytest.mark.parametrize("C,P,rows,cols", [(8, 3, 7, 8 * 70), (12, 4, 6, 12 * 33 + 5), (8, 3, 4, 3)])
-def test_round_trip(C, P, rows, cols):
+def test_word_and_exponent_positions_worked_by_hand_3bit_panels_of_16():
+    # rows=3 -> Mp=8; cols=12*20 -> nb=20: C=12 panels hold 16 blocks, so panel
+    # 0 has 16 blocks (rows of 16 words) and panel 1 has 4 (rows of 4 words,
+    # starting at word 8*16 = 128).  160 words = 640 B; exponents start at byte
+    # 768 and hold 160/4 = 40 uint16 (panel 0: 8 rows x 4, panel 1 from 32).
+    rows, cols = 3, 12 * 20
+    seeds, coeffs, exps = _unique_records(rows, 20, 4)
+    buf = O.write_packed(seeds, coeffs, exps, rows, cols, 12, 4)
+    assert len(buf) == 768 + 80
+    assert O.padding_words_ok(buf, rows, cols, 12, 4)
+
+    def seed_at(k):
+        return int.from_bytes(buf[4 * k:4 * k + 2], "little")
+
+    def nibble_at(k, j):
+        return (int.from_bytes(buf[768 + 2 * k:768 + 2 * k + 2], "little") >> (4 * j)) & 0xF
+
+    # (r=2, b=17): panel 1, q=1: 128 + 2*4 + ((1-2) mod 4 = 3) = 139; exps 32 + 2 = 34, nibble 3
+    assert seed_at(139) == seeds[2, 17] and nibble_at(34, 3) == exps[2, 17] + 15
+    # (r=1, b=14): panel 0, q=14: 16 + 12 + ((14-1) mod 4 = 1) = 29; exps 4 + 3 = 7, nibble 1
+    assert seed_at(29) == seeds[1, 14] and nibble_at(7, 1) == exps[1, 14] + 15
+    # (r=0, b=19): panel 1, q=3: 128 + 3 = 131; exps 32, nibble 3
+    assert seed_at(131) == seeds[0, 19] and nibble_at(32, 3) == exps[0, 19] + 15
+    # the first padding row of panel 1 (r=3) starts at word 128 + 12 = 140
+    assert all(int.from_bytes(buf[4 * k:4 * k + 4], "little") == 1 for k in range(140, 160))
+
+
+def test_words_of_the_other_formats_worked_by_hand():
+    # (8,4,16), 3-bit coefficients: seed 0x1234, t = (1, -2, 3, -4), e = -6:
+    # 0x1234 | 1<<16 | 6<<19 | 3<<22 | 4<<25 | 9<<28 = 0x98F11234
+    buf = O.write_packed(np.array([[0x1234]], np.uint16), np.array([[[1, -2, 3, -4]]], np.int8),
+                         np.array([[-6]], np.int8), 1, 8, 8, 4, K=16)
+    assert len(buf) == 4 * 8 * 4
+    assert int.from_bytes(buf[0:4], "little") == 0x98F11234
+    # (12,3,20): seed 0xABCDE, t = (7, -8, -1), e = -15:
+    # 0xABCDE | 7<<20 | 8<<24 | 15<<28 = 0xF87ABCDE, exponent nibble 0
+    buf = O.write_packed(np.array([[0xABCDE]], np.uint32), np.array([[[7, -8, -1]]], np.int8),
+                         np.array([[-15]], np.int8), 1, 12, 12, 3, K=20)
+    assert len(buf) == 256 + 16
+    assert int.from_bytes(buf[0:4], "little") == 0xF87ABCDE
+    assert buf[256] & 0xF == 0
+    # 3-bit coefficients outside [-4, 3] are rejected
+    with pytest.raises(ValueError):
+        O.write_packed(np.array([[1]], np.uint16), np.array([[[4, 0, 0, 0]]], np.int8),
+                       np.array([[0]], np.int8), 1, 8, 8, 4, K=16)
+
+
+@pytest.mark.parametrize("C,P,K,rows,cols", [(8, 3, 16, 7, 8 * 70), (12, 4, 16, 6, 12 * 33 + 5),
+                                             (8, 3, 16, 4, 3), (8, 4, 16, 5, 8 * 40 + 3),
+                                             (12, 3, 20, 9, 12 * 37 + 8)])
+def test_round_trip(C, P, K, rows, cols):
     rng = np.random.default_rng(rows * cols)
     nb = -(-cols // C)
-    seeds = rng.integers(1, 65536, (rows, nb)).astype(np.uint16)
-    coeffs = rng.integers(-8, 8, (rows, nb, P)).astype(np.int8)
+    Q = O.PACKED_FORMATS[(C, P, K)]
+    seeds = rng.integers(1, 1 << K, (rows, nb)).astype(np.uint16 if K <= 16 else np.uint32)
+    coeffs = rng.integers(-(1 << (Q - 1)), 1 << (Q - 1), (rows, nb, P)).astype(np.int8)
     exps = rng.integers(-15, 1, (rows, nb)).astype(np.int8)
-    buf = O.write_packed(seeds, coeffs, exps, rows, cols, C, P)
+    buf = O.write_packed(seeds, coeffs, exps, rows, cols, C, P, K=K)
     assert len(buf) == O.packed_size(rows, cols, C, P)
-    s, c, e = O.read_packed(buf, rows, cols, C, P)
+    assert O.padding_words_ok(buf, rows, cols, C, P)
+    s, c, e = O.read_packed(buf, rows, cols, C, P, K=K)
     assert (s == seeds).all() and (c == coeffs).all() and (e == exps).all()
 
 
