@@ -17,9 +17,10 @@ extern "C" {
 
 /*
  * seedlm_gemv_variant -- seedlm_gemv with the kernel chosen by the caller.
- * SEEDLM_VARIANT_AUTO is exactly seedlm_gemv (LUT for batch 1, both formats;
- * MFMA for every other fp16-x/fp16-y call; SIMPLE otherwise, where fp32 x or
- * fp32 y needs fp32 weights for the 1e-5 bar).  The others:
+ * SEEDLM_VARIANT_AUTO is exactly seedlm_gemv (for the pages' two formats: LUT
+ * at batch 1, DIRECT for small batch-1 calls, MFMA for every other fp16-x/
+ * fp16-y call; DIRECT otherwise, where fp32 x or fp32 y needs fp32 weights for
+ * the 1e-5 bar, and for the other packed formats).  The others:
  *   SEEDLM_VARIANT_LUT     batch 1, both formats: basis bits from GF(2) byte
  *                          tables in LDS, dot with x through activation byte
  *                          tables in LDS
@@ -31,6 +32,11 @@ extern "C" {
  *                          fp32 weights
  *   SEEDLM_VARIANT_MFMA    fp16 x and y, any batch: each block decoded once to
  *                          fp16 (weights x 2^10) in MFMA operand registers
+ *   SEEDLM_VARIANT_DIRECT  any format, batch and dtypes: exact per-lane decode
+ *                          of one block per lane, whole rows per workgroup, one
+ *                          launch (what seedlm_gemv runs for the other packed
+ *                          formats, for fp32 calls at batch > 1 and for small
+ *                          batch-1 calls)
  * Scratch, streams and errors as for seedlm_gemv; SEEDLM_E_UNSUPPORTED when
  * the variant does not take the format, batch or dtypes.
  */
@@ -39,6 +45,7 @@ extern "C" {
 #define SEEDLM_VARIANT_TABLE 2
 #define SEEDLM_VARIANT_SIMPLE 3
 #define SEEDLM_VARIANT_MFMA 4
+#define SEEDLM_VARIANT_DIRECT 5
 SEEDLM_API int seedlm_gemv_variant(seedlm_handle h, const void* x, void* y, int batch,
                                    int x_dtype, int y_dtype, int variant, void* stream);
 

@@ -18,10 +18,12 @@ from ._binding import (  # noqa: F401
     OK,
     STREAM_READ_SINK,
     VARIANT_AUTO,
+    VARIANT_DIRECT,
     VARIANT_MFMA,
     VARIANT_LUT,
     VARIANT_SIMPLE,
     VARIANT_TABLE,
+    GemvManyCall,
     SeedLMEncoder,
     SeedLMError,
     SeedLMMatrix,

@@ -28,6 +28,7 @@ VARIANT_LUT = 1
 VARIANT_TABLE = 2
 VARIANT_SIMPLE = 3
 VARIANT_MFMA = 4
+VARIANT_DIRECT = 5
 
 EXPORTED = (
     "seedlm_pack_host",
@@ -262,8 +263,32 @@ def _many_args(mats, xs, ys, batch):
     Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
     xdt = _dtype_code(xs[0]) if n else F16
     ydt = _dtype_code(ys[0]) if n else F16
+    # the arrays ride along in the cast pointers' _objects, so they stay alive
     return (ctypes.cast(H, ctypes.c_void_p), ctypes.cast(X, ctypes.c_void_p),
             ctypes.cast(Y, ctypes.c_void_p), n, batch, xdt, ydt)
+
+
+class GemvManyCall:
+    """One seedlm_gemv_many call whose arguments are checked and marshalled once,
+    for loops that repeat the same call (a serving step, a benchmark): calling
+    the object only crosses the C ABI.  It keeps the matrices and tensors alive;
+    their contents may change between calls, their storage may not."""
+
+    def __init__(self, mats, xs, ys, batch=1, stream=None):
+        self._args = _many_args(mats, xs, ys, batch)
+        self._keep = (list(mats), list(xs), list(ys))
+        L = lib()
+        self._fns = {"all": L.seedlm_gemv_many, "begin": L.seedlm_gemv_many_begin,
+                     "end": L.seedlm_gemv_many_end, "noalloc": L.seedlm_gemv_many_noalloc}
+        self._stream = None if stream is None else _stream_ptr(stream)
+
+    def __call__(self, stream=None, phase="all"):
+        """Run on `stream` (default: the one given at construction, else torch's
+        current stream)."""
+        sp = _stream_ptr(stream) if stream is not None or self._stream is None else self._stream
+        st = self._fns[phase](*self._args, sp)
+        if st != OK:
+            raise SeedLMError(st, "seedlm_gemv_many")
 
 
 def seedlm_gemv_many(mats, xs, ys, batch=1, stream=None, phase="all"):

@@ -1,4 +1,5 @@
 // C-ABI entry points that launch kernels: argument checks and kernel choice.
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -94,7 +95,20 @@ thread_local TimingEvents t_active;   // handed out during a call's main launche
 
 // ---- kernel choice and grouping ----
 
-enum Kind { kLut8, kLut12, kMfma, kSimple, kTable };
+enum Kind { kLut8, kLut12, kMfma, kSimple, kTable, kDirect };
+
+// Batch-1 calls in the pages' formats whose launch group holds at most this
+// many blocks, in matrices of at most kDirectMaxPanels panels per row, run the
+// direct kernel: there the table builds and the second (reduction) launch of
+// the table-lookup kernels cost more than the direct kernel's exact per-lane
+// decode.  GPU time per call (events around it): 4-bit 2048x2048 7.0 us direct
+// against 11.2 us, 2048x4096 9.1 against 12.2, 4096x4096 12.9 against 12.6,
+// 1024x8192 (32 panels) 13.0 against 12.3; 3-bit 4096x4096 13.7 against 16.2,
+// 4096x8192 22.2 against 18.7 (the 3-bit table-lookup kernel does about twice
+// the work per weight).
+constexpr int64_t kDirectMaxBlocks4 = 5 << 18;  // 1.25M blocks
+constexpr int64_t kDirectMaxBlocks3 = 1 << 21;  // 2M blocks
+constexpr int64_t kDirectMaxPanels = 24;
 
 struct Group {
   int begin, count;
@@ -131,23 +145,46 @@ int next_group(const seedlm_handle* hs, int n, int batch, int xdt, int ydt, int 
         if (!f16 || !fast(0)) return SEEDLM_E_UNSUPPORTED;
         *g = {0, 1, kMfma};
         return SEEDLM_OK;
+      case SEEDLM_VARIANT_DIRECT:
+        if (!direct_fits(hs[0], batch)) return SEEDLM_E_UNSUPPORTED;
+        *g = {0, 1, kDirect};
+        return SEEDLM_OK;
       default:
         return SEEDLM_E_UNSUPPORTED;
     }
   }
+  auto same_format = [&](int a, int b) {
+    return hs[a]->C == hs[b]->C && hs[a]->P == hs[b]->P && hs[a]->K == hs[b]->K;
+  };
+  // Up to 8 consecutive matrices of i's format that the direct kernel takes.
+  auto direct_run = [&]() {
+    int k = 0;
+    while (i + k < n && k < 8 && same_format(i, i + k) && direct_fits(hs[i + k], batch)) ++k;
+    return k;
+  };
   int k = 0;
   Kind kind = kSimple;
-  if (!fast(i)) {
-    k = 1;
+  if (!fast(i) || (batch > 1 && !f16)) {
+    // the exact kernels: direct for every shape it takes, else one wave per row
+    k = direct_run();
+    if (k > 0) kind = kDirect;
+    else k = 1;
   } else if (batch == 1) {
-    const bool four = hs[i]->is_4bit();
-    kind = four ? kLut8 : kLut12;
-    while (i + k < n && k < 8 && fast(i + k) && hs[i + k]->is_4bit() == four) ++k;
-  } else if (f16) {
+    while (i + k < n && k < 8 && same_format(i, i + k)) ++k;
+    kind = hs[i]->is_4bit() ? kLut8 : kLut12;
+    int64_t blocks = 0, np_max = 0;
+    bool fits = true;
+    for (int j = i; j < i + k; ++j) {
+      blocks += hs[j]->rows * hs[j]->nb;
+      np_max = std::max<int64_t>(np_max, hs[j]->np);
+      fits = fits && direct_fits(hs[j], batch);
+    }
+    if (fits && blocks <= (hs[i]->is_4bit() ? kDirectMaxBlocks4 : kDirectMaxBlocks3) &&
+        np_max <= kDirectMaxPanels)
+      kind = kDirect;
+  } else {
     kind = kMfma;
     while (i + k < n && k < 8 && fast(i + k)) ++k;
-  } else {
-    k = 1;
   }
   *g = {i, k, kind};
   return SEEDLM_OK;
@@ -291,6 +328,10 @@ int run_gemv(const seedlm_handle* hs, const void* const* x, void* const* y, int 
         break;
       case kSimple:
         st = (phases & 1) ? launch_gemv_simple(gh[0], gx[0], gy[0], batch, xdt, ydt, s)
+                          : SEEDLM_OK;
+        break;
+      case kDirect:
+        st = (phases & 1) ? launch_gemv_direct_group(gh, gx, gy, g.count, batch, xdt, ydt, s)
                           : SEEDLM_OK;
         break;
     }

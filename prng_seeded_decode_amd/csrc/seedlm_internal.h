@@ -123,6 +123,11 @@ int launch_gemv_lut_group(const seedlm_matrix* const* hs, const void* const* xs,
 int launch_gemv_lut12_group(const seedlm_matrix* const* hs, const void* const* xs,
                             void* const* ys, float* const* partials, int n, int xdt, int ydt,
                             hipStream_t s, int phases);
+// Direct kernel (any packed format, batch 1..16, any dtypes): whole rows per
+// workgroup, no partials, one launch.  direct_fits: x of the call fits its LDS.
+bool direct_fits(const seedlm_matrix* h, int batch);
+int launch_gemv_direct_group(const seedlm_matrix* const* hs, const void* const* xs,
+                             void* const* ys, int n, int batch, int xdt, int ydt, hipStream_t s);
 // Up to 8 matrices at batch > 1 (fp16): phases & 1 the decode-GEMM launches
 // (one per format and tiling present), phases & 2 one reduction launch.
 int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs,

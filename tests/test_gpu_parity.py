@@ -101,7 +101,8 @@ def test_small_full_parity(C, P, rows, cols, batch, xdt, ydt):
     assert O.normwise_error(y, y_ref) <= TOL[ydt]
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4], ids=["auto", "lut", "table", "simple", "mfma"])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5],
+                         ids=["auto", "lut", "table", "simple", "mfma", "direct"])
 @pytest.mark.parametrize("C,P,rows,cols", [(8, 3, 203, 8 * 97 + 3), (12, 4, 96, 12 * 77 + 8)])
 def test_variants_agree_with_oracle(variant, C, P, rows, cols):
     S = _S()
@@ -291,9 +292,15 @@ def test_gemv_many_matches_oracle_and_single_calls():
         ys3 = [torch.empty_like(y) for y in ys]
         for m, x, y in zip(mats, xd, ys3):
             S.seedlm_gemv(m, x, y)
+        # the same call marshalled once and run twice
+        ys4 = [torch.empty_like(y) for y in ys]
+        call = S.GemvManyCall(mats, xd, ys4)
+        call()
+        call(phase="begin")
+        call(phase="end")
         torch.cuda.synchronize()
-        for a, b, c3 in zip(ys, ys2, ys3):
-            assert torch.equal(a, b) and torch.equal(a, c3)
+        for a, b, c3, c4 in zip(ys, ys2, ys3, ys4):
+            assert torch.equal(a, b) and torch.equal(a, c3) and torch.equal(a, c4)
 
 
 def test_gemv_many_takes_a_repeated_handle():
@@ -606,3 +613,51 @@ def test_prefill_paths_reject_the_other_formats():
         with pytest.raises(S.SeedLMError) as err:
             S.seedlm_gemm_decoded(m, X, Y, ws)
         assert err.value.status == S.E_UNSUPPORTED
+
+
+DIRECT_CASES = [
+    # (C, P, K, rows, cols, batch, xdt, ydt): the direct kernel in every format,
+    # ragged rows, panels and blocks, batch 1 to 16, every dtype pair
+    (8, 3, 16, 203, 8 * 97 + 3, 1, "f32", "f32"),
+    (8, 3, 16, 2048, 2048, 1, "f16", "f16"),
+    (8, 3, 16, 40, 520, 5, "f16", "f32"),
+    (8, 3, 16, 1, 1, 16, "f32", "f16"),
+    (12, 4, 16, 96, 12 * 77 + 8, 1, "f16", "f16"),
+    (12, 4, 16, 17, 12 * 45 + 5, 16, "f32", "f32"),
+    (8, 4, 16, 300, 8 * 70, 2, "f16", "f16"),
+    (12, 3, 20, 70, 12 * 40 + 4, 1, "f32", "f32"),
+    (12, 3, 20, 33, 12 * 33, 16, "f16", "f16"),
+]
+
+
+@pytest.mark.parametrize("C,P,K,rows,cols,batch,xdt,ydt", DIRECT_CASES,
+                         ids=[f"C{c[0]}P{c[1]}K{c[2]}_{c[3]}x{c[4]}_b{c[5]}_{c[6]}{c[7]}"
+                              for c in DIRECT_CASES])
+def test_direct_kernel_against_oracle(C, P, K, rows, cols, batch, xdt, ydt):
+    S = _S()
+    Q = O.PACKED_FORMATS[(C, P, K)]
+    rng = np.random.default_rng(rows * 7 + cols * 3 + batch)
+    s, c, e = _records_k(rng, rows, cols, C, P, K, Q)
+    m = S.seedlm_pack(s, c, e, rows, cols, C, P, K)
+    W_ref = O.decode_rows(s, c, e, cols, C, P, K=K)
+    x = rng.standard_normal((batch, cols)).astype(np.float16 if xdt == "f16" else np.float32)
+    _say(f"direct C={C} P={P} K={K} {rows}x{cols} batch={batch} {xdt}->{ydt}")
+    y = _gemv_gpu(m, x, ydt, variant=5)
+    assert O.normwise_error(y, O.gemv(W_ref, x)) <= TOL[ydt]
+    assert np.array_equal(y, _gemv_gpu(m, x, ydt, variant=5))  # deterministic
+
+
+def test_direct_kernel_on_long_rows_agrees_with_the_per_row_kernel():
+    # A 14400-column (12,3,20) matrix (75 panels, x read from global memory),
+    # the direct kernel against the oracle and against the one-wave-per-row
+    # kernel, at the fp32 bar.
+    S = _S()
+    rows, cols, C, P, K = 24, 12 * 1200, 12, 3, 20
+    rng = np.random.default_rng(12)
+    s, c, e = _records_k(rng, rows, cols, C, P, K, 4)
+    m = S.seedlm_pack(s, c, e, rows, cols, C, P, K)
+    x = rng.standard_normal((2, cols)).astype(np.float32)
+    y_ref = O.gemv(O.decode_rows(s, c, e, cols, C, P, K=K), x)
+    y = _gemv_gpu(m, x, "f32")
+    assert O.normwise_error(y, y_ref) <= TOL["f32"]
+    assert O.normwise_error(_gemv_gpu(m, x, "f32", variant=3), y_ref) <= TOL["f32"]
