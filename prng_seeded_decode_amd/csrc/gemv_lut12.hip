@@ -258,10 +258,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
       v4u w;
       uint32_t e;
     };
+    // Slabs past the segment (the look-ahead of its last loads) get an
+    // out-of-range offset: they read zeros and fetch nothing from memory.
     auto load = [&](int sl) {
       Slab s;
-      s.w = __builtin_amdgcn_raw_buffer_load_b128(rsrc, wbase + (uint32_t)sl * wstride, 0, 0);
-      s.e = __builtin_amdgcn_raw_buffer_load_b16(rsrc, ebase + (uint32_t)sl * estride, 0, 0);
+      const bool in = sl < sb;
+      s.w = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc, in ? wbase + (uint32_t)sl * wstride : 0x80000000u, 0, 0);
+      s.e = __builtin_amdgcn_raw_buffer_load_b16(
+          rsrc, in ? ebase + (uint32_t)sl * estride : 0x80000000u, 0, 0);
       return s;
     };
     const int s_first = sa + wave;
