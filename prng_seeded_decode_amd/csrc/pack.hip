@@ -149,7 +149,7 @@ int seedlm_pack(const void* seeds, const int8_t* coeffs, const int8_t* exps, int
 
   seedlm_matrix* h = new (std::nothrow) seedlm_matrix();
   if (!h) {
-    hipHostFree(host);
+    (void)hipHostFree(host);
     return SEEDLM_E_NOMEM;
   }
   h->rows = rows;
@@ -172,7 +172,7 @@ int seedlm_pack(const void* seeds, const int8_t* coeffs, const int8_t* exps, int
   if (rc == SEEDLM_OK && hipMalloc(&h->d_buf, L.bytes) != hipSuccess) rc = SEEDLM_E_NOMEM;
   if (rc == SEEDLM_OK && hipMemcpy(h->d_buf, host, L.bytes, hipMemcpyHostToDevice) != hipSuccess)
     rc = SEEDLM_E_DEVICE;
-  hipHostFree(host);
+  (void)hipHostFree(host);
   // The device's 2^16-entry extension table (TABLE variant) is built here, once
   // per device, so that no gemv call allocates or synchronises for it.
   if (rc == SEEDLM_OK) rc = ensure_ext_table(h->device);
