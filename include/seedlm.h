@@ -48,8 +48,8 @@
  *             ((q-r) mod 4) of uint16 number p*Mp*(PB/4) + r*(Wp'/4) + q/4 of
  *             an array starting at byte align256(4 * total words).
  *   Kernels   every call takes every format; the batch-1 table-lookup and
- *             matrix-core kernels run the pages' two formats, the others run
- *             the exact per-lane kernel (seedlm_gemv) and seedlm_decode.
+ *             matrix-core kernels run the pages' two formats, the other two
+ *             run the direct per-lane kernel (seedlm_gemv) and seedlm_decode.
  *
  * Conventions: every call returns a status (0 = SEEDLM_OK, negative = error);
  * no C++ exception crosses this boundary.  "device" pointers are HIP device
@@ -136,9 +136,12 @@ SEEDLM_API int seedlm_pack(const void* seeds, const int8_t* coeffs,
  *   x  device [batch][cols], x_dtype SEEDLM_F32 or SEEDLM_F16 (row-major)
  *   y  device [batch][rows], y_dtype SEEDLM_F32 or SEEDLM_F16 (fp16: round to
  *      nearest even); both caller-owned.
- *   batch in [1, SEEDLM_MAX_BATCH].  batch 1 runs the fused decode-GEMV;
- *   batch > 1 decodes each weight tile once and contracts it on the matrix
- *   cores in fp16 with fp32 accumulation.
+ *   batch in [1, SEEDLM_MAX_BATCH].  batch 1 runs the fused decode-GEMV
+ *   (activation-side table lookups; small matrices, the direct kernel); batch
+ *   > 1 with fp16 x and y decodes each weight tile once and contracts it on
+ *   the matrix cores in fp16 with fp32 accumulation; fp32 x or y at batch > 1,
+ *   and the two extra formats, run the direct kernel, which rebuilds every
+ *   weight exactly in fp32 and needs no scratch.
  * Asynchronous on `stream`.  The kernels that split a row's reduction over
  * workgroups write fp32 partials into scratch that the library keeps per
  * (device, stream): calls on one stream share it in stream order, and calls on
