@@ -133,7 +133,8 @@ def parse_args():
 
 
 def cpu_baseline(cfg, budget_s):
-    """Time the oracle (decode + float64 matvec) on sampled rows of each matrix."""
+    """Time the oracle (decode + float64 matvec) on sampled rows of each matrix,
+    on one host thread (BLAS limited to one thread for the matvec too)."""
     from oracle import seedlm_oracle as O
     from workloads import gen_records, gen_x
 
@@ -147,34 +148,38 @@ def cpu_baseline(cfg, budget_s):
         x = gen_x(cfg.config_id, mid, 1, mat.cols, cfg.x_dtype)
         recs.append((mat, s, c, e, x))
     rng = np.random.default_rng(12345)
-    while t_dec + t_mv < budget_s:
-        for mat, s, c, e, x in recs:
-            pick = rng.choice(mat.rows, size=rows_per, replace=False)
-            t0 = time.perf_counter()
-            W = O.decode_rows(s[pick], c[pick], e[pick], mat.cols, cfg.C, cfg.P)
-            t1 = time.perf_counter()
-            O.gemv(W, x)
-            t2 = time.perf_counter()
-            t_dec += t1 - t0
-            t_mv += t2 - t1
-            weights += rows_per * mat.cols
-        rounds += 1
-        rows_per = min(rows_per * 2, 256)
-    try:
-        from threadpoolctl import threadpool_info
+    import contextlib
 
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    try:
+        from threadpoolctl import threadpool_limits
+
+        one_thread = threadpool_limits(limits=1)
     except Exception:
-        blas = 1
+        one_thread = contextlib.nullcontext()
+    with one_thread:
+        while t_dec + t_mv < budget_s:
+            for mat, s, c, e, x in recs:
+                pick = rng.choice(mat.rows, size=min(rows_per, mat.rows), replace=False)
+                t0 = time.perf_counter()
+                W = O.decode_rows(s[pick], c[pick], e[pick], mat.cols, cfg.C, cfg.P)
+                t1 = time.perf_counter()
+                O.gemv(W, x)
+                t2 = time.perf_counter()
+                t_dec += t1 - t0
+                t_mv += t2 - t1
+                weights += len(pick) * mat.cols
+            rounds += 1
+            rows_per = min(rows_per * 2, 256)
+    n = len(cfg.matrices)
     return {
         "value": weights / (t_dec + t_mv),
         "unit": "weights/s",
-        "cores": int(max(1, blas)),
+        "cores": 1,
         "kind": "oracle",
-        "sample": (f"{weights} weights from sampled rows of the 7 layer matrices "
-                   f"({rounds} rounds); decode {t_dec:.2f} s (NumPy, 1 thread), "
-                   f"float64 matvec {t_mv:.2f} s; host cores available "
-                   f"{len(os.sched_getaffinity(0))}"),
+        "sample": (f"{weights} weights from sampled rows of the {n} matri"
+                   f"{'ces' if n > 1 else 'x'} ({rounds} rounds), one host thread: "
+                   f"decode {t_dec:.2f} s, float64 matvec {t_mv:.2f} s; host cores "
+                   f"available {len(os.sched_getaffinity(0))}"),
     }
 
 
