@@ -329,7 +329,7 @@ __global__ void __launch_bounds__(kThreads, 1)
         const half2v p12 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ext[k], 0x64646464u, 0x01040007u));
         const half2v p3 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ext[k], 0x64646464u, 0x0C0C0005u));
         const float t2 = (float)(((int)(wk << 4)) >> 28);
-        const float mid = __builtin_amdgcn_fdot2(tc, p12, t2 * (float)p3[0], false);
+        const float mid = __builtin_amdgcn_fdot2(tc, p12, __builtin_fmaf(t2, (float)p3[0], 0.f), false);
         float V = t2 * (l0b2[k] + l2b4[k]);
         V = fmaf((float)tc[0], l0b0[k] + l2b2[k], V);
         V = fmaf((float)tc[1], l0b1[k] + l2b3[k], V);
