@@ -158,18 +158,24 @@ bool make_plan(hipblasLtHandle_t lt, int64_t rows, int64_t cols, int64_t ntok, s
   ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
        hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
                                              &max_ws, sizeof(max_ws)) == HIPBLAS_STATUS_SUCCESS;
-  hipblasLtMatmulHeuristicResult_t res[1];
+  // The heuristic's first candidate can ask for more scratch than is offered
+  // (8192 x 28672 at 512 and 1024 tokens did, despite the preference), so the
+  // plan takes the first of its candidates that runs within it.
+  constexpr int kCandidates = 16;
+  hipblasLtMatmulHeuristicResult_t res[kCandidates];
   int found = 0;
-  ok = ok && hipblasLtMatmulAlgoGetHeuristic(lt, p.desc, p.a, p.b, p.d, p.d, pref, 1, res,
-                                             &found) == HIPBLAS_STATUS_SUCCESS &&
-       found >= 1 && res[0].state == HIPBLAS_STATUS_SUCCESS && res[0].workspaceSize <= scratch_max;
+  ok = ok && hipblasLtMatmulAlgoGetHeuristic(lt, p.desc, p.a, p.b, p.d, p.d, pref, kCandidates,
+                                             res, &found) == HIPBLAS_STATUS_SUCCESS;
   if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (!ok) {
+  int pick = -1;
+  for (int i = 0; ok && i < found && i < kCandidates && pick < 0; ++i)
+    if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= scratch_max) pick = i;
+  if (pick < 0) {
     destroy(p);
     return false;
   }
-  p.algo = res[0].algo;
-  p.scratch = res[0].workspaceSize;
+  p.algo = res[pick].algo;
+  p.scratch = res[pick].workspaceSize;
   return true;
 }
 
