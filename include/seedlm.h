@@ -183,7 +183,7 @@ SEEDLM_API int seedlm_gemv_many(const seedlm_handle* handles, const void* const*
  * partials into the stream's scratch), _end adds the partials into y.  Called
  * with identical arguments on one stream they equal seedlm_gemv_many; the
  * split lets a caller time the two halves.  Between the two calls no other
- * gemv call may use that stream (it would reuse the scratch).
+ * gemv or gemm call may use that stream (it would reuse the scratch).
  */
 SEEDLM_API int seedlm_gemv_many_begin(const seedlm_handle* handles, const void* const* x,
                                       void* const* y, int n, int batch, int x_dtype,
@@ -225,11 +225,11 @@ SEEDLM_API int seedlm_gemv_scratch_bytes(const seedlm_handle* handles, int n, in
                                          int x_dtype, int y_dtype, size_t* bytes);
 
 /*
- * seedlm_scratch_release -- free the gemv scratch of every stream on every
- * device (each device is synchronised first; graphs captured from earlier
+ * seedlm_scratch_release -- free the gemv and gemm scratch of every stream on
+ * every device (each device is synchronised first; graphs captured from earlier
  * calls must not be replayed afterwards).  Later calls allocate again.  Call
- * it after destroying a stream that gemv calls used, before a new stream could
- * take over its handle value.  Errors: SEEDLM_E_DEVICE.
+ * it after destroying a stream that gemv or gemm calls used, before a new
+ * stream could take over its handle value.  Errors: SEEDLM_E_DEVICE.
  */
 SEEDLM_API int seedlm_scratch_release(void);
 
@@ -263,29 +263,47 @@ SEEDLM_API const char* seedlm_status_string(int status);
  * (paperhub.cn rebuttal text before Eq. (1): weights are reconstructed on the
  * fly from s and t and used to compute the activations).  Each 128-row tile of
  * W is decoded exactly once per 256 or 512 activation rows and contracted on
- * the matrix cores (fp16 operands, fp32 accumulation).
+ * the matrix cores (fp16 operands, fp32 accumulation).  Where the 4-bit
+ * format's 128 x 512 tiles would leave over half of the compute units idle in
+ * the last round of workgroups (or a small matrix has too few tiles to fill
+ * them), those tiles split their K range over up to 8 workgroups, which write
+ * fp32 partial tiles that a second launch adds in a fixed order: results are
+ * deterministic for a given shape and device.
  *   X  device fp16 [ntok][cols], 16-byte aligned (row-major)
  *   Y  device fp16 [ntok][rows] (round to nearest even); both caller-owned
  *   ntok >= 1.  Both packed formats (C = 8 and C = 12) with cols a multiple of
  *   8, fp16 X and Y only; other dtypes return SEEDLM_E_UNSUPPORTED (for up to
  *   16 rows seedlm_gemv covers them), as do X or the packed buffer of 2 GiB or
  *   more and ntok above 16,776,960.
- * Asynchronous on `stream`; no scratch, so calls may overlap.  Call with the
- * device h was packed on current.
+ * Asynchronous on `stream`.  Split tiles keep their partials in the stream's
+ * scratch, the gemv scratch (same rules: calls on different streams may
+ * overlap, a call that needs more than the stream has allocates -- not inside
+ * graph capture -- and seedlm_scratch_release frees it);
+ * seedlm_gemm_scratch_bytes gives a call's size (at most 64 MiB on a
+ * 256-compute-unit device).  Call with the device h was packed on current.
  * Errors: SEEDLM_E_INVALID (null, ntok < 1, another device current),
- * SEEDLM_E_UNSUPPORTED (format,
- * dtype, alignment), SEEDLM_E_DEVICE (launch failure).
+ * SEEDLM_E_UNSUPPORTED (format, dtype, alignment), SEEDLM_E_NOMEM (scratch),
+ * SEEDLM_E_DEVICE (launch failure).
  */
 SEEDLM_API int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok,
                            int x_dtype, int y_dtype, void* stream);
+
+/*
+ * seedlm_gemm_scratch_bytes -- the scratch bytes seedlm_gemm(h, ., ., ntok, ...)
+ * uses on the current device (0 when it splits no tile, and for the 3-bit
+ * format, whose kernel does not split).  *bytes is set on success.
+ * Errors: SEEDLM_E_INVALID (null, ntok < 1).
+ */
+SEEDLM_API int seedlm_gemm_scratch_bytes(seedlm_handle h, int64_t ntok, size_t* bytes);
 
 /*
  * seedlm_gemm_decoded -- the same product through a decoded copy of W: the
  * matrix is rebuilt once, exactly, into `workspace` as fp16(w * 2^10) (the
  * values the matrix-core kernels feed their MFMAs), then multiplied by a
  * hipBLASLt matmul (fp16 operands, fp32 accumulation, alpha = 2^-10).  With
- * hundreds of activation rows or more the product is compute-bound and this
- * path is faster than seedlm_gemm; below that seedlm_gemm is.  The weights are
+ * several hundred activation rows or more (from between 256 and 512 on a
+ * 4-bit Llama-3-70B layer) the product is compute-bound and this path is
+ * faster than seedlm_gemm; below that seedlm_gemm is.  The weights are
  * still rebuilt from the records (paperhub.cn rebuttal text before Eq. (1));
  * the copy lives only in the caller's workspace, for the duration of the call.
  *   X, Y       as for seedlm_gemm (fp16, cols a multiple of 8, X 16-byte aligned)

@@ -50,6 +50,7 @@ EXPORTED = (
     "seedlm_fp16_gemv",
     "seedlm_stream_read",
     "seedlm_gemm",
+    "seedlm_gemm_scratch_bytes",
     "seedlm_gemm_decoded",
     "seedlm_gemm_decoded_bytes",
     "seedlm_encoder_create",
@@ -112,6 +113,7 @@ def lib() -> ctypes.CDLL:
     L.seedlm_fp16_gemv.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     L.seedlm_stream_read.argtypes = [vp, i64, vp, vp]
     L.seedlm_gemm.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+    L.seedlm_gemm_scratch_bytes.argtypes = [vp, i64, ctypes.POINTER(sz)]
     L.seedlm_gemm_decoded.argtypes = [vp, vp, vp, i64, i32, i32, vp, ctypes.c_size_t, vp]
     L.seedlm_gemm_decoded_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     L.seedlm_encoder_create.argtypes = [i32, i32, i32, i32, ctypes.POINTER(vp)]
@@ -321,7 +323,7 @@ def seedlm_gemv_scratch_bytes(mats, batch=1, x_dtype=F16, y_dtype=F16) -> int:
 
 
 def seedlm_scratch_release():
-    """Free the library's per-stream gemv scratch (synchronises the devices)."""
+    """Free the library's per-stream gemv and gemm scratch (synchronises the devices)."""
     _check(lib().seedlm_scratch_release(), "seedlm_scratch_release")
 
 
@@ -348,6 +350,14 @@ def seedlm_gemm(m: SeedLMMatrix, X, Y, stream=None):
                              X.shape[0], _dtype_code(X), _dtype_code(Y), _stream_ptr(stream)),
            "seedlm_gemm")
     return Y
+
+
+def seedlm_gemm_scratch_bytes(m: SeedLMMatrix, ntok: int) -> int:
+    """Scratch bytes a seedlm_gemm call on m with ntok activation rows uses on its stream."""
+    n = ctypes.c_size_t(0)
+    _check(lib().seedlm_gemm_scratch_bytes(m.handle, ntok, ctypes.byref(n)),
+           "seedlm_gemm_scratch_bytes")
+    return n.value
 
 
 def seedlm_gemm_decoded_bytes(m: SeedLMMatrix) -> int:

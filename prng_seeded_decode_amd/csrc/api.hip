@@ -476,7 +476,22 @@ int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok, int x_dty
                 void* stream) {
   if (!h || !X || !Y || ntok < 1) return SEEDLM_E_INVALID;
   if (!on_handle_device(h)) return SEEDLM_E_INVALID;
-  return launch_gemm(h, X, Y, ntok, x_dtype, y_dtype, static_cast<hipStream_t>(stream));
+  int st = check_gemm(h, X, ntok, x_dtype, y_dtype);
+  if (st != SEEDLM_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* part = nullptr;
+  const size_t bytes = gemm_scratch_bytes(h, ntok);
+  if (bytes > 0) {
+    st = stream_scratch(h->device, s, bytes, &part);
+    if (st != SEEDLM_OK) return st;
+  }
+  return launch_gemm(h, X, Y, ntok, static_cast<float*>(part), s);
+}
+
+int seedlm_gemm_scratch_bytes(seedlm_handle h, int64_t ntok, size_t* bytes) {
+  if (!h || !bytes || ntok < 1) return SEEDLM_E_INVALID;
+  *bytes = (h->is_4bit() || h->is_3bit()) ? gemm_scratch_bytes(h, ntok) : 0;
+  return SEEDLM_OK;
 }
 
 int seedlm_gemm_decoded_bytes(seedlm_handle h, size_t* bytes) {

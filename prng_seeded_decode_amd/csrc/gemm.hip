@@ -11,16 +11,24 @@
 //
 // Tiles (one workgroup = 256 threads = 4 waves):
 //   rows    r0 .. r0+127 of W (output features), tokens t0 .. t0+T-1 of X,
-//           T = 512 (or 256 when 512-token tiles would leave over half the CUs
-//           idle);
+//           T = 512 (256 for inputs of at most 256 tokens);
 //   K step  32 columns = 4 blocks = one 16-byte group of a packed row;
-//   waves   2 x 2: wave (wr, wt) owns rows r0 + 64 wr .. +63 and tokens
-//           t0 + (T/2) wt .. +T/2-1, i.e. 2 x T/64 MFMA tiles of 32 x 32 (up to
-//           256 fp32 accumulators per lane), up to 32 MFMAs per K step.
+//   waves   1 x 4: wave w owns all 128 rows and tokens t0 + (T/4) w .. +T/4-1,
+//           i.e. 4 x T/128 MFMA tiles of 32 x 32 (up to 256 fp32 accumulators
+//           per lane), up to 32 MFMAs per K step.  (Against 2 x 2 waves of
+//           64 rows x T/2 tokens this reads 16 instead of 20 KiB of operands
+//           per wave and step from LDS.)
 // Per K step each thread loads one 16-byte group (4 blocks) of one row into
 // registers and copies 8 x 16 bytes of X straight into LDS, two steps ahead;
 // the decode of step k+1 and the MFMAs of step k use different LDS buffers, so
 // the matrix cores run while the VALU decodes.
+//
+// Work units: a call is cut into whole tiles and, where the tiles would not
+// fill the last round of workgroups on the GPU (or a small matrix would not
+// fill one), tiles whose K steps are split over several workgroups.  The whole
+// tiles run in one launch, the split units in a second, which writes fp32
+// partial tiles into scratch, and gemm_c8_fixup_kernel adds each tile's
+// partials in a fixed order (deterministic) and writes it.
 //
 // MFMA operand layout (v_mfma_f32_32x32x16_f16, wave64): lane l supplies the 8
 // K values 8*(l/32) .. 8*(l/32)+7 of A row l%32 and of B column l%32; the
@@ -28,6 +36,8 @@
 // register 4g + v (g, v = 0..3).  A = W rows, B = X tokens, so the result is
 // Y^T: lane l holds token l%32 and runs of four consecutive rows.
 #include <hip/hip_fp16.h>
+
+#include <algorithm>
 
 #include "lfsr_device.h"
 #include "mfma_decode.h"
@@ -46,15 +56,15 @@ constexpr int kXRow = kStepCols * 2;                // bytes per token row of an
 constexpr int kXChunks = kXRow / 16;                // 16-byte chunks per token row
 constexpr int kLdsStride = kStepCols * 2 + 16;      // bytes per W row in LDS (padded)
 constexpr int kWBytes = kTileRows * kLdsStride;     // 10 KiB
-static_assert(kXChunks == 4, "X tile layout");
+constexpr int kRG = kTileRows / 32;                 // 32-row MFMA tiles per wave
+static_assert(kXChunks == 4 && kSlices == 2, "X tile layout and operand sets");
 
-// Token tile: 512 (256 per wave, 256 accumulator registers) for long inputs,
-// 256 when 512-token tiles would leave more than half the compute units idle.
+// Token tile: 512 tokens (128 per wave), or 256 for short inputs.
 template <int TOKS>
 struct TokTile {
   static constexpr int kTileToks = TOKS;
-  static constexpr int kNTiles = TOKS / 2 / 32;     // 32-token MFMA tiles per wave
-  static constexpr int kXBytes = TOKS * kXRow;      // swizzled, no padding
+  static constexpr int kNTiles = TOKS / 4 / 32;        // 32-token MFMA tiles per wave
+  static constexpr int kXBytes = TOKS * kXRow;         // swizzled, no padding
   static constexpr int kXCopies = kXBytes / 1024 / 4;  // 1 KiB LDS copies per wave per step
 };
 
@@ -62,14 +72,19 @@ struct GemmArgs {
   const uint32_t* words;
   const __half* x;
   __half* y;
+  float* part;  // partial tiles of the split units (kTileRows x T floats each)
   int rows, cols, Mp, nb, ntok;
   uint32_t words_bytes, x_bytes;  // buffer sizes (< 2^31)
+  int row_tiles;  // tile t covers rows (t % row_tiles) * 128.., tokens (t / row_tiles) * T..
+  int full;       // units 0 .. full-1 are whole tiles 0 .. full-1
+  int splits;     // later units: tile full + v / splits, K part v % splits
+  int split_steps;  // K steps per part
 };
 
 // Chunk swizzle of the X tiles (see copy_x); depends on token bits 1..3 only.
 __device__ inline int xswz(int t) { return (((t >> 1) ^ (t >> 3)) & 1) | (((t >> 2) & 1) << 1); }
 
-template <int TOKS>
+template <int TOKS, bool kSplit>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs a) {
   constexpr int kTileToks = TokTile<TOKS>::kTileToks, kNTiles = TokTile<TOKS>::kNTiles;
   constexpr int kXBytes = TokTile<TOKS>::kXBytes, kXCopies = TokTile<TOKS>::kXCopies;
@@ -82,23 +97,36 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
   uint8_t* const wbuf[3] = {w0, w1, w2};
   uint8_t* const xbuf[3] = {x0, x1, x2};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wt = wave & 1;
-  const int r0 = blockIdx.x * kTileRows, t0 = blockIdx.y * kTileToks;
+
+  // This workgroup's unit: whole tile blockIdx.x (the K range a compile-time
+  // whole, which keeps the loop's address arithmetic as simple as before
+  // splitting existed: 4-5% faster than a runtime range), or, in a launch of
+  // the split units, K steps [kb, ke) of tile full + slot / splits.
+  const int nsteps = (a.nb + 3) / 4;
+  int tile = (int)blockIdx.x, kb = 0, ke = nsteps;
+  const int slot = (int)blockIdx.x;
+  if constexpr (kSplit) {
+    tile = a.full + slot / a.splits;
+    kb = (slot % a.splits) * a.split_steps;
+    ke = min(nsteps, kb + a.split_steps);
+  }
+  const int r0 = (tile % a.row_tiles) * kTileRows, t0 = (tile / a.row_tiles) * kTileToks;
 
   for (int e = tid; e < 512; e += kGemmThreads) {
-    const uint32_t u = (uint32_t)e & 255u;
-    if (e < 256) T0[u] = ext_bits<uint32_t>(u);
-    else T1[u] = ext_bits<uint32_t>(u << 8);
+    const uint32_t v = (uint32_t)e & 255u;
+    if (e < 256) T0[v] = ext_bits<uint32_t>(v);
+    else T1[v] = ext_bits<uint32_t>(v << 8);
   }
 
   // This thread's share of a K step: row dr = tid / 2 of the tile, whose step
   // is one 16-byte group (4 blocks) of the packed row; the two threads of a
   // row decode its words 2h and 2h+1 (h = tid & 1).  Buffer loads: an
   // out-of-range offset reads zeros, so no load is conditional and steps past
-  // the end simply load zeros.
+  // the matrix's end simply load zeros.  A split unit's steps are a whole
+  // number of rounds of three (below), so it multiplies no step past its own
+  // part; the loads it issues ahead past the part are not used.
   const int dr = tid >> 1, h = tid & 1;
   const int row = r0 + dr;
-  const int nsteps = (a.nb + 3) / 4;
   const __amdgpu_buffer_rsrc_t wrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.words, 0, (int)a.words_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t xrs =
@@ -140,8 +168,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
   // Decode word p of a step's group into a W buffer: it holds block
   // (p + row) & 3 of the step (the packed rows rotate their groups).
   auto put_w1 = [&](uint8_t* dst, uint32_t w, uint32_t ext, int p) {
-    const int slot = (p + row) & 3;
-    *reinterpret_cast<half8*>(dst + dr * kLdsStride + slot * 16) = decode_c8_ext(w, ext);
+    const int slot4 = (p + row) & 3;
+    *reinterpret_cast<half8*>(dst + dr * kLdsStride + slot4 * 16) = decode_c8_ext(w, ext);
   };
   auto mine = [&](uint4 wq, int j) -> uint32_t {  // word 2h + j of the group
     return h ? (j ? wq.w : wq.z) : (j ? wq.y : wq.x);
@@ -151,73 +179,86 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
     for (int j = 0; j < 2; ++j) put_w1(dst, mine(wq, j), ext_c8(mine(wq, j), T0, T1), 2 * h + j);
   };
 
-  f32x16 acc[2][kNTiles];
+  f32x16 acc[kRG][kNTiles];
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int g = 0; g < kRG; ++g)
 #pragma unroll
     for (int n = 0; n < kNTiles; ++n)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[g][n][v] = 0.f;
 
   const int arow = lane & 31, kq = lane >> 5, swz = xswz(arow);
-  // MFMAs of one step: operands of slice s (16 columns) read one slice ahead;
-  // after slice s's MFMAs, this thread's word s of the next step's group is
-  // decoded, and the scheduler is told to alternate one MFMA with a few VALU
-  // instructions, so that the decode issues while the matrix cores work.
+  // Operand registers of slices 0 and 1.  Set 1 carries a step's slice 1
+  // across the step's closing barrier: a step first issues the reads of its
+  // slice 0 and runs the MFMAs of the previous step's slice 1 while they are
+  // in flight, then reads its slice 1 (used after the barrier) while the MFMAs
+  // of its slice 0 run, so no MFMA waits on a read issued right before it.
+  half8 A[2][kRG], B[2][kNTiles];
+#pragma unroll
+  for (int g = 0; g < kRG; ++g) A[1][g] = half8{};
+#pragma unroll
+  for (int n = 0; n < kNTiles; ++n) B[1][n] = half8{};
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int g = 0; g < kRG; ++g)
+#pragma unroll
+      for (int n = 0; n < kNTiles; ++n)
+        acc[g][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[set][g], B[set][n], acc[g][n], 0, 0, 0);
+  };
+  // The scheduler is told to alternate one MFMA with up to six VALU
+  // instructions (the decode of one word of the next step), then the decode's
+  // store, so that the decode issues while the matrix cores work.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int m = 0; m < kRG * kNTiles; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+  };
   auto mma = [&](const uint8_t* wb, const uint8_t* xb, uint8_t* wnext, uint4 wq) {
-    uint32_t ext2[2];  // table lookups of both words, issued with slice 0's reads
+    uint32_t ext2[2];  // table lookups of both words
 #pragma unroll
     for (int j = 0; j < 2; ++j) ext2[j] = ext_c8(mine(wq, j), T0, T1);
-    const uint8_t* wl = wb + (64 * wr + arow) * kLdsStride + kq * 16;
-    const uint8_t* xl = xb + (kTileToks / 2 * wt + arow) * kXRow;
-    half8 A[2][2], B[2][kNTiles];
+    const uint8_t* wl = wb + arow * kLdsStride + kq * 16;
+    const uint8_t* xl = xb + (kTileToks / 4 * wave + arow) * kXRow;
     auto rd = [&](int s) {
       const int xo = ((2 * s + kq) ^ swz) * 16;
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
-        A[s & 1][g] = *reinterpret_cast<const half8*>(wl + g * 32 * kLdsStride + s * 32);
+      for (int g = 0; g < kRG; ++g)
+        A[s][g] = *reinterpret_cast<const half8*>(wl + g * 32 * kLdsStride + s * 32);
 #pragma unroll
       for (int n = 0; n < kNTiles; ++n)
-        B[s & 1][n] = *reinterpret_cast<const half8*>(xl + n * 32 * kXRow + xo);
+        B[s][n] = *reinterpret_cast<const half8*>(xl + n * 32 * kXRow + xo);
     };
     rd(0);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < kSlices; ++s) {
-      if (s + 1 < kSlices) rd(s + 1);
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int n = 0; n < kNTiles; ++n)
-          acc[g][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s & 1][g], B[s & 1][n], acc[g][n],
-                                                             0, 0, 0);
-      put_w1(wnext, mine(wq, s), ext2[s], 2 * h + s);
-      // LDS reads first (the next slice's operands), then MFMAs alternating
-      // with VALU, then the decode's store.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 + kNTiles, 0);
-#pragma unroll
-      for (int m = 0; m < 2 * kNTiles; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then up to six VALU
-      }
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      __builtin_amdgcn_sched_barrier(0);  // slices stay in order
-    }
+    mfmas(1);
+    put_w1(wnext, mine(wq, 0), ext2[0], 2 * h);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    rd(1);
+    mfmas(0);
+    put_w1(wnext, mine(wq, 1), ext2[1], 2 * h + 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, kRG + kNTiles, 0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Prologue: steps 0 and 1 in flight, step 0 decoded.
+  // Prologue: steps kb and kb+1 in flight, step kb decoded.
   uint4 wr3[3];
-  copy_x(0, xbuf[0]);
-  wr3[0] = load_w(0);
-  copy_x(1, xbuf[1]);
-  wr3[1] = load_w(1);
+  copy_x(kb, xbuf[0]);
+  wr3[0] = load_w(kb);
+  copy_x(kb + 1, xbuf[1]);
+  wr3[1] = load_w(kb + 1);
   __syncthreads();  // T0/T1 ready (waits for all loads too)
   put_w(wbuf[0], wr3[0]);
   __syncthreads();
 
-  // Step k (buffers k % 3): start the copies of step k + 2, run the MFMAs of
-  // step k, decode step k + 1, then wait until only step k + 2's nine loads are
-  // in flight (vmcnt counts in issue order) and meet at the barrier.
+  // Step k (buffers (k - kb) % 3): start the copies of step k + 2, run the
+  // MFMAs of step k (its slice 1 at the start of the next step), decode step
+  // k + 1, then wait until only step k + 2's nine loads are in flight (vmcnt
+  // counts in issue order) and meet at the barrier.
   auto step = [&](int k, int b) {
     const int b1 = b == 2 ? 0 : b + 1, b2 = b == 0 ? 2 : b - 1;
     copy_x(k + 2, xbuf[b2]);
@@ -227,29 +268,76 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
     __builtin_amdgcn_s_barrier();
   };
   // Whole rounds of three steps (one loop exit, so the accumulators keep their
-  // registers); the at most two steps past the end multiply zeros.
-  for (int ks = 0; ks < nsteps; ks += 3) {
+  // registers); the at most two steps past the matrix's end multiply zeros.
+  for (int ks = kb; ks < ke; ks += 3) {
     step(ks, 0);
     step(ks + 1, 1);
     step(ks + 2, 2);
   }
+  mfmas(1);  // the last step's slice 1
 
-  // Y[t][r]: lane holds token 32n + l%32 and rows 32g + 8j + 4(l/32) + v.
+  // Lane holds token 32n + l%32 of its wave's T/4 and rows 32g + 8j + 4(l/32) + v.
+  if constexpr (kSplit) {
+    // Partial tile, token-major: element (token i, row r) at i * 128 + r.
+    float* const dst = a.part + (int64_t)slot * kTileRows * kTileToks;
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < kRG; ++g)
 #pragma unroll
-    for (int n = 0; n < kNTiles; ++n) {
-      const int tok = t0 + kTileToks / 2 * wt + 32 * n + arow;
-      if (tok >= a.ntok) continue;
+      for (int n = 0; n < kNTiles; ++n) {
+        const int i = kTileToks / 4 * wave + 32 * n + arow;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rb = r0 + 64 * wr + 32 * g + 8 * j + 4 * kq;
-        __half* dst = a.y + (int64_t)tok * a.rows + rb;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (rb + v < a.rows) dst[v] = __float2half_rn(acc[g][n][4 * j + v] * 0x1p-10f);
+        for (int j = 0; j < 4; ++j) {
+          const int r = 32 * g + 8 * j + 4 * kq;
+          *reinterpret_cast<float4*>(dst + i * kTileRows + r) =
+              make_float4(acc[g][n][4 * j], acc[g][n][4 * j + 1], acc[g][n][4 * j + 2],
+                          acc[g][n][4 * j + 3]);
+        }
       }
-    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < kRG; ++g)
+#pragma unroll
+      for (int n = 0; n < kNTiles; ++n) {
+        const int tok = t0 + kTileToks / 4 * wave + 32 * n + arow;
+        if (tok >= a.ntok) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rb = r0 + 32 * g + 8 * j + 4 * kq;
+          __half* dst = a.y + (int64_t)tok * a.rows + rb;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (rb + v < a.rows) dst[v] = __float2half_rn(acc[g][n][4 * j + v] * 0x1p-10f);
+        }
+      }
+  }
+}
+
+// Y of the split tiles: tile full + q adds its `splits` partial tiles in part
+// order and writes fp16(sum * 2^-10).  A thread owns four consecutive rows of
+// one token (one 16-byte load per partial).
+template <int TOKS>
+__global__ void __launch_bounds__(256) gemm_c8_fixup_kernel(const GemmArgs a) {
+  constexpr int kPer = kTileRows * TOKS / 4 / 256;  // workgroups per tile
+  const int q = (int)blockIdx.x / kPer;
+  const int idx = ((int)blockIdx.x % kPer) * 256 + (int)threadIdx.x;
+  const int i = idx / (kTileRows / 4), r = (idx % (kTileRows / 4)) * 4;
+  const int tile = a.full + q;
+  const int tok = (tile / a.row_tiles) * TOKS + i, row = (tile % a.row_tiles) * kTileRows + r;
+  if (tok >= a.ntok) return;
+  const float* src = a.part + (int64_t)q * a.splits * kTileRows * TOKS + i * kTileRows + r;
+  float4 s = *reinterpret_cast<const float4*>(src);
+  for (int k = 1; k < a.splits; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)k * kTileRows * TOKS);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  __half* dst = a.y + (int64_t)tok * a.rows + row;
+  const float o[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    if (row + v < a.rows) dst[v] = __float2half_rn(o[v] * 0x1p-10f);
 }
 
 // The 3-bit format (C = 12, P = 4): the same scheme with a K step of 48 columns
@@ -533,17 +621,86 @@ void launch_c12(const Gemm12Args& a, hipStream_t s) {
   hipLaunchKernelGGL((gemm_c12_kernel<ROWS, TOKS>), grid, dim3(2 * ROWS), 0, s, a);
 }
 
+// How a 4-bit launch is cut into work units.  Tiles past the last whole round
+// of workgroups on the GPU (every tile, when a small matrix has fewer tiles
+// than compute units) run as `splits` units each, over consecutive ranges of
+// K steps, when they would otherwise leave at least half of the compute units
+// idle in that round: 896 tiles of the 28672 x 8192 matrix at 2048 tokens run
+// as 768 whole tiles and 256 half tiles (3.5 rounds of work instead of 4), the
+// 32 tiles of a 1024 x 8192 matrix as 256 eighths.
+constexpr int64_t kMaxSplits = 8;
+constexpr int64_t kMinSplitSteps = 8;  // K steps per part, at least
+struct C8Plan {
+  int toks;  // token tile: 512, or 256 for inputs of at most 256 tokens
+  int64_t row_tiles, tiles, full, tail, splits, split_steps;
+  int64_t units() const { return full + tail * splits; }
+  size_t part_bytes() const { return (size_t)(tail * splits) * kTileRows * toks * sizeof(float); }
+};
+C8Plan plan_c8(const seedlm_matrix* h, int64_t ntok) {
+  C8Plan p{};
+  p.toks = ntok > 256 ? 512 : 256;
+  p.row_tiles = (h->rows + kTileRows - 1) / kTileRows;
+  p.tiles = p.row_tiles * ((ntok + p.toks - 1) / p.toks);
+  const int64_t nsteps = (h->nb + 3) / 4;
+  p.full = p.tiles;
+  p.splits = 1;
+  p.split_steps = nsteps;
+  const int64_t cus = device_cu_count();
+  const int64_t rem = p.tiles % cus;
+  if (rem > 0 && 2 * rem <= cus) {
+    const int64_t sp = std::min(std::min(cus / rem, kMaxSplits), nsteps / kMinSplitSteps);
+    if (sp >= 2) {
+      // whole rounds of three steps per part (the kernel's loop unit)
+      p.split_steps = ((nsteps + sp - 1) / sp + 2) / 3 * 3;
+      p.splits = (nsteps + p.split_steps - 1) / p.split_steps;  // no empty part
+      p.tail = rem;
+      p.full = p.tiles - rem;
+    }
+  }
+  return p;
+}
+
+// Whole tiles, then the split units, then the additions of their partials.
+template <int TOKS>
+void launch_c8(const GemmArgs& a, const C8Plan& p, hipStream_t s) {
+  if (p.full > 0)
+    hipLaunchKernelGGL((gemm_c8_kernel<TOKS, false>), dim3((unsigned)p.full), dim3(kGemmThreads),
+                       0, s, a);
+  if (p.tail > 0) {
+    hipLaunchKernelGGL((gemm_c8_kernel<TOKS, true>), dim3((unsigned)(p.tail * p.splits)),
+                       dim3(kGemmThreads), 0, s, a);
+    hipLaunchKernelGGL(gemm_c8_fixup_kernel<TOKS>,
+                       dim3((unsigned)(p.tail * (kTileRows * TOKS / 4 / 256))), dim3(256), 0, s, a);
+  }
+}
+
 }  // namespace
 
-int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
-                hipStream_t s) {
+int check_gemm(const seedlm_matrix* h, const void* x, int64_t ntok, int xdt, int ydt) {
   if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
-  // token tiles go on grid.y, which holds at most 65535 workgroups
+  // token tiles of the 3-bit kernel go on grid.y, which holds at most 65535
+  // workgroups; both formats keep the same limit
   if ((ntok + 255) / 256 > 65535) return SEEDLM_E_UNSUPPORTED;
   if (!h->is_4bit() && !h->is_3bit()) return SEEDLM_E_UNSUPPORTED;
+  if (h->cols % 8 != 0 || (uintptr_t)x % 16 != 0) return SEEDLM_E_UNSUPPORTED;
   if (h->C == 12) {
-    if (h->cols % 8 != 0 || (uintptr_t)x % 16 != 0) return SEEDLM_E_UNSUPPORTED;
     if (h->bytes >= (1ULL << 31) || ntok * h->cols * 2 >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;
+    return SEEDLM_OK;
+  }
+  // 32-bit buffer offsets: the packed words and X must each stay below 2 GiB.
+  if (h->nwords * 4 >= (1LL << 31) || ntok * h->cols * 2 >= (1LL << 31))
+    return SEEDLM_E_UNSUPPORTED;
+  if (plan_c8(h, ntok).units() >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;
+  return SEEDLM_OK;
+}
+
+size_t gemm_scratch_bytes(const seedlm_matrix* h, int64_t ntok) {
+  return h->C == 8 ? plan_c8(h, ntok).part_bytes() : 0;
+}
+
+int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, float* part,
+                hipStream_t s) {
+  if (h->C == 12) {
     Gemm12Args a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
                  static_cast<__half*>(y), (int)h->rows, (int)h->cols, (int)h->Mp, (int)h->nb,
                  (int)ntok, (uint32_t)h->bytes, (uint32_t)h->exp_off, (uint32_t)(ntok * h->cols * 2)};
@@ -554,24 +711,15 @@ int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, in
     SEEDLM_HIP_CHECK(hipGetLastError());
     return SEEDLM_OK;
   }
-  if (h->C != 8) return SEEDLM_E_UNSUPPORTED;
-  if (h->cols % 8 != 0 || (uintptr_t)x % 16 != 0) return SEEDLM_E_UNSUPPORTED;
-  // 32-bit buffer offsets: the packed words and X must each stay below 2 GiB.
-  if (h->nwords * 4 >= (1LL << 31) || ntok * h->cols * 2 >= (1LL << 31))
-    return SEEDLM_E_UNSUPPORTED;
-  GemmArgs a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
-             static_cast<__half*>(y), (int)h->rows, (int)h->cols, (int)h->Mp, (int)h->nb,
-             (int)ntok, (uint32_t)(h->nwords * 4), (uint32_t)(ntok * h->cols * 2)};
-  const int64_t row_tiles = (h->rows + kTileRows - 1) / kTileRows;
-  // 512-token tiles once they fill at least half of the compute units (each
-  // does twice the MFMA work per decoded weight); 256-token tiles below that.
-  if (2 * row_tiles * ((ntok + 511) / 512) >= device_cu_count()) {
-    const dim3 grid((unsigned)row_tiles, (unsigned)((ntok + 511) / 512));
-    hipLaunchKernelGGL(gemm_c8_kernel<512>, grid, dim3(kGemmThreads), 0, s, a);
-  } else {
-    const dim3 grid((unsigned)row_tiles, (unsigned)((ntok + 255) / 256));
-    hipLaunchKernelGGL(gemm_c8_kernel<256>, grid, dim3(kGemmThreads), 0, s, a);
-  }
+  const C8Plan p = plan_c8(h, ntok);
+  if (p.part_bytes() > 0 && !part) return SEEDLM_E_INVALID;
+  const GemmArgs a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
+                   static_cast<__half*>(y), part, (int)h->rows, (int)h->cols, (int)h->Mp,
+                   (int)h->nb, (int)ntok, (uint32_t)(h->nwords * 4),
+                   (uint32_t)(ntok * h->cols * 2), (int)p.row_tiles, (int)p.full,
+                   (int)p.splits, (int)p.split_steps};
+  if (p.toks == 512) launch_c8<512>(a, p, s);
+  else launch_c8<256>(a, p, s);
   SEEDLM_HIP_CHECK(hipGetLastError());
   return SEEDLM_OK;
 }

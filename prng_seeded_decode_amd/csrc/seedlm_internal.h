@@ -133,8 +133,13 @@ int launch_gemv_direct_group(const seedlm_matrix* const* hs, const void* const* 
 int launch_gemv_mfma_group(const seedlm_matrix* const* hs, const void* const* xs,
                            void* const* ys, float* const* partials, int n, int batch, int xdt,
                            int ydt, hipStream_t s, int phases);
-// Prefill GEMM (both packed formats, fp16 X and Y; E_UNSUPPORTED otherwise).
-int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, int xdt, int ydt,
+// Prefill GEMM (both packed formats, fp16 X and Y): check_gemm gives
+// E_UNSUPPORTED for what the kernels do not take, gemm_scratch_bytes the
+// partial tiles a call writes (0 when it splits no tile), and launch_gemm runs
+// a checked call with that much scratch at `part`.
+int check_gemm(const seedlm_matrix* h, const void* x, int64_t ntok, int xdt, int ydt);
+size_t gemm_scratch_bytes(const seedlm_matrix* h, int64_t ntok);
+int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, float* part,
                 hipStream_t s);
 int launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 // Prefill through a decoded fp16 copy of W in a caller workspace and hipBLASLt.

@@ -224,6 +224,8 @@ int run_abi() {
   expect("export null handle", seedlm_export(nullptr, nullptr, &sb), SEEDLM_E_INVALID);
   expect("gemm null handle", seedlm_gemm(nullptr, xbuf, ybuf, 4, SEEDLM_F16, SEEDLM_F16, nullptr),
          SEEDLM_E_INVALID);
+  expect("gemm_scratch_bytes null handle", seedlm_gemm_scratch_bytes(nullptr, 4, &sb),
+         SEEDLM_E_INVALID);
   expect("gemm_decoded_bytes null handle", seedlm_gemm_decoded_bytes(nullptr, &sb),
          SEEDLM_E_INVALID);
   expect("gemm_decoded null handle",

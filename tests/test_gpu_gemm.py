@@ -6,8 +6,10 @@ same fp16 values.  Every token row of Y is a GEMV with fp16 output, so the bar
 is that of the fp16-output GEMV: normwise max|y - y_ref| / max|y_ref| <= 2e-3
 per token row.  Small shapes are checked on every output (ragged row, panel,
 block-group and token tails included, for both token tilings: 256 tokens per
-workgroup on small grids, 512 on large ones); the full 8192x8192, 2048-token
-shape on sampled rows and tokens, which the oracle computes one by one.
+workgroup for short inputs, 512 otherwise); the full 8192x8192, 2048-token
+shape on sampled rows and tokens, which the oracle computes one by one.  Small
+grids of the 4-bit kernel split tiles along K (partials added by a second
+launch); one launch with both whole and split tiles is checked on samples too.
 """
 import ctypes
 
@@ -86,6 +88,47 @@ def test_gemm_full_shape_sampled():
     err = _rowwise_err(Yg[np.ix_(ts, rs)], Yr)
     _say(f"  sampled max per-token normwise error {err:.2e}")
     assert err <= TOL
+
+
+def test_gemm_whole_and_split_tiles_sampled():
+    """320 tiles of 128 rows x 512 tokens: on 256 compute units the last 64 (the
+    second token tile's rows 12288..20479) run as four K parts each, whose fp32
+    partials the fixup launch adds; the other 256 run whole."""
+    S = _S()
+    rows, cols, ntok = 20480, 1024, 1024
+    _say(f"gemm sampled {rows}x{cols} ntok={ntok} (whole and split tiles)")
+    (s, c, e), X, Yg, m, *_ = _run(67, rows, cols, ntok)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus == 256:  # 64 tiles x 4 parts x 128 x 512 fp32 partials
+        assert S.seedlm_gemm_scratch_bytes(m, ntok) == 64 * 4 * 128 * 512 * 4
+    rng = np.random.default_rng(7)
+    rs = np.concatenate([[0, rows - 1, 12287, 12288], rng.choice(rows, 40, replace=False)])
+    ts = np.concatenate([[0, 511, 512, ntok - 1], rng.choice(ntok, 12, replace=False)])
+    W = O.decode_rows(s[rs], c[rs], e[rs], cols, 8, 3)
+    Yr = X[ts].astype(np.float64) @ W.T
+    err = _rowwise_err(Yg[np.ix_(ts, rs)], Yr)
+    _say(f"  sampled max per-token normwise error {err:.2e}")
+    assert err <= TOL
+
+
+def test_gemm_scratch_bytes():
+    """A matrix with too few K steps to split and the 3-bit format need no scratch;
+    a small grid's tiles split (on 256 compute units)."""
+    S = _S()
+    _dev()
+    s, c, e = gen_records(68, 0, 256, 64, 8, 3)
+    m0 = S.seedlm_pack(s, c, e, 256, 64, 8, 3, 16)
+    assert S.seedlm_gemm_scratch_bytes(m0, 600) == 0  # 2 K steps
+    s, c, e = gen_records(68, 1, 256, 1024, 8, 3)
+    m = S.seedlm_pack(s, c, e, 256, 1024, 8, 3, 16)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        # 2 x 2 tiles of 512 tokens, 32 K steps -> 4 parts (9, 9, 9 and 5 steps)
+        assert S.seedlm_gemm_scratch_bytes(m, 600) == 4 * 4 * 128 * 512 * 4
+        # one token: 2 tiles of 256 tokens, 4 parts
+        assert S.seedlm_gemm_scratch_bytes(m, 1) == 2 * 4 * 128 * 256 * 4
+    s3, c3, e3 = gen_records(68, 2, 256, 1200, 12, 4)
+    m3 = S.seedlm_pack(s3, c3, e3, 256, 1200, 12, 4, 16)
+    assert S.seedlm_gemm_scratch_bytes(m3, 600) == 0
 
 
 # 3-bit format (C = 12, P = 4): K steps of 48 columns (4 blocks) and 256-token
@@ -308,3 +351,33 @@ def test_gemm_decoded_full_shape_sampled_and_rejects():
         S.seedlm_gemm_decoded(m, Xd, Y, ws[: rows * cols - 1])
     with pytest.raises(S.SeedLMError):
         S.seedlm_gemm_decoded(m, Xd.float(), Y, ws)
+
+
+@pytest.mark.parametrize("ntok", [512, 1024])
+def test_gemm_decoded_long_k_shape(ntok):
+    """Llama-3-70B down projection (8192x28672, 4-bit): at 512 and 1024 tokens
+    hipBLASLt's first heuristic candidate wants more scratch than the workspace
+    offers, and the plan must fall back to one that fits.  Sampled against the
+    oracle, and equal to the fused kernel within the bar."""
+    dev = _dev()
+    S = _S()
+    rows, cols = 8192, 28672
+    s, c, e = gen_records(4, 6, rows, cols, 8, 3)
+    m = S.seedlm_pack(s, c, e, rows, cols, 8, 3, 16)
+    X = gen_x(4, 6, ntok, cols, "f16")
+    Xd = torch.from_numpy(X).to(dev)
+    ws = torch.empty((S.seedlm_gemm_decoded_bytes(m) // 2,), dtype=torch.float16, device=dev)
+    Y = torch.empty((ntok, rows), dtype=torch.float16, device=dev)
+    _say(f"gemm decoded sampled {rows}x{cols} ntok={ntok}")
+    S.seedlm_gemm_decoded(m, Xd, Y, ws)
+    Yf = torch.empty_like(Y)
+    S.seedlm_gemm(m, Xd, Yf)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(ntok)
+    rs = np.concatenate([[0, rows - 1], rng.choice(rows, 24, replace=False)])
+    ts = np.concatenate([[0, ntok - 1], rng.choice(ntok, 10, replace=False)])
+    W = O.decode_rows(s[rs], c[rs], e[rs], cols, 8, 3)
+    Yr = X[ts].astype(np.float64) @ W.T
+    Yg = Y.cpu().numpy().astype(np.float64)
+    assert _rowwise_err(Yg[np.ix_(ts, rs)], Yr) <= TOL
+    assert _rowwise_err(Yg, Yf.cpu().numpy().astype(np.float64)) <= TOL
