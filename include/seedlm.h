@@ -263,12 +263,12 @@ SEEDLM_API const char* seedlm_status_string(int status);
  * (paperhub.cn rebuttal text before Eq. (1): weights are reconstructed on the
  * fly from s and t and used to compute the activations).  Each 128-row tile of
  * W is decoded exactly once per 256 or 512 activation rows and contracted on
- * the matrix cores (fp16 operands, fp32 accumulation).  Where the 4-bit
- * format's 128 x 512 tiles would leave over half of the compute units idle in
- * the last round of workgroups (or a small matrix has too few tiles to fill
- * them), those tiles split their K range over up to 8 workgroups, which write
- * fp32 partial tiles that a second launch adds in a fixed order: results are
- * deterministic for a given shape and device.
+ * the matrix cores (fp16 operands, fp32 accumulation).  Where the tiles would
+ * leave over half of the compute units idle in the last round of workgroups
+ * (or a small matrix has too few tiles to fill them), those tiles split their K
+ * range over up to 8 workgroups, which write fp32 partial tiles that another
+ * launch adds in a fixed order: results are deterministic for a given shape
+ * and device.
  *   X  device fp16 [ntok][cols], 16-byte aligned (row-major)
  *   Y  device fp16 [ntok][rows] (round to nearest even); both caller-owned
  *   ntok >= 1.  Both packed formats (C = 8 and C = 12) with cols a multiple of
@@ -290,8 +290,8 @@ SEEDLM_API int seedlm_gemm(seedlm_handle h, const void* X, void* Y, int64_t ntok
 
 /*
  * seedlm_gemm_scratch_bytes -- the scratch bytes seedlm_gemm(h, ., ., ntok, ...)
- * uses on the current device (0 when it splits no tile, and for the 3-bit
- * format, whose kernel does not split).  *bytes is set on success.
+ * uses on the current device (0 when it splits no tile).  *bytes is set on
+ * success.
  * Errors: SEEDLM_E_INVALID (null, ntok < 1).
  */
 SEEDLM_API int seedlm_gemm_scratch_bytes(seedlm_handle h, int64_t ntok, size_t* bytes);

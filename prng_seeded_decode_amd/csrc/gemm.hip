@@ -27,8 +27,9 @@
 // fill the last round of workgroups on the GPU (or a small matrix would not
 // fill one), tiles whose K steps are split over several workgroups.  The whole
 // tiles run in one launch, the split units in a second, which writes fp32
-// partial tiles into scratch, and gemm_c8_fixup_kernel adds each tile's
-// partials in a fixed order (deterministic) and writes it.
+// partial tiles into scratch, and gemm_fixup_kernel adds each tile's
+// partials in a fixed order (deterministic) and writes it.  The 3-bit kernel
+// is split the same way.
 //
 // MFMA operand layout (v_mfma_f32_32x32x16_f16, wave64): lane l supplies the 8
 // K values 8*(l/32) .. 8*(l/32)+7 of A row l%32 and of B column l%32; the
@@ -312,22 +313,29 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
   }
 }
 
-// Y of the split tiles: tile full + q adds its `splits` partial tiles in part
-// order and writes fp16(sum * 2^-10).  A thread owns four consecutive rows of
-// one token (one 16-byte load per partial).
-template <int TOKS>
-__global__ void __launch_bounds__(256) gemm_c8_fixup_kernel(const GemmArgs a) {
-  constexpr int kPer = kTileRows * TOKS / 4 / 256;  // workgroups per tile
+// Y of the split tiles (either format): tile full + q adds its `splits`
+// partial tiles (ROWS x TOKS floats, token-major) in part order and writes
+// fp16(sum * 2^-10).  A thread owns four consecutive rows of one token (one
+// 16-byte load per partial).
+struct FixupArgs {
+  const float* part;
+  __half* y;
+  int rows, ntok, row_tiles, full, splits;
+};
+
+template <int ROWS, int TOKS>
+__global__ void __launch_bounds__(256) gemm_fixup_kernel(const FixupArgs a) {
+  constexpr int kPer = ROWS * TOKS / 4 / 256;  // workgroups per tile
   const int q = (int)blockIdx.x / kPer;
   const int idx = ((int)blockIdx.x % kPer) * 256 + (int)threadIdx.x;
-  const int i = idx / (kTileRows / 4), r = (idx % (kTileRows / 4)) * 4;
+  const int i = idx / (ROWS / 4), r = (idx % (ROWS / 4)) * 4;
   const int tile = a.full + q;
-  const int tok = (tile / a.row_tiles) * TOKS + i, row = (tile % a.row_tiles) * kTileRows + r;
+  const int tok = (tile / a.row_tiles) * TOKS + i, row = (tile % a.row_tiles) * ROWS + r;
   if (tok >= a.ntok) return;
-  const float* src = a.part + (int64_t)q * a.splits * kTileRows * TOKS + i * kTileRows + r;
+  const float* src = a.part + (int64_t)q * a.splits * ROWS * TOKS + i * ROWS + r;
   float4 s = *reinterpret_cast<const float4*>(src);
   for (int k = 1; k < a.splits; ++k) {
-    const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)k * kTileRows * TOKS);
+    const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)k * ROWS * TOKS);
     s.x += v.x;
     s.y += v.y;
     s.z += v.z;
@@ -354,7 +362,9 @@ __global__ void __launch_bounds__(256) gemm_c8_fixup_kernel(const GemmArgs a) {
 // for the same MFMA work when ROWS TOKS is fixed: copying X is the scarcer of
 // the two here, so large grids take 256 x 256 tiles (eight waves, two per
 // SIMD) and smaller grids 128 x 256 (four waves), which leaves more
-// workgroups.
+// workgroups.  Tiles past the last full round split their K steps as in the
+// 4-bit kernel (the 1024-row k and v projections of a Llama-3-8B layer: 64
+// tiles of 128 x 256 at 2048 tokens, run as 256 quarters).
 //
 // Pipeline over three buffers of each kind: in step k the word loads and the
 // X copy of step k+2 are issued, the MFMAs of step k run, and the decode of
@@ -384,11 +394,13 @@ struct Gemm12Args {
   const uint32_t* words;
   const __half* x;
   __half* y;
+  float* part;  // partial tiles of the split units (ROWS x TOKS floats each)
   int rows, cols, Mp, nb, ntok;
   uint32_t buf_bytes, exp_off, x_bytes;  // packed buffer size, exponent array offset, X size
+  int row_tiles, full, splits, split_steps;  // work units, as for the 4-bit kernel
 };
 
-template <int ROWS, int TOKS>
+template <int ROWS, int TOKS, bool kSplit>
 __global__ void __launch_bounds__(2 * ROWS, 1) gemm_c12_kernel(const Gemm12Args a) {
   using TL = Tile12<ROWS, TOKS>;
   constexpr int kNTiles = TL::kNTiles, kXBytes = TL::kXBytes, kWBytes = TL::kWBytes;
@@ -400,7 +412,17 @@ __global__ void __launch_bounds__(2 * ROWS, 1) gemm_c12_kernel(const Gemm12Args 
   uint8_t* const xbuf[3] = {x0, x1, x2};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wt = wave & 1;
-  const int r0 = blockIdx.x * ROWS, t0 = blockIdx.y * TOKS;
+  // This workgroup's unit: whole tile blockIdx.x, or (split launch) K steps
+  // [kb, ke) of tile full + slot / splits, as in the 4-bit kernel.
+  const int nsteps = (a.nb + 3) / 4;
+  int tile = (int)blockIdx.x, kb = 0, ke = nsteps;
+  const int slot = (int)blockIdx.x;
+  if constexpr (kSplit) {
+    tile = a.full + slot / a.splits;
+    kb = (slot % a.splits) * a.split_steps;
+    ke = min(nsteps, kb + a.split_steps);
+  }
+  const int r0 = (tile % a.row_tiles) * ROWS, t0 = (tile / a.row_tiles) * TOKS;
 
   for (int e = tid; e < 512; e += kThreads) {
     const uint32_t u = (uint32_t)e & 255u;
@@ -413,7 +435,6 @@ __global__ void __launch_bounds__(2 * ROWS, 1) gemm_c12_kernel(const Gemm12Args 
   // decode to t = 0).
   const int dr = tid >> 1, h = tid & 1;
   const int row = r0 + dr;
-  const int nsteps = (a.nb + 3) / 4;
   const __amdgpu_buffer_rsrc_t wrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.words, 0, (int)a.buf_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t xrs =
@@ -553,12 +574,12 @@ __global__ void __launch_bounds__(2 * ROWS, 1) gemm_c12_kernel(const Gemm12Args 
     }
   };
 
-  // Prologue: the words and X of steps 0 and 1 in flight; step 0 decoded.
+  // Prologue: the words and X of steps kb and kb+1 in flight; step kb decoded.
   Group gq[3];
-  gq[0] = load_w(0);
-  gq[1] = load_w(1);
-  copy_x(0, xbuf[0]);
-  copy_x(1, xbuf[1]);
+  gq[0] = load_w(kb);
+  gq[1] = load_w(kb + 1);
+  copy_x(kb, xbuf[0]);
+  copy_x(kb + 1, xbuf[1]);
   __syncthreads();  // T0/T1 ready (waits for all loads too)
   {
     const Dec12 d0 = setup(gq[0], 0);
@@ -589,60 +610,71 @@ __global__ void __launch_bounds__(2 * ROWS, 1) gemm_c12_kernel(const Gemm12Args 
     __builtin_amdgcn_s_waitcnt(0x0070 | (kXCopies + 2));  // vmcnt(kXCopies + 2) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
   };
-  // Whole rounds of three steps (one loop exit); steps past the end multiply
-  // zeros.
-  for (int ks = 0; ks < nsteps; ks += 3) {
+  // Whole rounds of three steps (one loop exit); steps past the matrix's end
+  // multiply zeros, and a split unit's steps are whole rounds of its part.
+  for (int ks = kb; ks < ke; ks += 3) {
     step(ks, 0);
     step(ks + 1, 1);
     step(ks + 2, 2);
   }
 
-  // Y[t][r]: lane holds token 32n + l%32 and rows 32g + 8j + 4(l/32) + v.
+  // Lane holds token 32n + l%32 of its wave's half and rows 32g + 8j + 4(l/32) + v
+  // of its wave's 64.
+  if constexpr (kSplit) {
+    // Partial tile, token-major: element (token i, row r) at i * ROWS + r.
+    float* const dst = a.part + (int64_t)slot * ROWS * TOKS;
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int n = 0; n < kNTiles; ++n) {
-      const int tok = t0 + TOKS / 2 * wt + 32 * n + arow;
-      if (tok >= a.ntok) continue;
+      for (int n = 0; n < kNTiles; ++n) {
+        const int i = TOKS / 2 * wt + 32 * n + arow;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rb = r0 + 64 * wr + 32 * g + 8 * j + 4 * kq;
-        __half* dst = a.y + (int64_t)tok * a.rows + rb;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (rb + v < a.rows) dst[v] = __float2half_rn(acc[g][n][4 * j + v] * 0x1p-10f);
+        for (int j = 0; j < 4; ++j) {
+          const int r = 64 * wr + 32 * g + 8 * j + 4 * kq;
+          *reinterpret_cast<float4*>(dst + i * ROWS + r) =
+              make_float4(acc[g][n][4 * j], acc[g][n][4 * j + 1], acc[g][n][4 * j + 2],
+                          acc[g][n][4 * j + 3]);
+        }
       }
-    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int n = 0; n < kNTiles; ++n) {
+        const int tok = t0 + TOKS / 2 * wt + 32 * n + arow;
+        if (tok >= a.ntok) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rb = r0 + 64 * wr + 32 * g + 8 * j + 4 * kq;
+          __half* dst = a.y + (int64_t)tok * a.rows + rb;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (rb + v < a.rows) dst[v] = __float2half_rn(acc[g][n][4 * j + v] * 0x1p-10f);
+        }
+      }
+  }
 }
 
-template <int ROWS, int TOKS>
-void launch_c12(const Gemm12Args& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.rows + ROWS - 1) / ROWS), (unsigned)((a.ntok + TOKS - 1) / TOKS));
-  hipLaunchKernelGGL((gemm_c12_kernel<ROWS, TOKS>), grid, dim3(2 * ROWS), 0, s, a);
-}
-
-// How a 4-bit launch is cut into work units.  Tiles past the last whole round
-// of workgroups on the GPU (every tile, when a small matrix has fewer tiles
-// than compute units) run as `splits` units each, over consecutive ranges of
-// K steps, when they would otherwise leave at least half of the compute units
-// idle in that round: 896 tiles of the 28672 x 8192 matrix at 2048 tokens run
-// as 768 whole tiles and 256 half tiles (3.5 rounds of work instead of 4), the
-// 32 tiles of a 1024 x 8192 matrix as 256 eighths.
+// How a launch is cut into work units.  Tiles past the last whole round of
+// workgroups on the GPU (every tile, when a small matrix has fewer tiles than
+// compute units) run as `splits` units each, over consecutive ranges of K
+// steps, when they would otherwise leave at least half of the compute units
+// idle in that round: 896 tiles of the 4-bit 28672 x 8192 matrix at 2048
+// tokens run as 768 whole tiles and 256 half tiles (3.5 rounds of work instead
+// of 4), the 32 tiles of a 1024 x 8192 matrix as 256 eighths.
 constexpr int64_t kMaxSplits = 8;
 constexpr int64_t kMinSplitSteps = 8;  // K steps per part, at least
-struct C8Plan {
-  int toks;  // token tile: 512, or 256 for inputs of at most 256 tokens
+struct Plan {
+  int rows_tile, toks;  // tile: 128 x 512 or 128 x 256 (4-bit), 256 or 128 x 256 (3-bit)
   int64_t row_tiles, tiles, full, tail, splits, split_steps;
   int64_t units() const { return full + tail * splits; }
-  size_t part_bytes() const { return (size_t)(tail * splits) * kTileRows * toks * sizeof(float); }
+  size_t part_bytes() const {
+    return (size_t)(tail * splits) * rows_tile * toks * sizeof(float);
+  }
 };
-C8Plan plan_c8(const seedlm_matrix* h, int64_t ntok) {
-  C8Plan p{};
-  p.toks = ntok > 256 ? 512 : 256;
-  p.row_tiles = (h->rows + kTileRows - 1) / kTileRows;
-  p.tiles = p.row_tiles * ((ntok + p.toks - 1) / p.toks);
-  const int64_t nsteps = (h->nb + 3) / 4;
+void split_tail(Plan& p, int64_t nsteps) {
   p.full = p.tiles;
+  p.tail = 0;
   p.splits = 1;
   p.split_steps = nsteps;
   const int64_t cus = device_cu_count();
@@ -650,27 +682,59 @@ C8Plan plan_c8(const seedlm_matrix* h, int64_t ntok) {
   if (rem > 0 && 2 * rem <= cus) {
     const int64_t sp = std::min(std::min(cus / rem, kMaxSplits), nsteps / kMinSplitSteps);
     if (sp >= 2) {
-      // whole rounds of three steps per part (the kernel's loop unit)
+      // whole rounds of three steps per part (the kernels' loop unit)
       p.split_steps = ((nsteps + sp - 1) / sp + 2) / 3 * 3;
       p.splits = (nsteps + p.split_steps - 1) / p.split_steps;  // no empty part
       p.tail = rem;
       p.full = p.tiles - rem;
     }
   }
+}
+Plan plan_for(const seedlm_matrix* h, int64_t ntok) {
+  Plan p{};
+  if (h->C == 8) {
+    p.rows_tile = kTileRows;
+    p.toks = ntok > 256 ? 512 : 256;
+  } else {
+    // 256 x 256 tiles where they give every compute unit a workgroup
+    p.toks = 256;
+    p.rows_tile = ((h->rows + 255) / 256) * ((ntok + 255) / 256) >= device_cu_count() ? 256 : 128;
+  }
+  p.row_tiles = (h->rows + p.rows_tile - 1) / p.rows_tile;
+  p.tiles = p.row_tiles * ((ntok + p.toks - 1) / p.toks);
+  split_tail(p, (h->nb + 3) / 4);
   return p;
+}
+
+FixupArgs fixup_args(const Plan& p, const float* part, void* y, const seedlm_matrix* h,
+                     int64_t ntok) {
+  return FixupArgs{part, static_cast<__half*>(y), (int)h->rows, (int)ntok, (int)p.row_tiles,
+                   (int)p.full, (int)p.splits};
 }
 
 // Whole tiles, then the split units, then the additions of their partials.
 template <int TOKS>
-void launch_c8(const GemmArgs& a, const C8Plan& p, hipStream_t s) {
+void launch_c8(const GemmArgs& a, const Plan& p, const FixupArgs& f, hipStream_t s) {
   if (p.full > 0)
     hipLaunchKernelGGL((gemm_c8_kernel<TOKS, false>), dim3((unsigned)p.full), dim3(kGemmThreads),
                        0, s, a);
   if (p.tail > 0) {
     hipLaunchKernelGGL((gemm_c8_kernel<TOKS, true>), dim3((unsigned)(p.tail * p.splits)),
                        dim3(kGemmThreads), 0, s, a);
-    hipLaunchKernelGGL(gemm_c8_fixup_kernel<TOKS>,
-                       dim3((unsigned)(p.tail * (kTileRows * TOKS / 4 / 256))), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_fixup_kernel<kTileRows, TOKS>),
+                       dim3((unsigned)(p.tail * (kTileRows * TOKS / 4 / 256))), dim3(256), 0, s, f);
+  }
+}
+template <int ROWS, int TOKS>
+void launch_c12(const Gemm12Args& a, const Plan& p, const FixupArgs& f, hipStream_t s) {
+  if (p.full > 0)
+    hipLaunchKernelGGL((gemm_c12_kernel<ROWS, TOKS, false>), dim3((unsigned)p.full),
+                       dim3(2 * ROWS), 0, s, a);
+  if (p.tail > 0) {
+    hipLaunchKernelGGL((gemm_c12_kernel<ROWS, TOKS, true>), dim3((unsigned)(p.tail * p.splits)),
+                       dim3(2 * ROWS), 0, s, a);
+    hipLaunchKernelGGL((gemm_fixup_kernel<ROWS, TOKS>),
+                       dim3((unsigned)(p.tail * (ROWS * TOKS / 4 / 256))), dim3(256), 0, s, f);
   }
 }
 
@@ -678,48 +742,43 @@ void launch_c8(const GemmArgs& a, const C8Plan& p, hipStream_t s) {
 
 int check_gemm(const seedlm_matrix* h, const void* x, int64_t ntok, int xdt, int ydt) {
   if (xdt != SEEDLM_F16 || ydt != SEEDLM_F16) return SEEDLM_E_UNSUPPORTED;
-  // token tiles of the 3-bit kernel go on grid.y, which holds at most 65535
-  // workgroups; both formats keep the same limit
+  // the token limit of the earlier 2-D grids (65535 token tiles of 256), kept
   if ((ntok + 255) / 256 > 65535) return SEEDLM_E_UNSUPPORTED;
   if (!h->is_4bit() && !h->is_3bit()) return SEEDLM_E_UNSUPPORTED;
   if (h->cols % 8 != 0 || (uintptr_t)x % 16 != 0) return SEEDLM_E_UNSUPPORTED;
-  if (h->C == 12) {
-    if (h->bytes >= (1ULL << 31) || ntok * h->cols * 2 >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;
-    return SEEDLM_OK;
-  }
-  // 32-bit buffer offsets: the packed words and X must each stay below 2 GiB.
-  if (h->nwords * 4 >= (1LL << 31) || ntok * h->cols * 2 >= (1LL << 31))
-    return SEEDLM_E_UNSUPPORTED;
-  if (plan_c8(h, ntok).units() >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;
+  // 32-bit buffer offsets: the packed buffer and X must each stay below 2 GiB.
+  const int64_t packed = h->C == 12 ? (int64_t)h->bytes : h->nwords * 4;
+  if (packed >= (1LL << 31) || ntok * h->cols * 2 >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;
+  if (plan_for(h, ntok).units() >= (1LL << 31)) return SEEDLM_E_UNSUPPORTED;
   return SEEDLM_OK;
 }
 
 size_t gemm_scratch_bytes(const seedlm_matrix* h, int64_t ntok) {
-  return h->C == 8 ? plan_c8(h, ntok).part_bytes() : 0;
+  return plan_for(h, ntok).part_bytes();
 }
 
 int launch_gemm(const seedlm_matrix* h, const void* x, void* y, int64_t ntok, float* part,
                 hipStream_t s) {
-  if (h->C == 12) {
-    Gemm12Args a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
-                 static_cast<__half*>(y), (int)h->rows, (int)h->cols, (int)h->Mp, (int)h->nb,
-                 (int)ntok, (uint32_t)h->bytes, (uint32_t)h->exp_off, (uint32_t)(ntok * h->cols * 2)};
-    // 256 x 256 tiles where they give every compute unit a workgroup
-    const int64_t big = ((h->rows + 255) / 256) * ((ntok + 255) / 256);
-    if (big >= device_cu_count()) launch_c12<256, 256>(a, s);
-    else launch_c12<128, 256>(a, s);
-    SEEDLM_HIP_CHECK(hipGetLastError());
-    return SEEDLM_OK;
-  }
-  const C8Plan p = plan_c8(h, ntok);
+  const Plan p = plan_for(h, ntok);
   if (p.part_bytes() > 0 && !part) return SEEDLM_E_INVALID;
-  const GemmArgs a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
-                   static_cast<__half*>(y), part, (int)h->rows, (int)h->cols, (int)h->Mp,
-                   (int)h->nb, (int)ntok, (uint32_t)(h->nwords * 4),
-                   (uint32_t)(ntok * h->cols * 2), (int)p.row_tiles, (int)p.full,
-                   (int)p.splits, (int)p.split_steps};
-  if (p.toks == 512) launch_c8<512>(a, p, s);
-  else launch_c8<256>(a, p, s);
+  const FixupArgs f = fixup_args(p, part, y, h, ntok);
+  if (h->C == 12) {
+    const Gemm12Args a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
+                       static_cast<__half*>(y), part, (int)h->rows, (int)h->cols, (int)h->Mp,
+                       (int)h->nb, (int)ntok, (uint32_t)h->bytes, (uint32_t)h->exp_off,
+                       (uint32_t)(ntok * h->cols * 2), (int)p.row_tiles, (int)p.full,
+                       (int)p.splits, (int)p.split_steps};
+    if (p.rows_tile == 256) launch_c12<256, 256>(a, p, f, s);
+    else launch_c12<128, 256>(a, p, f, s);
+  } else {
+    const GemmArgs a{static_cast<const uint32_t*>(h->d_buf), static_cast<const __half*>(x),
+                     static_cast<__half*>(y), part, (int)h->rows, (int)h->cols, (int)h->Mp,
+                     (int)h->nb, (int)ntok, (uint32_t)(h->nwords * 4),
+                     (uint32_t)(ntok * h->cols * 2), (int)p.row_tiles, (int)p.full,
+                     (int)p.splits, (int)p.split_steps};
+    if (p.toks == 512) launch_c8<512>(a, p, f, s);
+    else launch_c8<256>(a, p, f, s);
+  }
   SEEDLM_HIP_CHECK(hipGetLastError());
   return SEEDLM_OK;
 }
