@@ -383,3 +383,58 @@ def test_gemm_decoded_long_k_shape(ntok):
     Yg = Y.cpu().numpy().astype(np.float64)
     assert _rowwise_err(Yg[np.ix_(ts, rs)], Yr) <= TOL
     assert _rowwise_err(Yg, Yf.cpu().numpy().astype(np.float64)) <= TOL
+
+
+def test_gemm_split_tiles_graph_replays_and_two_streams():
+    """Split-tile calls (three launches and the stream's scratch) captured in a HIP
+    graph and replayed with eager work between the replays, and run on two streams
+    at once: every result must equal the eager call's bits."""
+    dev = _dev()
+    S = _S()
+    shapes = [(8, 3, 1024, 2048, 600), (12, 4, 1000, 2048, 513)]
+    mats, xs, ref = [], [], []
+    for k, (C, P, rows, cols, ntok) in enumerate(shapes):
+        s, c, e = gen_records(69, k, rows, cols, C, P)
+        m = S.seedlm_pack(s, c, e, rows, cols, C, P, 16)
+        x = torch.from_numpy(gen_x(69, k, ntok, cols, "f16")).to(dev)
+        y = torch.empty((ntok, rows), dtype=torch.float16, device=dev)
+        S.seedlm_gemm(m, x, y)
+        mats.append(m)
+        xs.append(x)
+        ref.append(y)
+    torch.cuda.synchronize()
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert all(S.seedlm_gemm_scratch_bytes(m, x.shape[0]) > 0 for m, x in zip(mats, xs))
+    # graph: the capture stream gets its scratch from one eager call first
+    cs = torch.cuda.Stream()
+    ys = [torch.empty_like(y) for y in ref]
+    for m, x, y in zip(mats, xs, ys):
+        S.seedlm_gemm(m, x, y, stream=cs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        for m, x, y in zip(mats, xs, ys):
+            S.seedlm_gemm(m, x, y, stream=cs)
+    for k in range(4):
+        for y in ys:
+            y.fill_(float("nan"))
+        other = [torch.empty_like(y) for y in ref]
+        for m, x, o in zip(mats, xs, other):
+            S.seedlm_gemm(m, x, o)
+        torch.cuda.synchronize()
+        _say(f"gemm graph replay {k}")
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b, o in zip(ys, ref, other):
+            assert torch.equal(a, b) and torch.equal(o, b)
+    # two streams at once, interleaved, no synchronisation between the calls
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty_like(ref[i]) for _ in range(4)] for i in range(2)]
+    _say("gemm on two streams")
+    for k in range(4):
+        for i in range(2):
+            S.seedlm_gemm(mats[i], xs[i], outs[i][k], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for y in outs[i]:
+            assert torch.equal(y, ref[i])
