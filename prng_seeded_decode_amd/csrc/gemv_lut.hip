@@ -85,10 +85,14 @@ __device__ void build_panel_lut(Smem& sm, float xval) {
   __syncthreads();
   // Thread -> (slot, value group): kNV consecutive table rows per thread; the
   // low kLB bits of the row index come from small tables built by doubling,
-  // the high bits are fixed per thread.
-  constexpr int kNV = 256 / (kThreads / 32);
-  constexpr int kLB = kNV == 16 ? 4 : (kNV == 8 ? 3 : 2);
-  static_assert((1 << kLB) == kNV, "threads must give 4, 8 or 16 rows per thread");
+  // the high bits are fixed per thread.  Half of the workgroup builds, 16 rows
+  // per thread: the build's cost is its instructions per wave, and 8 waves of
+  // 16 rows issue about half of what 16 waves of 8 rows do (1-2% of the launch).
+  constexpr int kBuildThreads = 512;
+  constexpr int kNV = 256 / (kBuildThreads / 32);
+  constexpr int kLB = 4;
+  static_assert((1 << kLB) == kNV && kBuildThreads <= kThreads, "16 rows per thread");
+  if (tid >= kBuildThreads) return;
   const int slot = tid & 31, vg = tid >> 5;
   float xv[8];
 #pragma unroll
