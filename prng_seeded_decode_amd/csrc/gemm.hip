@@ -17,11 +17,14 @@
 //           i.e. 4 x T/128 MFMA tiles of 32 x 32 (up to 256 fp32 accumulators
 //           per lane), up to 32 MFMAs per K step.  (Against 2 x 2 waves of
 //           64 rows x T/2 tokens this reads 16 instead of 20 KiB of operands
-//           per wave and step from LDS.)
-// Per K step each thread loads one 16-byte group (4 blocks) of one row into
-// registers and copies 8 x 16 bytes of X straight into LDS, two steps ahead;
-// the decode of step k+1 and the MFMAs of step k use different LDS buffers, so
-// the matrix cores run while the VALU decodes.
+//           per wave and step.)
+// Per K step each thread loads one 16-byte group (4 blocks) of one row, two
+// steps ahead, and decodes the previous one into a W buffer in LDS, which all
+// four waves read.  X is read by one wave only, so it does not pass through
+// LDS: each lane loads its own B operands (16 bytes per 32-token tile and
+// slice) straight into registers, one step ahead, in two register sets.  The
+// decode of step k+1 and the MFMAs of step k use different W buffers, so the
+// matrix cores run while the VALU decodes.
 //
 // Work units: a call is cut into whole tiles and, where the tiles would not
 // fill the last round of workgroups on the GPU (or a small matrix would not
@@ -53,20 +56,16 @@ constexpr int kGemmThreads = 256;
 constexpr int kTileRows = 128;
 constexpr int kStepCols = 32;                       // 4 blocks of 8 columns, one 16-byte group
 constexpr int kSlices = kStepCols / 16;             // MFMAs of K = 16 per step
-constexpr int kXRow = kStepCols * 2;                // bytes per token row of an X tile
-constexpr int kXChunks = kXRow / 16;                // 16-byte chunks per token row
 constexpr int kLdsStride = kStepCols * 2 + 16;      // bytes per W row in LDS (padded)
 constexpr int kWBytes = kTileRows * kLdsStride;     // 10 KiB
 constexpr int kRG = kTileRows / 32;                 // 32-row MFMA tiles per wave
-static_assert(kXChunks == 4 && kSlices == 2, "X tile layout and operand sets");
+static_assert(kSlices == 2, "operand sets");
 
 // Token tile: 512 tokens (128 per wave), or 256 for short inputs.
 template <int TOKS>
 struct TokTile {
   static constexpr int kTileToks = TOKS;
-  static constexpr int kNTiles = TOKS / 4 / 32;        // 32-token MFMA tiles per wave
-  static constexpr int kXBytes = TOKS * kXRow;         // swizzled, no padding
-  static constexpr int kXCopies = kXBytes / 1024 / 4;  // 1 KiB LDS copies per wave per step
+  static constexpr int kNTiles = TOKS / 4 / 32;  // 32-token MFMA tiles per wave
 };
 
 struct GemmArgs {
@@ -82,21 +81,14 @@ struct GemmArgs {
   int split_steps;  // K steps per part
 };
 
-// Chunk swizzle of the X tiles (see copy_x); depends on token bits 1..3 only.
-__device__ inline int xswz(int t) { return (((t >> 1) ^ (t >> 3)) & 1) | (((t >> 2) & 1) << 1); }
-
 template <int TOKS, bool kSplit>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs a) {
   constexpr int kTileToks = TokTile<TOKS>::kTileToks, kNTiles = TokTile<TOKS>::kNTiles;
-  constexpr int kXBytes = TokTile<TOKS>::kXBytes, kXCopies = TokTile<TOKS>::kXCopies;
-  // Three buffers of each kind, as separate objects indexed at compile time, so
-  // that the compiler can tell that reads of one never wait for copies into
-  // another.
   __shared__ uint32_t T0[256], T1[256];
+  // Three W buffers, as separate objects indexed at compile time, so that the
+  // compiler can tell that reads of one never wait for writes into another.
   __shared__ __attribute__((aligned(16))) uint8_t w0[kWBytes], w1[kWBytes], w2[kWBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t x0[kXBytes], x1[kXBytes], x2[kXBytes];
   uint8_t* const wbuf[3] = {w0, w1, w2};
-  uint8_t* const xbuf[3] = {x0, x1, x2};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // This workgroup's unit: whole tile blockIdx.x (the K range a compile-time
@@ -123,9 +115,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
   // is one 16-byte group (4 blocks) of the packed row; the two threads of a
   // row decode its words 2h and 2h+1 (h = tid & 1).  Buffer loads: an
   // out-of-range offset reads zeros, so no load is conditional and steps past
-  // the matrix's end simply load zeros.  A split unit's steps are a whole
-  // number of rounds of three (below), so it multiplies no step past its own
-  // part; the loads it issues ahead past the part are not used.
+  // the matrix's end simply load zeros (zero words decode to t = 0).  A split
+  // unit's steps are a whole number of pairs (below), so it multiplies no step
+  // past its own part; the loads it issues ahead past the part are not used.
   const int dr = tid >> 1, h = tid & 1;
   const int row = r0 + dr;
   const __amdgpu_buffer_rsrc_t wrs =
@@ -137,34 +129,11 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
     const int p = b0 / kPanelBlocks;
     const int Wps = (int)panel_stored_width(p, a.nb, kPanelBlocks);
     const int q0 = b0 - p * kPanelBlocks;
-    // zero words decode to t = 0
     const uint32_t off = (row < a.Mp && q0 < Wps)
                              ? (uint32_t)((p * a.Mp * kPanelBlocks + row * Wps + q0) * 4)
                              : 0x80000000u;
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
-  };
-  // X of a step goes straight into LDS (buffer_load ... lds, 16 bytes per
-  // lane): the tile is T tokens x 64 bytes, and 16-byte chunk c of token t sits
-  // at t*64 + ((c ^ f(t)) * 16) with f(t) = ((t>>1 ^ t>>3) & 1) | (t>>2 & 1) << 1.
-  // Tokens with equal t mod 4 (equal bank offset t*64 within 256 bytes) get
-  // distinct chunk positions over any 16 consecutive tokens, and tokens with
-  // equal t mod 2 over any 8, so operand reads are free of bank conflicts
-  // whether 16 lanes share 64 banks or 8 lanes share 32.  Wave w, copy i fills
-  // LDS pieces P = (kXCopies w + i) * 64 + lane.
-  auto copy_x = [&](int ks, uint8_t* dst) {
-#pragma unroll
-    for (int i = 0; i < kXCopies; ++i) {
-      const int P = (kXCopies * wave + i) * 64 + lane;
-      const int tok = P >> 2, c = (P & 3) ^ xswz(tok);
-      const int col = ks * kStepCols + 8 * c;
-      const uint32_t off = (t0 + tok < a.ntok && col < a.cols)
-                               ? (uint32_t)((t0 + tok) * a.cols + col) * 2u
-                               : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrs, (__attribute__((address_space(3))) void*)(dst + (kXCopies * wave + i) * 1024), 16,
-          off, 0, 0, 0);
-    }
   };
   // Decode word p of a step's group into a W buffer: it holds block
   // (p + row) & 3 of the step (the packed rows rotate their groups).
@@ -188,23 +157,52 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[g][n][v] = 0.f;
 
-  const int arow = lane & 31, kq = lane >> 5, swz = xswz(arow);
-  // Operand registers of slices 0 and 1.  Set 1 carries a step's slice 1
-  // across the step's closing barrier: a step first issues the reads of its
-  // slice 0 and runs the MFMAs of the previous step's slice 1 while they are
-  // in flight, then reads its slice 1 (used after the barrier) while the MFMAs
-  // of its slice 0 run, so no MFMA waits on a read issued right before it.
-  half8 A[2][kRG], B[2][kNTiles];
+  const int arow = lane & 31, kq = lane >> 5;
+  // B operands straight from X (no LDS: only this wave uses its tokens).  Lane
+  // l takes token l % 32 of each of the wave's 32-token tiles and the columns
+  // 16 s + 8 (l / 32) .. +7 of slice s of a step: one 16-byte load per tile and
+  // slice.  Tokens past the input and columns past the matrix read zeros; the
+  // column test is needed only in a step that reaches the last column (cols is
+  // a multiple of 8, so a load never straddles a token row's end).  Staging X
+  // in LDS with buffer_load ... lds, as an earlier version did, was up to 22%
+  // slower below 2048 tokens, and at 2048 up to 9% slower (8192 x 8192) and
+  // within 1% on the largest shapes.
+  uint32_t xo[kNTiles];
+#pragma unroll
+  for (int n = 0; n < kNTiles; ++n) {
+    const int tok = t0 + kTileToks / 4 * wave + 32 * n + arow;
+    xo[n] = tok < a.ntok ? (uint32_t)tok * (uint32_t)a.cols * 2u + 16u * kq : 0x80000000u;
+  }
+  half8 XB[2][2][kNTiles];  // [register set][slice][token tile]
+  auto load_b = [&](int ks, int set) {
+    const bool whole = (ks + 1) * kStepCols <= a.cols;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int n = 0; n < kNTiles; ++n) {
+        uint32_t off = xo[n] + (uint32_t)(ks * kStepCols * 2 + s * 32);
+        if (!whole && ks * kStepCols + 16 * s + 8 * kq >= a.cols) off = 0x80000000u;
+        XB[set][s][n] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+      }
+  };
+
+  // A operands of slices 0 and 1 (read from the W buffer).  Set 1 carries a
+  // step's slice 1 across the step's closing barrier: a step first issues the
+  // reads of its slice 0 and runs the MFMAs of the previous step's slice 1
+  // while they are in flight, then reads its slice 1 (used after the barrier)
+  // while the MFMAs of its slice 0 run, so no MFMA waits on a read issued right
+  // before it.  The first step's "previous slice" multiplies zeros.
+  half8 A[2][kRG];
 #pragma unroll
   for (int g = 0; g < kRG; ++g) A[1][g] = half8{};
 #pragma unroll
-  for (int n = 0; n < kNTiles; ++n) B[1][n] = half8{};
-  auto mfmas = [&](int set) {
+  for (int n = 0; n < kNTiles; ++n) XB[1][1][n] = half8{};
+  auto mfmas = [&](int aset, int bset, int s) {
 #pragma unroll
     for (int g = 0; g < kRG; ++g)
 #pragma unroll
       for (int n = 0; n < kNTiles; ++n)
-        acc[g][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[set][g], B[set][n], acc[g][n], 0, 0, 0);
+        acc[g][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[aset][g], XB[bset][s][n], acc[g][n], 0, 0, 0);
   };
   // The scheduler is told to alternate one MFMA with up to six VALU
   // instructions (the decode of one word of the next step), then the decode's
@@ -217,65 +215,79 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
     }
     __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
   };
-  auto mma = [&](const uint8_t* wb, const uint8_t* xb, uint8_t* wnext, uint4 wq) {
+  // The MFMAs of step ks (W buffer wb, B register set c) with the previous
+  // step's slice 1 first, the B loads of step ks + 1 into the other set once
+  // those MFMAs have read it, and the decode of step ks + 1 into wnext.
+  auto mma = [&](const uint8_t* wb, uint8_t* wnext, uint4 wq, int ks, int c) {
     uint32_t ext2[2];  // table lookups of both words
 #pragma unroll
     for (int j = 0; j < 2; ++j) ext2[j] = ext_c8(mine(wq, j), T0, T1);
     const uint8_t* wl = wb + arow * kLdsStride + kq * 16;
-    const uint8_t* xl = xb + (kTileToks / 4 * wave + arow) * kXRow;
     auto rd = [&](int s) {
-      const int xo = ((2 * s + kq) ^ swz) * 16;
 #pragma unroll
       for (int g = 0; g < kRG; ++g)
         A[s][g] = *reinterpret_cast<const half8*>(wl + g * 32 * kLdsStride + s * 32);
-#pragma unroll
-      for (int n = 0; n < kNTiles; ++n)
-        B[s][n] = *reinterpret_cast<const half8*>(xl + n * 32 * kXRow + xo);
     };
     rd(0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
+    mfmas(1, 1 - c, 1);
+    load_b(ks + 1, 1 - c);
     put_w1(wnext, mine(wq, 0), ext2[0], 2 * h);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
     rd(1);
-    mfmas(0);
+    mfmas(0, c, 0);
     put_w1(wnext, mine(wq, 1), ext2[1], 2 * h + 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, kRG + kNTiles, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kRG, 0);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Prologue: steps kb and kb+1 in flight, step kb decoded.
+  // Prologue: step kb's words and B operands and step kb+1's words in flight,
+  // step kb decoded.
   uint4 wr3[3];
-  copy_x(kb, xbuf[0]);
   wr3[0] = load_w(kb);
-  copy_x(kb + 1, xbuf[1]);
   wr3[1] = load_w(kb + 1);
-  __syncthreads();  // T0/T1 ready (waits for all loads too)
+  load_b(kb, 0);
+  __syncthreads();  // T0/T1 ready
   put_w(wbuf[0], wr3[0]);
   __syncthreads();
 
-  // Step k (buffers (k - kb) % 3): start the copies of step k + 2, run the
-  // MFMAs of step k (its slice 1 at the start of the next step), decode step
-  // k + 1, then wait until only step k + 2's nine loads are in flight (vmcnt
-  // counts in issue order) and meet at the barrier.
-  auto step = [&](int k, int b) {
+  // Step k (W buffers (k - kb) % 3, B set (k - kb) % 2): load the words of
+  // step k + 2, run the MFMAs of step k, decode step k + 1, then wait for this
+  // thread's LDS work only (the compiler waits for each load where its
+  // registers are used) and meet at the barrier.
+  auto step = [&](int k, int b, int c) {
     const int b1 = b == 2 ? 0 : b + 1, b2 = b == 0 ? 2 : b - 1;
-    copy_x(k + 2, xbuf[b2]);
     wr3[b2] = load_w(k + 2);
-    mma(wbuf[b], xbuf[b], wbuf[b1], wr3[b1]);
-    __builtin_amdgcn_s_waitcnt(0x0079);  // vmcnt(9) expcnt(7) lgkmcnt(0)
+    mma(wbuf[b], wbuf[b1], wr3[b1], k, c);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's W writes are done
     __builtin_amdgcn_s_barrier();
   };
-  // Whole rounds of three steps (one loop exit, so the accumulators keep their
-  // registers); the at most two steps past the matrix's end multiply zeros.
-  for (int ks = kb; ks < ke; ks += 3) {
-    step(ks, 0);
-    step(ks + 1, 1);
-    step(ks + 2, 2);
+  // An even number of steps (a padded step multiplies zeros): rounds of six,
+  // the loop unit of three W buffers and two B register sets, with buffers
+  // indexed at compile time and one loop exit, so the accumulators keep their
+  // registers; then two or four more.  (Parts rounded to six steps made the
+  // 1024-row projections 4% slower: a part of 32 steps ran 36.)
+  const int kend = kb + ((ke - kb + 1) & ~1);
+  int ks = kb;
+  for (; ks + 6 <= kend; ks += 6) {
+    step(ks, 0, 0);
+    step(ks + 1, 1, 1);
+    step(ks + 2, 2, 0);
+    step(ks + 3, 0, 1);
+    step(ks + 4, 1, 0);
+    step(ks + 5, 2, 1);
   }
-  mfmas(1);  // the last step's slice 1
+  if (ks < kend) {
+    step(ks, 0, 0);
+    step(ks + 1, 1, 1);
+    if (ks + 2 < kend) {
+      step(ks + 2, 2, 0);
+      step(ks + 3, 0, 1);
+    }
+  }
+  mfmas(1, 1, 1);  // the last step's slice 1 (an even count: the last step used set 1)
 
   // Lane holds token 32n + l%32 of its wave's T/4 and rows 32g + 8j + 4(l/32) + v.
   if constexpr (kSplit) {
@@ -672,7 +684,7 @@ struct Plan {
     return (size_t)(tail * splits) * rows_tile * toks * sizeof(float);
   }
 };
-void split_tail(Plan& p, int64_t nsteps) {
+void split_tail(Plan& p, int64_t nsteps, int64_t unit) {
   p.full = p.tiles;
   p.tail = 0;
   p.splits = 1;
@@ -682,8 +694,8 @@ void split_tail(Plan& p, int64_t nsteps) {
   if (rem > 0 && 2 * rem <= cus) {
     const int64_t sp = std::min(std::min(cus / rem, kMaxSplits), nsteps / kMinSplitSteps);
     if (sp >= 2) {
-      // whole rounds of three steps per part (the kernels' loop unit)
-      p.split_steps = ((nsteps + sp - 1) / sp + 2) / 3 * 3;
+      // whole loop units per part: pairs of steps (4-bit), rounds of three (3-bit)
+      p.split_steps = ((nsteps + sp - 1) / sp + unit - 1) / unit * unit;
       p.splits = (nsteps + p.split_steps - 1) / p.split_steps;  // no empty part
       p.tail = rem;
       p.full = p.tiles - rem;
@@ -702,7 +714,7 @@ Plan plan_for(const seedlm_matrix* h, int64_t ntok) {
   }
   p.row_tiles = (h->rows + p.rows_tile - 1) / p.rows_tile;
   p.tiles = p.row_tiles * ((ntok + p.toks - 1) / p.toks);
-  split_tail(p, (h->nb + 3) / 4);
+  split_tail(p, (h->nb + 3) / 4, h->C == 8 ? 2 : 3);
   return p;
 }
 

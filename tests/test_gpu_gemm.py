@@ -122,7 +122,7 @@ def test_gemm_scratch_bytes():
     s, c, e = gen_records(68, 1, 256, 1024, 8, 3)
     m = S.seedlm_pack(s, c, e, 256, 1024, 8, 3, 16)
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        # 2 x 2 tiles of 512 tokens, 32 K steps -> 4 parts (9, 9, 9 and 5 steps)
+        # 2 x 2 tiles of 512 tokens, 32 K steps -> 4 parts of 8 steps
         assert S.seedlm_gemm_scratch_bytes(m, 600) == 4 * 4 * 128 * 512 * 4
         # one token: 2 tiles of 256 tokens, 4 parts
         assert S.seedlm_gemm_scratch_bytes(m, 1) == 2 * 4 * 128 * 256 * 4
