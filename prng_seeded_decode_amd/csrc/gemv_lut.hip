@@ -31,7 +31,10 @@
 //
 // Per block the arithmetic is arranged to keep VALU work low:
 //   * TC[v] is the coefficient byte v = (t1 << 4 | t0) as the fp16 pair
-//     (t0, t1), used directly by v_fma_mix_f32 and v_dot2_f32_f16;
+//     (t0/16, t1/16), used directly by v_fma_mix_f32 and v_dot2_f32_f16, and
+//     t2/16 is one v_cvt_off_f32_i4 of the word's top byte (the instruction
+//     turns a signed nibble into nibble/16); every coefficient carries the
+//     same 1/16, an exact power of two that the panel reduction's scale undoes;
 //   * T1[v] carries v in its top byte, so ext = T0[B0] ^ T1[B1] holds
 //     (B2, B3, B4, B1) and one v_perm_b32 makes the fp16 pair
 //     (1024 + B1, 1024 + B2) (0x64 is the fp16 exponent of 1024); then
@@ -209,10 +212,10 @@ __global__ void __launch_bounds__(kThreads, 1)
       if (part < 4) {
         val = sm.gf2[u];
         dst = reinterpret_cast<uint4*>(&sm.B[u][kColT0]) + part;
-      } else {  // (t0, t1) of the coefficient byte u, as an fp16 pair
+      } else {  // (t0, t1)/16 of the coefficient byte u, as an fp16 pair (exact)
         const int lo = u & 15, hi = u >> 4;
-        const __half h0 = __int2half_rn(lo - ((lo & 8) << 1));
-        const __half h1 = __int2half_rn(hi - ((hi & 8) << 1));
+        const __half h0 = __float2half((float)(lo - ((lo & 8) << 1)) * 0.0625f);
+        const __half h1 = __float2half((float)(hi - ((hi & 8) << 1)) * 0.0625f);
         val = (uint32_t)__half_as_ushort(h0) | ((uint32_t)__half_as_ushort(h1) << 16);
         dst = reinterpret_cast<uint4*>(&sm.B[u][kColTC]) + (part - 4);
       }
@@ -328,11 +331,11 @@ __global__ void __launch_bounds__(kThreads, 1)
       for (int k = 0; k < NB; ++k) {
         const int j = k & 3;
         const uint32_t wk = w[k];
-        const half2v tc = __builtin_bit_cast(half2v, tcv[k]);  // (t0, t1)
+        const half2v tc = __builtin_bit_cast(half2v, tcv[k]);  // (t0, t1)/16
         // (1024 + B1, 1024 + B2) and (1024 + B3, 0) as fp16 pairs
         const half2v p12 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ext[k], 0x64646464u, 0x01040007u));
         const half2v p3 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(ext[k], 0x64646464u, 0x0C0C0005u));
-        const float t2 = (float)(((int)(wk << 4)) >> 28);
+        const float t2 = __builtin_amdgcn_cvt_off_f32_i4(wk >> 24);  // t2/16
         const float mid = __builtin_amdgcn_fdot2(tc, p12, __builtin_fmaf(t2, (float)p3[0], 0.f), false);
         float V = t2 * (l0b2[k] + l2b4[k]);
         V = fmaf((float)tc[0], l0b0[k] + l2b2[k], V);
@@ -348,7 +351,7 @@ __global__ void __launch_bounds__(kThreads, 1)
         acc[h] += dpp<0x4E>(acc[h]);
         acc[h] += dpp<0x141>(acc[h]);
         if (h < nvalid)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[h] * 0x1p-30f), prsrc,
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[h]), prsrc,
                                                 pstore + (uint32_t)(sl0 + h * kWaves) * 32u, 0, 0);
       }
     };
@@ -412,6 +415,9 @@ bool fill_group(const seedlm_matrix* const* hs, const void* const* xs, void* con
     M.np = (int)h->np;
     M.slabs = (int)(h->Mp / 8);
   }
+  // The partials hold 2^g sum_j (t_j/16) D_j with g = e + 15, and the window
+  // values z - 2^15 are 2^15 times the entries of U: 2^-15 * 2^-15 * 16.
+  grp.scale = 0x1p-26f;
   return split_group(grp, kBuildCost);
 }
 

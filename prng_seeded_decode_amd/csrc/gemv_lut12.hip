@@ -364,10 +364,13 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
           const float D2 = (h[kk][6] + h[kk][7]) + (h[kk][8] + h[kk][9]);
           const float D3 = (h[kk][10] + h[kk][11]) + (h[kk][12] + h[kk][13]);
           const uint32_t wk = w[k];
-          float V = (float)(((int)(wk << 12)) >> 28) * D0;
-          V = fmaf((float)(((int)(wk << 8)) >> 28), D1, V);
-          V = fmaf((float)(((int)(wk << 4)) >> 28), D2, V);
-          V = fmaf((float)(((int)wk) >> 28), D3, V);
+          // t_j/16 from the coefficient nibbles (v_cvt_off_f32_i4: signed
+          // nibble -> nibble/16; nibbles 0 and 2 through a byte select);
+          // the 1/16 is undone by the panel reduction's scale.
+          float V = __builtin_amdgcn_cvt_off_f32_i4(wk >> 16) * D0;
+          V = fmaf(__builtin_amdgcn_cvt_off_f32_i4(wk >> 20), D1, V);
+          V = fmaf(__builtin_amdgcn_cvt_off_f32_i4(wk >> 24), D2, V);
+          V = fmaf(__builtin_amdgcn_cvt_off_f32_i4(wk >> 28), D3, V);
           acc += ldexpf(V, (int)((q.e >> (4 * k)) & 15u));
         }
       }
@@ -376,7 +379,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_lut12_kernel(const LutGroup 
       acc += dpp<0x4E>(acc);
       const int64_t row = (int64_t)kRowsPerSlab * sl + rho;
       const uint32_t poff = (g == 0 && row < Mp) ? (uint32_t)(u * Mp + row) * 4u : 0x80000000u;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc * 0x1p-30f), prsrc, poff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), prsrc, poff, 0, 0);
     };
 
     // A wave's first two slabs are fixed (their loads went out before the
@@ -442,6 +445,9 @@ bool fill_group12(const seedlm_matrix* const* hs, const void* const* xs, void* c
     M.np = (int)units;
     M.slabs = (int)((h->Mp + kRowsPerSlab - 1) / kRowsPerSlab);
   }
+  // The partials hold 2^g sum_j (t_j/16) D_j with g = e + 15, and the window
+  // values z - 2^15 are 2^15 times the entries of U: 2^-15 * 2^-15 * 16.
+  grp.scale = 0x1p-26f;
   return split_group(grp, kBuildCost);
 }
 

@@ -41,6 +41,7 @@ struct LutGroup {
   LutMatrix m[kMaxGroup];
   int n;
   int red_blocks;  // reduce workgroups over all matrices
+  float scale;     // power of two applied to each row's sum of partials
   int grid;
   // Workgroup w processes global work items [bounds[w], bounds[w+1]).
   int32_t bounds[kMaxWorkgroups + 1];
@@ -112,7 +113,9 @@ __device__ inline void store_y<float>(float* p, float v) { *p = v; }
 template <>
 __device__ inline void store_y<__half>(__half* p, float v) { *p = __float2half_rn(v); }
 
-// Panel reduction: y[r] = sum over units p of partial[p][r].  A workgroup owns
+// Panel reduction: y[r] = scale * sum over units p of partial[p][r] (scale is a
+// power of two, so applying it to the sum instead of to every partial gives the
+// same bits and saves the main kernels a multiply per row sum).  A workgroup owns
 // 64 consecutive rows of one matrix (lane = row, so every load reads 256
 // contiguous bytes); wave w adds units w, w+4, w+8, ... with up to 32 loads in
 // flight, and the four wave sums combine through LDS as (w0+w1)+(w2+w3).  The
@@ -145,7 +148,8 @@ __global__ void __launch_bounds__(256) reduce_panels_kernel(const LutGroup grp) 
   wsum[wv][lane] = s;
   __syncthreads();
   if (wv == 0 && r < M.rows)
-    store_y(static_cast<YT*>(M.y) + r, (wsum[0][lane] + wsum[1][lane]) + (wsum[2][lane] + wsum[3][lane]));
+    store_y(static_cast<YT*>(M.y) + r,
+            ((wsum[0][lane] + wsum[1][lane]) + (wsum[2][lane] + wsum[3][lane])) * grp.scale);
 }
 
 inline int launch_reduce(const LutGroup& grp, int ydt, hipStream_t s) {

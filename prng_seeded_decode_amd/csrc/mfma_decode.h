@@ -71,15 +71,18 @@ __device__ inline uint32_t ext_c8(uint32_t w, const uint32_t* T0, const uint32_t
 // (three bfe, three mad24); 4% off the batch-8 layer step in an interleaved
 // A/B, with identical results.
 __device__ inline half8 decode_c8_ext(uint32_t w, uint32_t ext) {
-  const uint32_t lo = (w & 0xFFFFu) | (ext << 16);  // stream bits 0..31
-  const uint32_t hi = ext >> 16;                    // stream bits 32..47
+  // stream bits 0..31: the seed, then ext's low half (one v_perm_b32)
+  const uint32_t lo = __builtin_amdgcn_perm(ext, w, 0x05040100u);
+  const uint32_t hi = ext >> 16;  // stream bits 32..47
   const int t0 = ((int)(w << 12)) >> 28;
   const int t1 = ((int)(w << 8)) >> 28;
   const int t2 = ((int)(w << 4)) >> 28;
   const short2v t02 = short2v{(short)t0, (short)t2};
-  const int base = kMagic - 32768 * t1;
-  const float sc = block_scale(w >> 28);
-  const float off = -kMagicF * sc;
+  const int base = mad24(t1, -32768, kMagic);
+  // 2^(g - 20) and -1.5 * 2^23 * 2^(g - 20) as two v_ldexp_f32 of g = w >> 28
+  const int g = (int)(w >> 28);
+  const float sc = __builtin_amdgcn_ldexpf(0x1p-20f, g);
+  const float off = __builtin_amdgcn_ldexpf(-kMagicF * 0x1p-20f, g);
   int I[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -113,7 +116,7 @@ __device__ inline Dec12 dec12_setup(uint32_t w, uint32_t g, const uint64_t* T0,
                                     const uint64_t* T1) {
   Dec12 d;
   const uint64_t ext = T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];  // stream bits 16..79
-  d.s0 = (w & 0xFFFFu) | ((uint32_t)ext << 16);
+  d.s0 = __builtin_amdgcn_perm((uint32_t)ext, w, 0x05040100u);  // seed, ext bits 0..15
   d.s1 = (uint32_t)ext;
   d.s2 = (uint32_t)(ext >> 16);
 #pragma unroll
