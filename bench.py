@@ -715,9 +715,22 @@ def main():
         for k in range(args.steps):
             time_next(*kev_ptr[k])
             run_step(k)
+    # A third pass right behind: the same steps' main launches alone, back to back
+    # between two events, so that their mean holds the kernel and the short gap
+    # between dispatches but no per-launch event work (a cross-check of the
+    # per-launch events, which read a few percent above a kernel trace).
+    bb0 = torch.cuda.Event(enable_timing=True)
+    bb1 = torch.cuda.Event(enable_timing=True)
+    if timed_kernel:
+        bb0.record(stream)
+        for k in range(args.steps):
+            run_step(k, phase="begin")
+        bb1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     kern_ms = [a.elapsed_time(b) for a, b in kev]
+    back_to_back_us = (round(bb0.elapsed_time(bb1) / args.steps * 1e3, 2)
+                       if timed_kernel else None)
     # The dominant kernel is part of every step, so its mean time must not exceed
     # the step's; the line reports whether it holds (a profiler attached to the
     # process can inflate the kernel events of tiny steps).
@@ -905,6 +918,7 @@ def main():
         "per_matrix": per_matrix or None,
         "kernel_us_per_launch": round(float(np.mean(kern_ms)) * 1e3, 2) if kern_ms else None,
         "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 2) if kern_ms else None,
+        "kernel_us_back_to_back": back_to_back_us,
         "kernel_timing": ("HIP events recorded by the fused decode-GEMV launch of each step "
                           "itself (hipExtLaunchKernel start/stop events on the launch stream), "
                           "in a second pass of the same steps queued right behind the timed "
