@@ -107,8 +107,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_c8_kernel(const GemmArgs
 
   for (int e = tid; e < 512; e += kGemmThreads) {
     const uint32_t v = (uint32_t)e & 255u;
-    if (e < 256) T0[v] = ext_bits<uint32_t>(v);
-    else T1[v] = ext_bits<uint32_t>(v << 8);
+    if (e < 256) T0[v] = c8_table_word(ext_bits<uint32_t>(v));
+    else T1[v] = c8_table_word(ext_bits<uint32_t>(v << 8));
   }
 
   // This thread's share of a K step: row dr = tid / 2 of the tile, whose step

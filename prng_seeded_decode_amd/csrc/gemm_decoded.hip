@@ -47,8 +47,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_f16_kernel(
   __shared__ Ext T0[256], T1[256];
   for (int e = threadIdx.x; e < 512; e += kDecThreads) {
     const uint32_t u = (uint32_t)e & 255u;
-    if (e < 256) T0[u] = ext_bits<Ext>(u);
-    else T1[u] = ext_bits<Ext>(u << 8);
+    if (e < 256) T0[u] = c8_table_word(ext_bits<Ext>(u));
+    else T1[u] = c8_table_word(ext_bits<Ext>(u << 8));
   }
   __syncthreads();
   constexpr int PB = panel_blocks(C);

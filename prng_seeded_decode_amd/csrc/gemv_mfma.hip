@@ -121,8 +121,8 @@ gemv_mfma_kernel(const MfmaGroup grp) {
 
   for (int e = tid; e < 512; e += kThreads) {
     const uint32_t u = (uint32_t)e & 255u;
-    if (e < 256) T0[u] = ext_bits<Ext>(u);
-    else T1[u] = ext_bits<Ext>(u << 8);
+    if (e < 256) T0[u] = c8_table_word(ext_bits<Ext>(u));
+    else T1[u] = c8_table_word(ext_bits<Ext>(u << 8));
   }
 
   // x staging: thread t holds batch row t / 16 and the kPer consecutive panel

@@ -55,13 +55,24 @@ __device__ inline uint32_t to_f16_pair(int I0, int I1, float sc, float off) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// Stream bits 16..47 of a 4-bit block's seed from the two GF(2) byte tables.
+// The GF(2) byte tables of the 4-bit decode hold their 32 extension bits
+// rotated by 16 (the XOR of two rotated words is the rotated XOR), so that
+// one word is both halves a block needs: its high half completes stream bits
+// 0..31 beside the seed, and its low half is stream bits 32..47, the high word
+// of every v_alignbit below (which reads only its low i < 8 bits).
+template <typename Ext>
+__device__ inline Ext c8_table_word(Ext e) {
+  if constexpr (sizeof(Ext) == 4) return (e >> 16) | (e << 16);
+  else return e;
+}
+
+// Stream bits 16..47 of a 4-bit block's seed, rotated by 16, from the tables.
 __device__ inline uint32_t ext_c8(uint32_t w, const uint32_t* T0, const uint32_t* T1) {
   return T0[w & 0xFFu] ^ T1[(w >> 8) & 0xFFu];
 }
 
 // Eight fp16 weights (x 2^10) of a 4-bit block, in column order, given its
-// stream bits 16..47.  Weight i needs the windows z_i, z_{8+i} and z_{16+i}
+// stream bits 16..47 rotated by 16 (ext_c8).  Weight i needs the windows z_i, z_{8+i} and z_{16+i}
 // (bits i.., 8+i.., 16+i.. of the stream, 16 each).  V = stream bits i..i+31
 // (one v_alignbit) holds z_i in its low half and z_{16+i} in its high half;
 // XOR with 0x80008000 turns both into z - 2^15 as signed 16-bit values, so one
@@ -71,9 +82,9 @@ __device__ inline uint32_t ext_c8(uint32_t w, const uint32_t* T0, const uint32_t
 // (three bfe, three mad24); 4% off the batch-8 layer step in an interleaved
 // A/B, with identical results.
 __device__ inline half8 decode_c8_ext(uint32_t w, uint32_t ext) {
-  // stream bits 0..31: the seed, then ext's low half (one v_perm_b32)
-  const uint32_t lo = __builtin_amdgcn_perm(ext, w, 0x05040100u);
-  const uint32_t hi = ext >> 16;  // stream bits 32..47
+  // stream bits 0..31: the seed, then the rotated word's high half (one v_perm_b32)
+  const uint32_t lo = __builtin_amdgcn_perm(ext, w, 0x07060100u);
+  const uint32_t hi = ext;  // stream bits 32..47 in its low half
   const int t0 = ((int)(w << 12)) >> 28;
   const int t1 = ((int)(w << 8)) >> 28;
   const int t2 = ((int)(w << 4)) >> 28;
